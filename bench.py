@@ -1,0 +1,285 @@
+"""Throughput of one paged decode step on one MI355X.
+
+A step is one pass of the whole device path over one batch: for every layer
+of the workload, kv_append of each sequence's new token, the split-KV paged
+decode kernel, and the log-sum-exp combine.  The page pool and block tables
+are built by the library's host allocator before timing; every input is
+resident in HBM when the timed region starts.
+
+value = algorithmic KV bytes read per step / step time, where the algorithmic
+bytes are 2 (K and V) x head_dim x element size per attended token per KV head
+per layer (the per-token KV formula of the pages' chapter 17 equation M_kv).
+
+Prints one JSON line.  Default workload: batch 16 x 4096 tokens, 32/32 heads,
+head_dim 128, bf16 (one layer of the Llama-2-7B example).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 << 20         # last-level (Infinity) cache
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_254_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama2_7b_mha")
+    ap.add_argument("--n-items", type=int, default=0)
+    ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    pass
+
+
+def setup(w, device):
+    import torch
+    import paged_kv_cache_254_amd as pkv
+    import workloads as W
+    cached = W.cached_lens(w)
+    att = cached + 1
+    P = W.pool_pages(w)
+    mb = int(max((att + 15) // 16))
+    pool = pkv.PagePool(P, W.free_order(w))
+    for b in range(w.batch):
+        pool.reserve(b, int(cached[b]))
+    grown = sum(pool.reserve(b, int(att[b])) for b in range(w.batch))  # the step's new pages
+    bt_np = pool.block_table(range(w.batch), mb)
+    common = dict(
+        bt=torch.from_numpy(bt_np).to(device),
+        positions=torch.from_numpy(cached.astype(np.int32)).to(device),
+        seq_lens=torch.from_numpy(att.astype(np.int32)).to(device),
+    )
+    kv_bytes_layer = int(att.sum()) * w.n_kv_heads * w.head_dim * 2 * w.elem_bytes
+    # Small caches fit in the last-level cache: rotate enough copies that one
+    # step streams at least 4x its size from HBM.
+    n_copies = max(w.n_layers, math.ceil(4 * MALL_BYTES / kv_bytes_layer)) if kv_bytes_layer < 2 * MALL_BYTES \
+        else w.n_layers
+    layers = []
+    for i in range(n_copies):
+        L = Layer()
+        L.k_pages, L.v_pages = W.make_pools(w, i % max(1, w.n_layers), device)
+        L.q = W.make_q(w, i, device)
+        L.k_new, L.v_new = W.make_new_kv(w, i, device)
+        L.out = torch.empty_like(L.q)
+        layers.append(L)
+    return dict(common, layers=layers, cached=cached, att=att, bt_np=bt_np, mb=mb, P=P,
+                kv_bytes_layer=kv_bytes_layer, grown=grown, n_copies=n_copies)
+
+
+def cpu_baseline(w, S, budget_s):
+    """The oracle, as it stands, on a bounded sample: whole sequences of layer 0
+    (append + decode for every query head), until the time budget is used."""
+    import torch
+    import workloads as W
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    L = S["layers"][0]
+    rng = np.random.default_rng(0)
+    pick = list(rng.permutation(w.batch))
+    done, secs, kv_bytes, toks = 0, 0.0, 0, 0
+    for b in pick:
+        nblk = (int(S["att"][b]) + 15) // 16
+        pages = torch.from_numpy(S["bt_np"][b, :nblk].astype(np.int64)).to(L.k_pages.device)
+        kp = L.k_pages.index_select(0, pages).double().cpu().numpy()
+        vp = L.v_pages.index_select(0, pages).double().cpu().numpy()
+        kn = L.k_new[b:b + 1].double().cpu().numpy()
+        vn = L.v_new[b:b + 1].double().cpu().numpy()
+        qb = L.q[b:b + 1].double().cpu().numpy()
+        bt = np.arange(nblk, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        k2, v2 = OA.append(kp, vp, bt, [int(S["cached"][b])], kn, vn, 16)
+        OA.decode(qb, k2, v2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
+        secs += time.perf_counter() - t0
+        done += 1
+        kv_bytes += int(S["att"][b]) * w.n_kv_heads * w.head_dim * 2 * w.elem_bytes
+        toks += 1
+        if secs >= budget_s:
+            break
+    return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch} sequences of one layer (append + decode, all {w.n_q_heads} query "
+                      f"heads), {kv_bytes / 2**20:.0f} MiB of KV, {secs:.1f} s",
+            "seconds": secs}
+
+
+def hbm_probe(device):
+    import torch
+    import paged_kv_cache_254_amd as pkv
+    props = torch.cuda.get_device_properties(device)
+    n_cu = props.multi_processor_count
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    sink = torch.empty(n_cu * 64, dtype=torch.int32, device=device)
+    best = 0.0
+    for blocks_per_cu in (4, 8, 16):
+        nb = n_cu * blocks_per_cu
+        for _ in range(2):
+            pkv.hbm_read_probe(buf, sink, nb)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(5):
+            pkv.hbm_read_probe(buf, sink, nb)
+        e.record()
+        torch.cuda.synchronize()
+        best = max(best, 5 * buf.numel() / (s.elapsed_time(e) / 1e3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+def traffic_for(workload):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counters, if
+    they were taken on the current kernel source; otherwise None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_sha") != kernel_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this path is single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_254_amd as pkv
+    import workloads as W
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    w = W.get(args.workload)
+    log(f"setup {w.name}")
+    S = setup(w, device)
+    dt = W.torch_dtype(w)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, args.n_items, args.min_chunk,
+                      device=device)
+    layers = S["layers"]
+    n_layers = w.n_layers
+    kv_step = S["kv_bytes_layer"] * n_layers
+    stream = torch.cuda.current_stream()
+    rot = [0]
+
+    def step(ev=None):
+        """One step; ev (optional) holds 3 events per layer: before split,
+        after split, after combine."""
+        for li in range(n_layers):
+            L = layers[rot[0] % len(layers)]
+            rot[0] += 1
+            pkv.kv_append(L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["positions"], stream)
+            if ev is not None:
+                ev[3 * li].record(stream)
+            dec.split(L.q, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+            if ev is not None:
+                ev[3 * li + 1].record(stream)
+            dec.combine(S["seq_lens"], L.out, S["mb"], stream)
+            if ev is not None:
+                ev[3 * li + 2].record(stream)
+
+    log(f"warmup {args.warmup} (n_items={dec.n_items}, copies={len(layers)})")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps
+    t_s, t_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_s.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_e.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_s.elapsed_time(t_e) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    # per-kernel durations, same launches with events between them
+    n_launch = args.steps * n_layers
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n_launch)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[3 * n_layers * i: 3 * n_layers * (i + 1)])
+    torch.cuda.synchronize()
+    split_ms = [evs[3 * k].elapsed_time(evs[3 * k + 1]) for k in range(n_launch)]
+    comb_ms = [evs[3 * k + 1].elapsed_time(evs[3 * k + 2]) for k in range(n_launch)]
+    split_avg = float(np.mean(split_ms))
+    achieved = S["kv_bytes_layer"] / (split_avg / 1e3) / 1e9
+    value = kv_step / (ms_per_step / 1e3) / 1e9
+    traffic = traffic_for(w.name)
+
+    probe = None if args.no_probe else hbm_probe(device)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, S, args.cpu_seconds)
+        cpu.pop("seconds", None)
+
+    rec = {
+        "metric": "KV-cache GB/s read and % of MI355X HBM peak for paged GQA decode attention",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+            "head_dim": w.head_dim, "block_size": 16, "layers": n_layers,
+            "attended_tokens": int(S["att"].sum()), "kv_bytes_per_step": kv_step,
+            "accumulate": "fp32", "n_items": dec.n_items, "pool_copies": len(layers),
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.batch / (ms_per_step / 1e3), 1),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "split_kernel", "avg_launch_ms": round(split_avg, 5),
+            "algorithmic_bytes_per_launch": S["kv_bytes_layer"],
+        },
+        "combine_avg_ms": round(float(np.mean(comb_ms)), 5),
+        "hbm_read_probe_gbs": None if probe is None else round(probe, 1),
+        "cpu_baseline": cpu,
+        "kernel_sha": kernel_sha(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

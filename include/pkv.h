@@ -1,0 +1,255 @@
+/*
+ * pkv.h - C ABI of libpkv, paged GQA decode attention for MI355X (gfx950).
+ *
+ * One decode step of a transformer layer: every sequence in the batch has one
+ * new token whose query attends over that sequence's cached keys and values,
+ * softmax(q K^T * scale) V, with K/V stored in fixed-size pages found through a
+ * per-sequence block table and each KV head shared by a group of query heads.
+ *
+ * Sources for the operations (web pages on LLM inference):
+ *  - attention and the cache it forces: evaltude "Part 6 - Inference
+ *    Fundamentals", section "Q, K, V - and why they force a cache"; evaltude
+ *    docs "Transformer inference mechanics", sections "What Q, K, and V do in
+ *    causal attention" and "What the KV cache stores per layer";
+ *  - MHA / MQA / GQA head sharing: the same docs, "MHA versus MQA versus GQA";
+ *  - paged storage, 16-token blocks, per-request block table: hoshank.vercel.app
+ *    "Inference Engines" (chapter 17), "The Breakthrough"; CS336 lecture 10
+ *    notes (rraushan-blog), "PagedAttention (vLLM)";
+ *  - online softmax, exact rescaling of partial results: learn.byteknotlabs.com
+ *    "Efficient inference", "FlashAttention: exact attention without the
+ *    matrix"; split-KV decode (FlashDecoding) is named in the CS336 notes;
+ *  - KV byte formula: chapter 17 "The Mathematics" (equation M_kv).
+ *
+ * Conventions
+ *  - Every function returns an int status (PKV_OK = 0 or a negative PKV_ERR_*)
+ *    unless stated otherwise; no C++ exception crosses the ABI.  On error,
+ *    pkv_last_error() returns a thread-local description.
+ *  - "device" pointers are HIP device memory owned by the caller; the library
+ *    never allocates, frees or synchronises device memory and launches only on
+ *    the given stream (a hipStream_t passed as void*, NULL = default stream).
+ *    Device calls return after the launch (asynchronous); a launch failure
+ *    returns PKV_ERR_HIP.
+ *  - "host" pointers are ordinary CPU memory owned by the caller.
+ *  - All scalar arguments are checked on the host before anything is
+ *    launched; nothing is launched on error.  Device-side data (block-table
+ *    entries, lengths, positions) is checked in the kernels: an entry that
+ *    would address outside the pool is never dereferenced (see each call).
+ *
+ * Data layout (device, row-major; elem = float or bfloat16; X = 16 / sizeof(elem),
+ * i.e. 4 for fp32 and 8 for bf16; the block size is 16 tokens):
+ *  - q        [batch][n_q_heads][head_dim]
+ *  - out      [batch][n_q_heads][head_dim] (same dtype as q)
+ *  - k_pages  [num_pages][n_kv_heads][head_dim / X][16][X]: key element d of the
+ *             token in slot s of page p, head h, is at [p][h][d / X][s][d % X];
+ *  - v_pages  [num_pages][n_kv_heads][head_dim][16]: value element d of slot s
+ *             is at [p][h][d][s] (V is stored transposed inside a page);
+ *  - block_table int32 [batch][max_blocks_per_seq]: logical block i of sequence
+ *             b lives in physical page block_table[b][i]; entries past the
+ *             sequence's last block are ignored (-1 by convention);
+ *  - seq_lens int32 [batch]: number of tokens each query attends to, all of
+ *             them already in the cache (token t < seq_len is slot t % 16 of
+ *             page block_table[b][t / 16]).
+ *  - GQA head map: query head hq reads KV head hq / (n_q_heads / n_kv_heads).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or shape   */
+  PKV_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim, dtype, block  */
+  PKV_ERR_OUT_OF_PAGES = -3, /* pool exhausted; the pool is left unchanged   */
+  PKV_ERR_WORKSPACE = -4,    /* workspace smaller than required              */
+  PKV_ERR_HIP = -5,          /* a HIP runtime call or launch failed          */
+  PKV_ERR_NOT_FOUND = -6,    /* unknown sequence id                          */
+  PKV_ERR_EXISTS = -7        /* sequence id already in use                   */
+};
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* Description of a status code (static string). */
+const char* pkv_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Byte accounting (host).  Chapter 17 "The Mathematics", equation M_kv:
+ *   M = 2 * n_layers * n_kv_heads * head_dim * seq_len * batch * elem_bytes
+ * (factor 2: keys and values).  Returns 0 if any argument is negative.
+ * ------------------------------------------------------------------------ */
+uint64_t pkv_kv_cache_bytes(int64_t n_layers, int64_t n_kv_heads, int64_t head_dim,
+                            int64_t seq_len, int64_t batch, int64_t elem_bytes);
+/* Per-token form (seq_len = batch = 1). */
+uint64_t pkv_kv_bytes_per_token(int64_t n_layers, int64_t n_kv_heads, int64_t head_dim,
+                                int64_t elem_bytes);
+
+/* ------------------------------------------------------------------------ *
+ * Page pool and block tables (host).  Blocks are allocated on demand as a
+ * sequence grows, from a free list, instead of reserving a worst-case slab
+ * (chapter 17 "The Breakthrough"; CS336 notes "PagedAttention (vLLM)").
+ * Rules:
+ *  - the free list starts in the order given (free_order: a permutation of
+ *    0..num_pages-1; NULL means 0, 1, 2, ...);
+ *  - reserve takes pages from the front of the free list, in order;
+ *  - release returns a sequence's pages, in block order, to the back of the
+ *    free list (a page shared by a fork is returned when its last user goes);
+ *  - fork lets a child share all of a parent's pages (reference counted);
+ *    reserve_for_write replaces a shared block with a fresh page before a
+ *    write (copy-on-write, CS336 notes "PagedAttention (vLLM)").
+ * A pool is not thread-safe; use one per thread or lock around calls.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_pool pkv_pool;
+
+/* Create a pool of num_pages (>= 1) pages.  *out receives the pool. */
+int pkv_pool_create(int32_t num_pages, const int32_t* free_order /* host, nullable */,
+                    pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+/* Number of free pages, or a negative status if pool is NULL. */
+int32_t pkv_pool_num_free(const pkv_pool* pool);
+/* Grow seq_id (created if new) to hold n_tokens tokens, i.e. ceil(n_tokens /
+ * block_size) blocks.  Never shrinks.  *n_new_pages (nullable) receives the
+ * number of pages taken.  PKV_ERR_OUT_OF_PAGES leaves the pool unchanged. */
+int pkv_seq_reserve(pkv_pool* pool, int64_t seq_id, int64_t n_tokens, int32_t block_size,
+                    int32_t* n_new_pages);
+/* Forget seq_id and return its pages (PKV_ERR_NOT_FOUND if unknown). */
+int pkv_seq_release(pkv_pool* pool, int64_t seq_id);
+/* child shares every page of parent (PKV_ERR_EXISTS if child exists). */
+int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t child);
+/* Make token `position` of seq_id writable: grow it if needed; if the block
+ * holding position is shared, give seq_id a fresh page for it.  *copy_src and
+ * *copy_dst receive (old page, new page) when the caller must copy the block's
+ * contents, or -1 and -1 when no copy is needed. */
+int pkv_seq_reserve_for_write(pkv_pool* pool, int64_t seq_id, int64_t position,
+                              int32_t block_size, int32_t* copy_src, int32_t* copy_dst);
+/* Number of blocks held by seq_id. */
+int pkv_seq_num_blocks(const pkv_pool* pool, int64_t seq_id, int32_t* out);
+/* Fill out (host int32 [batch][max_blocks_per_seq]) with each sequence's pages
+ * in logical order, padded with -1.  Unknown ids give an all -1 row.  Returns
+ * PKV_ERR_INVALID_ARG if a sequence has more than max_blocks_per_seq blocks. */
+int pkv_build_block_table(const pkv_pool* pool, const int64_t* seq_ids, int32_t batch,
+                          int32_t max_blocks_per_seq, int32_t* out);
+
+/* ------------------------------------------------------------------------ *
+ * kv_append (device): write the step's new key and value of every sequence
+ * into its slot (evaltude docs "What the KV cache stores per layer": each
+ * layer's cache gains the new token's K/V every step).
+ *   k_new, v_new  device [batch][n_kv_heads][head_dim] (dtype)
+ *   positions     device int32 [batch]: token index to write; it lands in slot
+ *                 positions[b] % 16 of page block_table[b][positions[b] / 16].
+ * A bit-for-bit copy.  A position < 0 or >= 16 * max_blocks_per_seq, or a
+ * block-table entry outside [0, num_pages), skips that sequence's write (no
+ * memory outside the pool is touched).
+ * ------------------------------------------------------------------------ */
+int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                  const int32_t* block_table, const int32_t* positions, int32_t batch,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * paged_decode_attn (device): out[b][hq] = softmax(scale * q[b][hq] . K_b^T) V_b
+ * over the seq_lens[b] cached tokens of sequence b and KV head
+ * hq / (n_q_heads / n_kv_heads), computed with an online softmax (running
+ * maximum and sum, no score matrix) and split over the KV pages; the splits'
+ * partial results are merged by a log-sum-exp combine.
+ *
+ * Supported: head_dim 64 or 128; block_size 16; dtype PKV_F32 or PKV_BF16 (q,
+ * pages and out share it; accumulation is fp32); n_q_heads a multiple of
+ * n_kv_heads with group n_q_heads / n_kv_heads <= 64; 0 <= batch <= 16000.
+ * seq_lens[b] == 0 gives a zero row.  A length < 0 or > 16 * max_blocks_per_seq,
+ * or a block-table entry outside [0, num_pages), gives a NaN row for that
+ * sequence (nothing outside the pool is read).
+ *
+ * Work split: the pages of all (sequence, KV head) pairs, taken in that order,
+ * are cut into n_items equal chunks of C = max(min_chunk_pages,
+ * ceil(total / n_items)) pages.  Each chunk is processed by one wavefront (or
+ * ceil(group / 16) wavefronts for groups above 16).  A (sequence, KV head)
+ * whose pages fall in one chunk gets its output written directly; otherwise
+ * each chunk writes a partial (normalised output and natural-log sum of
+ * exponentials) and the combine merges them.
+ *
+ * workspace: device, 256-byte aligned, at least
+ * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
+ * bytes (n_items after defaults are applied).  Contents on entry are ignored.
+ * opts (nullable): n_items <= 0 means one chunk per wavefront the device can
+ * hold at once; min_chunk_pages <= 0 means 8.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_decode_opts {
+  int32_t n_items;
+  int32_t min_chunk_pages;
+} pkv_decode_opts;
+
+int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_size, float scale, void* out, void* stream,
+                          int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                          int32_t dtype, void* workspace, size_t workspace_bytes,
+                          const pkv_decode_opts* opts);
+
+/* The split half of pkv_paged_decode_attn alone (same arguments): writes the
+ * rows of single-chunk (sequence, KV head) pairs into out and every other
+ * chunk's partial into the workspace:
+ *   partial_o   float [slots][group][head_dim] at workspace offset 0
+ *   partial_lse float [slots][group] right after partial_o
+ * with slots = n_items + batch * n_kv_heads; chunk c's partial for pair
+ * (b, h) is slot c + b * n_kv_heads + h.  partial_o is softmax-weighted V over
+ * the chunk's tokens of that pair, partial_lse = log(sum exp(scale * q.k)). */
+int pkv_paged_decode_split(const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t block_size, float scale, void* out, void* stream,
+                           int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                           int32_t dtype, void* workspace, size_t workspace_bytes,
+                           const pkv_decode_opts* opts);
+
+/* The combine half: for every (sequence, KV head) pair split over several
+ * chunks, out = sum_i exp(lse_i - M) o_i / sum_i exp(lse_i - M), M = max lse_i
+ * (byteknotlabs "FlashAttention: exact attention without the matrix": partial
+ * results rescaled by the running maximum and combined exactly).  Also writes
+ * the zero rows (seq_len 0) and NaN rows (invalid length).  Must be given the
+ * same seq_lens, shapes and opts as the split call that filled workspace. */
+int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens,
+                    int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, void* out, int32_t dtype,
+                    const pkv_decode_opts* opts, void* stream);
+
+/* Workspace bytes for the calls above (negative status on bad arguments). */
+int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, int32_t n_items);
+
+/* The n_items the device calls use when opts->n_items <= 0, for this device
+ * (the current HIP device), dtype, head_dim and group (host query; needs a GPU). */
+int pkv_decode_default_items(int32_t dtype, int32_t head_dim, int32_t group, int32_t* out);
+
+/* Host mirror of the split plan, for callers that size or inspect partials:
+ * seq_lens (host int32 [batch]) -> *chunk_pages (C above), and for every pair
+ * (b, h) first_chunk[b * n_kv + h] and last_chunk[b * n_kv + h] (host int32,
+ * nullable; -1 for empty sequences).  n_items must already be resolved. */
+int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
+                    int32_t block_size, int32_t max_blocks_per_seq, int32_t n_items,
+                    int32_t min_chunk_pages, int32_t* chunk_pages, int32_t* first_chunk,
+                    int32_t* last_chunk);
+
+/* ------------------------------------------------------------------------ *
+ * Bandwidth probes (device), for measuring what the HBM path can sustain.
+ * pkv_hbm_read_probe streams `bytes` (multiple of 16, buf 16-byte aligned)
+ * through 16-byte loads and writes one word per workgroup to sink (device,
+ * >= 4 * n_blocks bytes); pkv_copy_probe copies bytes (multiple of 16).
+ * ------------------------------------------------------------------------ */
+int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_blocks, void* stream);
+int pkv_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

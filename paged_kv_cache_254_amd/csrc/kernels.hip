@@ -1,0 +1,800 @@
+// Device side of libpkv for gfx950 (CDNA4): kv_append, the split-KV paged
+// decode kernel, the log-sum-exp combine and two bandwidth probes, with their
+// C-ABI launch entry points.
+//
+// The operation: for every sequence b and query head hq,
+//   out[b][hq] = softmax(scale * q[b][hq] . K^T) V
+// over the seq_lens[b] tokens of KV head hq / G held in 16-token pages found
+// through the block table (evaltude docs "Transformer inference mechanics",
+// "What Q, K, and V do in causal attention" and "MHA versus MQA versus GQA";
+// "Inference Engines" chapter 17, "The Breakthrough", for pages and block
+// tables).  The softmax is computed online, keeping a running maximum and sum
+// so partial results rescale and combine exactly (byteknotlabs "Efficient
+// inference", "FlashAttention: exact attention without the matrix"); the KV
+// pages are split across wavefronts and merged afterwards (split-KV decode,
+// named as FlashDecoding in the CS336 lecture 10 notes).
+//
+// Mapping onto CDNA4.  One wavefront handles one chunk of pages of one
+// (sequence, KV head) pair for 16 query heads of its group at once:
+//   * scores S[t][g] = K[t][:] . Q[g][:] for the 16 tokens t of a page is one
+//     16x16 MFMA tile (tokens along M, query heads along N, head_dim along K);
+//   * the PV product O^T[d][g] += V^T[d][t] P^T[t][g] is D/16 MFMA tiles
+//     (head_dim along M, query heads along N, the page's tokens along K).
+// Both products put the query head on the MFMA column (lane % 16), so the
+// softmax state of head g (running max, sum) lives in the lanes of column g
+// and the score tile feeds the PV product as its B operand without any data
+// movement.  The page layouts are chosen so that every lane loads its MFMA
+// operands straight from HBM with 16-byte (K) or 8/16-byte (V) loads and each
+// load instruction of the wavefront covers a contiguous 512 B - 1 KiB:
+//   K page [D/X][16][X]: lane l of load i reads bytes 1024 i + 16 l;
+//   V page [D][16]:      lane (c = l/16, n = l%16) reads tokens 4c..4c+3 of
+//                        feature row 16 nb + n.
+// No LDS is needed for the tiles; each K/V tile is read from HBM once and used
+// for all query heads of the group from registers.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309417232121458176568f;
+constexpr float kLog2e = 1.442695040888963407359924681001892137f;
+
+// float -> bfloat16 bits, round to nearest even (NaN kept quiet): add half an
+// ulp of the 16 kept bits, minus one when the kept part is already even, and
+// truncate.
+__device__ inline uint32_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
+
+// ---------------------------------------------------------------------------
+// Per-dtype operand handling.
+//   NK: 16-byte K (and Q) registers per lane per page; NV: V registers per lane
+//   (4 elements each, tokens 4c..4c+3 of one feature row).
+// ---------------------------------------------------------------------------
+template <bool kBf16, int D>
+struct Ops;
+
+template <int D>
+struct Ops<true, D> {  // bfloat16
+  static constexpr int ES = 2;
+  static constexpr int NK = D * ES / 64;
+  static constexpr int NV = D / 16;
+  using VReg = u32x2;
+
+  __device__ static f32x4 qk(const u32x4 (&k)[NK], const u32x4 (&q)[NK]) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NK; i += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[i]),
+                                                   __builtin_bit_cast(bf16x8, q[i]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[i + 1]),
+                                                   __builtin_bit_cast(bf16x8, q[i + 1]), s1, 0, 0, 0);
+    }
+    return s0 + s1;
+  }
+
+  // Zero the V elements of tokens >= valid (lane holds tokens 4c..4c+3).
+  __device__ static VReg mask_v(VReg v, int c, int valid) {
+    uint32_t m0 = (4 * c + 0 < valid ? 0x0000ffffu : 0u) | (4 * c + 1 < valid ? 0xffff0000u : 0u);
+    uint32_t m1 = (4 * c + 2 < valid ? 0x0000ffffu : 0u) | (4 * c + 3 < valid ? 0xffff0000u : 0u);
+    v.x &= m0;
+    v.y &= m1;
+    return v;
+  }
+
+  // Rounds the four probabilities to the MFMA input type, accumulates the
+  // rounded values into l (so the weights that are summed are the weights that
+  // are applied) and runs acc[nb] += V^T[nb] * P^T.
+  __device__ static void pv(const VReg (&v)[NV], const float (&p)[4], float& l,
+                            f32x4 (&acc)[NV]) {
+    uint32_t b0 = f32_to_bf16(p[0]), b1 = f32_to_bf16(p[1]);
+    uint32_t b2 = f32_to_bf16(p[2]), b3 = f32_to_bf16(p[3]);
+    l += (bf16_to_f32(b0) + bf16_to_f32(b1)) + (bf16_to_f32(b2) + bf16_to_f32(b3));
+    u32x2 pk = {b0 | (b1 << 16), b2 | (b3 << 16)};
+    i16x4 pb = __builtin_bit_cast(i16x4, pk);
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v[nb]), pb,
+                                                           acc[nb], 0, 0, 0);
+  }
+
+  __device__ static void store_out(void* out, size_t elem_off, f32x4 x) {
+    u32x2 w = {f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16),
+               f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + elem_off) = w;
+  }
+};
+
+template <int D>
+struct Ops<false, D> {  // float32
+  static constexpr int ES = 4;
+  static constexpr int NK = D * ES / 64;
+  static constexpr int NV = D / 16;
+  using VReg = u32x4;
+
+  __device__ static f32x4 qk(const u32x4 (&k)[NK], const u32x4 (&q)[NK]) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].x),
+                                                __builtin_bit_cast(float, q[i].x), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].y),
+                                                __builtin_bit_cast(float, q[i].y), s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].z),
+                                                __builtin_bit_cast(float, q[i].z), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].w),
+                                                __builtin_bit_cast(float, q[i].w), s1, 0, 0, 0);
+    }
+    return s0 + s1;
+  }
+
+  __device__ static VReg mask_v(VReg v, int c, int valid) {
+    v.x = 4 * c + 0 < valid ? v.x : 0u;
+    v.y = 4 * c + 1 < valid ? v.y : 0u;
+    v.z = 4 * c + 2 < valid ? v.z : 0u;
+    v.w = 4 * c + 3 < valid ? v.w : 0u;
+    return v;
+  }
+
+  __device__ static void pv(const VReg (&v)[NV], const float (&p)[4], float& l,
+                            f32x4 (&acc)[NV]) {
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb) {
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].x), p[0],
+                                                     acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].y), p[1],
+                                                     acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].z), p[2],
+                                                     acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].w), p[3],
+                                                     acc[nb], 0, 0, 0);
+    }
+  }
+
+  __device__ static void store_out(void* out, size_t elem_off, f32x4 x) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + elem_off) = x;
+  }
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* part_o;
+  float* part_lse;
+  int32_t batch, n_q, n_kv, group, max_blocks, num_pages;
+  int32_t n_items, min_chunk, waves_per_chunk;
+  float scale_log2;
+};
+
+// Pages per sequence, exclusive prefix over the batch, into LDS (whole
+// workgroup).  s_prefix[b] = pages of sequences before b; s_prefix[batch] =
+// total.  A length outside [0, 16 * max_blocks] counts as zero pages.
+__device__ void build_prefix(const int32_t* __restrict__ seq_lens, int batch, int max_blocks,
+                             int32_t* s_prefix, int32_t* s_wsum) {
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int per = (batch + nthr - 1) / nthr;
+  const int b0 = min(batch, tid * per);
+  const int b1 = min(batch, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += pages_of_len(seq_lens[b], max_blocks);
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) s_wsum[wid] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += s_wsum[w];
+  int run = base + x - local;
+  for (int b = b0; b < b1; ++b) {
+    s_prefix[b] = run;
+    run += pages_of_len(seq_lens[b], max_blocks);
+  }
+  if (tid == nthr - 1) s_prefix[batch] = base + x;
+  __syncthreads();
+}
+
+// Largest b in [0, batch) with n_kv * prefix[b] <= f (f < total): the sequence
+// that owns flattened page f; it always holds at least one page.
+__device__ inline int find_seq(const int32_t* s_prefix, int batch, int n_kv, int f) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (n_kv * s_prefix[mid] <= f) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Sliding window of 64 block-table entries held one per lane, with the next 64
+// already requested; get(j) returns the page of logical block j (wave-uniform).
+struct BtWindow {
+  const int32_t* row;
+  int end, jw, cur, nxt;
+  __device__ void init(const int32_t* r, int j0, int j1, int lane) {
+    row = r;
+    end = j1;
+    jw = j0;
+    cur = (j0 + lane < j1) ? row[j0 + lane] : 0;
+    nxt = (j0 + kWave + lane < j1) ? row[j0 + kWave + lane] : 0;
+  }
+  __device__ int get(int j, int lane) {
+    if (j - jw >= kWave) {
+      jw += kWave;
+      cur = nxt;
+      nxt = (jw + kWave + lane < end) ? row[jw + kWave + lane] : 0;
+    }
+    return __builtin_amdgcn_readlane(cur, j - jw);
+  }
+};
+
+template <bool kBf16, int D>
+struct PageRegs {
+  using O = Ops<kBf16, D>;
+  u32x4 k[O::NK];
+  typename O::VReg v[O::NV];
+};
+
+template <bool kBf16, int D>
+__device__ inline void load_page(PageRegs<kBf16, D>& r, const char* kbase, const char* vbase,
+                                 int lane) {
+  using O = Ops<kBf16, D>;
+  const u32x4* kp = reinterpret_cast<const u32x4*>(kbase) + lane;
+#pragma unroll
+  for (int i = 0; i < O::NK; ++i) r.k[i] = kp[i * kWave];
+  const int c = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int nb = 0; nb < O::NV; ++nb)
+    r.v[nb] = *reinterpret_cast<const typename O::VReg*>(
+        vbase + O::ES * ((16 * nb + n) * kBlock + 4 * c));
+}
+
+// One page of the online softmax for the 16 query heads of this wavefront.
+template <bool kBf16, int D>
+__device__ inline void compute_page(const PageRegs<kBf16, D>& r, int valid,
+                                    const u32x4 (&qreg)[Ops<kBf16, D>::NK], float scale_log2,
+                                    int c, float& m, float& l,
+                                    f32x4 (&acc)[Ops<kBf16, D>::NV]) {
+  using O = Ops<kBf16, D>;
+  f32x4 s = O::qk(r.k, qreg);   // lane (c, n): tokens 4c + i, query head n
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = s[i] * scale_log2;
+  typename O::VReg v[O::NV];
+#pragma unroll
+  for (int nb = 0; nb < O::NV; ++nb) v[nb] = r.v[nb];
+  if (valid < kBlock) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * c + i < valid) ? x[i] : -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) v[nb] = O::mask_v(v[nb], c, valid);
+  }
+  float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  pm = fmaxf(pm, __shfl_xor(pm, 16));
+  pm = fmaxf(pm, __shfl_xor(pm, 32));
+  const float mn = fmaxf(m, pm);
+  const float alpha = __builtin_amdgcn_exp2f(m - mn);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mn);
+  l *= alpha;
+#pragma unroll
+  for (int nb = 0; nb < O::NV; ++nb) acc[nb] *= alpha;
+  m = mn;
+  O::pv(v, p, l, acc);
+}
+
+template <bool kBf16, int D>
+__device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j1, int n_pages,
+                                int seg_start, int chunk, int C, int gblk, int lane) {
+  using O = Ops<kBf16, D>;
+  constexpr int kTileBytes = kBlock * D * O::ES;
+  const int c = lane >> 4, n = lane & 15;
+  const int g = gblk * 16 + n;
+  const bool g_ok = g < a.group;
+  const int hq = h * a.group + g;
+  const int len = a.seq_lens[b];
+
+  // Query operand: lane (c, n) holds q[hq][(4i + c) * X .. +X) for each i.
+  u32x4 qreg[O::NK];
+  {
+    const char* qb = static_cast<const char*>(a.q) +
+                     (static_cast<size_t>(b) * a.n_q + (g_ok ? hq : 0)) * D * O::ES;
+#pragma unroll
+    for (int i = 0; i < O::NK; ++i) {
+      u32x4 t = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * i + c));
+      qreg[i] = g_ok ? t : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const char* kpool = static_cast<const char*>(a.k_pages);
+  const char* vpool = static_cast<const char*>(a.v_pages);
+  const size_t head_stride = static_cast<size_t>(kTileBytes);
+  const size_t page_stride = head_stride * a.n_kv;
+  BtWindow bw;
+  bw.init(a.block_table + static_cast<size_t>(b) * a.max_blocks, j0, j1, lane);
+  bool bad = false;
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc[O::NV];
+#pragma unroll
+  for (int nb = 0; nb < O::NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  PageRegs<kBf16, D> A, B;
+  {
+    int pg = bw.get(j0, lane);
+    if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) { bad = true; pg = 0; }
+    load_page(A, kpool + pg * page_stride + h * head_stride,
+              vpool + pg * page_stride + h * head_stride, lane);
+  }
+  const int last = n_pages - 1;
+  int j = j0;
+  // Double-buffered: the next page's loads are in flight while this page is
+  // computed.  At the end of the range the last page is requested again
+  // (cache hit) so that every iteration issues the same loads.
+  while (true) {
+    {
+      int jn = (j + 1 < j1) ? j + 1 : j;
+      int pg = bw.get(jn, lane);
+      if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) { bad = true; pg = 0; }
+      load_page(B, kpool + pg * page_stride + h * head_stride,
+                vpool + pg * page_stride + h * head_stride, lane);
+    }
+    compute_page<kBf16, D>(A, j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c, m,
+                           l, acc);
+    if (++j >= j1) break;
+    {
+      int jn = (j + 1 < j1) ? j + 1 : j;
+      int pg = bw.get(jn, lane);
+      if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) { bad = true; pg = 0; }
+      load_page(A, kpool + pg * page_stride + h * head_stride,
+                vpool + pg * page_stride + h * head_stride, lane);
+    }
+    compute_page<kBf16, D>(B, j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c, m,
+                           l, acc);
+    if (++j >= j1) break;
+  }
+
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  float inv = bad ? NAN : 1.0f / lt;
+  const int first_chunk = seg_start / C;
+  const int last_chunk = (seg_start + n_pages - 1) / C;
+  if (!g_ok) return;
+  if (first_chunk == last_chunk) {
+    const size_t row = (static_cast<size_t>(b) * a.n_q + hq) * D;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, acc[nb] * inv);
+  } else {
+    const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
+    float* po = a.part_o + (slot * a.group + g) * D;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb)
+      *reinterpret_cast<f32x4*>(po + 16 * nb + 4 * c) = acc[nb] * inv;
+    if (c == 0) a.part_lse[slot * a.group + g] = bad ? NAN : (m + __log2f(lt)) * kLn2;
+  }
+}
+
+template <bool kBf16, int D>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+split_kernel(DecodeArgs a) {
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  int32_t* s_wsum = smem + a.batch + 1;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wpc = a.waves_per_chunk;
+  const int chunk = blockIdx.x * (kWavesPerGroup / wpc) + wave / wpc;
+  const int gblk = wave % wpc;
+  if (chunk >= a.n_items || gblk * 16 >= a.group) return;
+  const int total = a.n_kv * s_prefix[a.batch];
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int64_t f64 = static_cast<int64_t>(chunk) * C;
+  if (f64 >= total) return;
+  int f = static_cast<int>(f64);
+  const int fend = static_cast<int>(min(f64 + C, static_cast<int64_t>(total)));
+
+  int b = find_seq(s_prefix, a.batch, a.n_kv, f);
+  int n = s_prefix[b + 1] - s_prefix[b];
+  int off = f - a.n_kv * s_prefix[b];
+  int h = off / n;
+  int j = off - h * n;
+  while (true) {
+    const int cnt = min(n - j, fend - f);
+    const int seg_start = a.n_kv * s_prefix[b] + h * n;
+    process_segment<kBf16, D>(a, b, h, j, j + cnt, n, seg_start, chunk, C, gblk, lane);
+    f += cnt;
+    if (f >= fend) break;
+    j = 0;
+    if (++h == a.n_kv) {
+      h = 0;
+      do {
+        ++b;
+        n = s_prefix[b + 1] - s_prefix[b];
+      } while (n == 0);
+    }
+  }
+}
+
+// Merge the partials of every (sequence, KV head) pair that spans several
+// chunks; write zero rows for empty sequences and NaN rows for invalid lengths.
+template <bool kBf16>
+__global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  int32_t* s_wsum = smem + a.batch + 1;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
+  const int pair = blockIdx.x;
+  const int b = pair / a.n_kv;
+  const int h = pair - b * a.n_kv;
+  const int n = s_prefix[b + 1] - s_prefix[b];
+  const int G = a.group;
+  const size_t row0 = (static_cast<size_t>(b) * a.n_q + static_cast<size_t>(h) * G) * D;
+  if (n == 0) {
+    const int len = a.seq_lens[b];
+    const float fill = (len == 0) ? 0.f : NAN;
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+      if (kBf16) static_cast<uint16_t*>(a.out)[row0 + i] = static_cast<uint16_t>(f32_to_bf16(fill));
+      else static_cast<float*>(a.out)[row0 + i] = fill;
+    }
+    return;
+  }
+  const int total = a.n_kv * s_prefix[a.batch];
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int seg_start = a.n_kv * s_prefix[b] + h * n;
+  const int c0 = seg_start / C;
+  const int c1 = (seg_start + n - 1) / C;
+  if (c0 == c1) return;
+  const size_t slot0 = static_cast<size_t>(c0) + pair;
+  const int nparts = c1 - c0 + 1;
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int g = i / D;
+    const int d = i - g * D;
+    float mx = -INFINITY;
+    for (int s = 0; s < nparts; ++s) mx = fmaxf(mx, a.part_lse[(slot0 + s) * G + g]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nparts; ++s) {
+      const float w = __expf(a.part_lse[(slot0 + s) * G + g] - mx);
+      num += w * a.part_o[((slot0 + s) * G + g) * D + d];
+      den += w;
+    }
+    const float r = num / den;
+    if (kBf16) static_cast<uint16_t*>(a.out)[row0 + i] = static_cast<uint16_t>(f32_to_bf16(r));
+    else static_cast<float*>(a.out)[row0 + i] = r;
+  }
+}
+
+// kv_append: one wavefront per (sequence, KV head); a bit copy of the new key
+// (16-byte pieces) and value (single elements) into slot pos % 16.
+template <int ES>
+__global__ void __launch_bounds__(256)
+append_kernel(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+              const int32_t* block_table, const int32_t* positions, int batch, int n_kv, int D,
+              int max_blocks, int num_pages) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int pair = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
+  if (pair >= batch * n_kv) return;
+  const int b = pair / n_kv;
+  const int h = pair - b * n_kv;
+  const int pos = positions[b];
+  if (pos < 0 || pos >= max_blocks * kBlock) return;
+  const int page = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
+  if (page < 0 || page >= num_pages) return;
+  const int slot = pos % kBlock;
+  constexpr int X = 16 / ES;
+  const size_t tile = static_cast<size_t>(page) * n_kv + h;  // (page, head) tile index
+  const char* ksrc = static_cast<const char*>(k_new) + static_cast<size_t>(pair) * D * ES;
+  char* kdst = static_cast<char*>(k_pages) + tile * kBlock * D * ES;
+  for (int i = lane; i < D / X; i += kWave)
+    *reinterpret_cast<u32x4*>(kdst + (static_cast<size_t>(i) * kBlock + slot) * 16) =
+        *reinterpret_cast<const u32x4*>(ksrc + 16 * i);
+  if (ES == 2) {
+    const uint16_t* vsrc = static_cast<const uint16_t*>(v_new) + static_cast<size_t>(pair) * D;
+    uint16_t* vdst = static_cast<uint16_t*>(v_pages) + tile * kBlock * D;
+    for (int d = lane; d < D; d += kWave) vdst[d * kBlock + slot] = vsrc[d];
+  } else {
+    const uint32_t* vsrc = static_cast<const uint32_t*>(v_new) + static_cast<size_t>(pair) * D;
+    uint32_t* vdst = static_cast<uint32_t*>(v_pages) + tile * kBlock * D;
+    for (int d = lane; d < D; d += kWave) vdst[d * kBlock + slot] = vsrc[d];
+  }
+}
+
+__global__ void __launch_bounds__(256)
+read_probe_kernel(const u32x4* __restrict__ buf, size_t n16, uint32_t* sink) {
+  uint32_t x = 0;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    u32x4 v = __builtin_nontemporal_load(buf + i);
+    x ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // Keep the loads live: one word per workgroup, written by the lane holding x.
+  x ^= __shfl_xor(x, 1);
+  if (threadIdx.x == 0) sink[blockIdx.x] = x;
+}
+
+__global__ void __launch_bounds__(256)
+copy_probe_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, size_t n16) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers.
+// ---------------------------------------------------------------------------
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_fail(const char* what, hipError_t e) {
+  return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct Resolved {
+  int n_items;
+  int min_chunk;
+  int wpc;
+  size_t lds;
+};
+
+using SplitFn = void (*)(DecodeArgs);
+
+SplitFn split_fn(int dtype, int head_dim) {
+  if (dtype == PKV_BF16) return head_dim == 128 ? split_kernel<true, 128> : split_kernel<true, 64>;
+  return head_dim == 128 ? split_kernel<false, 128> : split_kernel<false, 64>;
+}
+
+int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  int n_cu = 0;
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, reinterpret_cast<const void*>(split_fn(dtype, head_dim)), kWave * kWavesPerGroup, lds);
+  if (e != hipSuccess) return hip_fail("hipOccupancyMaxActiveBlocksPerMultiprocessor", e);
+  if (per_cu < 1) per_cu = 1;
+  *out = n_cu * per_cu * (kWavesPerGroup / waves_per_chunk(group));
+  return ok();
+}
+
+int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t batch, int32_t max_blocks_per_seq,
+                        int32_t num_pages, int32_t dtype) {
+  std::string f(fn);
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, f + ": dtype");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (block_size != kBlock) return fail(PKV_ERR_UNSUPPORTED, f + ": block_size must be 16");
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, f + ": n_q_heads must be a positive multiple of n_kv_heads");
+  if (n_q_heads / n_kv_heads > kMaxGroup)
+    return fail(PKV_ERR_UNSUPPORTED, f + ": more than 64 query heads per KV head");
+  if (batch < 0 || batch > kMaxBatch)
+    return fail(PKV_ERR_UNSUPPORTED, f + ": batch must be in [0, 16000]");
+  if (max_blocks_per_seq < 1 || num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARG, f + ": max_blocks_per_seq and num_pages must be >= 1");
+  if (static_cast<int64_t>(batch) * max_blocks_per_seq * n_kv_heads >= (int64_t{1} << 31))
+    return fail(PKV_ERR_UNSUPPORTED, f + ": batch * max_blocks_per_seq * n_kv_heads >= 2^31");
+  return PKV_OK;
+}
+
+int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch,
+                 const pkv_decode_opts* opts, Resolved* r) {
+  r->wpc = waves_per_chunk(group);
+  r->lds = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
+  r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages : kDefaultMinChunk;
+  if (opts && opts->n_items > 0) {
+    if (opts->n_items > kMaxItems)
+      return fail(PKV_ERR_INVALID_ARG, "decode: n_items above 2^22");
+    r->n_items = opts->n_items;
+    return PKV_OK;
+  }
+  return default_items(dtype, head_dim, group, r->lds, &r->n_items);
+}
+
+int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
+                  const void* k_pages, const void* v_pages, const int32_t* block_table,
+                  const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                  int32_t block_size, float scale, void* out, void* stream, int32_t batch,
+                  int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
+                  size_t workspace_bytes, const pkv_decode_opts* opts) {
+  int st = check_decode_shapes(fn, n_q_heads, n_kv_heads, head_dim, block_size, batch,
+                               max_blocks_per_seq, num_pages, dtype);
+  if (st != PKV_OK) return st;
+  std::string f(fn);
+  if (batch == 0) return ok();
+  if (!seq_lens || !out || !workspace || !aligned(seq_lens, 4) || !aligned(out, 16) ||
+      !aligned(workspace, 256))
+    return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned seq_lens/out/workspace");
+  if (do_split && (!q || !k_pages || !v_pages || !block_table || !aligned(q, 16) ||
+                   !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(block_table, 4)))
+    return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned q/k_pages/v_pages/block_table");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, f + ": scale is not finite");
+  const int group = n_q_heads / n_kv_heads;
+  Resolved r;
+  st = resolve_opts(dtype, head_dim, group, batch, opts, &r);
+  if (st != PKV_OK) return st;
+  const int64_t need = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
+  if (need < 0) return static_cast<int>(need);
+  if (workspace_bytes < static_cast<size_t>(need))
+    return fail(PKV_ERR_WORKSPACE, f + ": workspace needs " + std::to_string(need) + " bytes");
+
+  const int64_t slots = decode_slots(batch, n_kv_heads, r.n_items);
+  DecodeArgs a;
+  a.q = q;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = static_cast<float*>(workspace) + slots * group * head_dim;
+  a.batch = batch;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.group = group;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.n_items = r.n_items;
+  a.min_chunk = r.min_chunk;
+  a.waves_per_chunk = r.wpc;
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (do_split) {
+    const int chunks_per_group = kWavesPerGroup / r.wpc;
+    const int grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
+    hipLaunchKernelGGL(split_fn(dtype, head_dim), dim3(grid), dim3(kWave * kWavesPerGroup), r.lds,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("split kernel launch", e);
+  }
+  if (do_combine) {
+    auto fn_c = dtype == PKV_BF16 ? combine_kernel<true> : combine_kernel<false>;
+    hipLaunchKernelGGL(fn_c, dim3(batch * n_kv_heads), dim3(256), r.lds, s, a, head_dim);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("combine kernel launch", e);
+  }
+  return ok();
+}
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+using pkv::ok;
+
+extern "C" {
+
+int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                  const int32_t* block_table, const int32_t* positions, int32_t batch,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append: dtype");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append: head_dim must be 64 or 128");
+  if (block_size != pkv::kBlock) return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append: block_size must be 16");
+  if (batch < 0 || n_kv_heads < 1 || max_blocks_per_seq < 1 || num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_kv_append: bad batch/n_kv_heads/max_blocks/num_pages");
+  if (static_cast<int64_t>(batch) * n_kv_heads >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(batch) * max_blocks_per_seq >= (int64_t{1} << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append: batch too large");
+  if (batch == 0) return ok();
+  if (!k_new || !v_new || !k_pages || !v_pages || !block_table || !positions ||
+      !pkv::aligned(k_new, 16) || !pkv::aligned(v_new, 4) || !pkv::aligned(k_pages, 16) ||
+      !pkv::aligned(v_pages, 4) || !pkv::aligned(block_table, 4) || !pkv::aligned(positions, 4))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_kv_append: NULL or misaligned pointer");
+  const int pairs = batch * n_kv_heads;
+  const int grid = (pairs + pkv::kWavesPerGroup - 1) / pkv::kWavesPerGroup;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PKV_BF16)
+    hipLaunchKernelGGL(pkv::append_kernel<2>, dim3(grid), dim3(256), 0, s, k_new, v_new, k_pages,
+                       v_pages, block_table, positions, batch, n_kv_heads, head_dim,
+                       max_blocks_per_seq, num_pages);
+  else
+    hipLaunchKernelGGL(pkv::append_kernel<4>, dim3(grid), dim3(256), 0, s, k_new, v_new, k_pages,
+                       v_pages, block_table, positions, batch, n_kv_heads, head_dim,
+                       max_blocks_per_seq, num_pages);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::hip_fail("append kernel launch", e);
+  return ok();
+}
+
+int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                          int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                          void* out, void* stream, int32_t batch, int32_t max_blocks_per_seq,
+                          int32_t num_pages, int32_t dtype, void* workspace,
+                          size_t workspace_bytes, const pkv_decode_opts* opts) {
+  return pkv::decode_common(true, true, "pkv_paged_decode_attn", q, k_pages, v_pages, block_table,
+                            seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out,
+                            stream, batch, max_blocks_per_seq, num_pages, dtype, workspace,
+                            workspace_bytes, opts);
+}
+
+int pkv_paged_decode_split(const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                           int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                           void* out, void* stream, int32_t batch, int32_t max_blocks_per_seq,
+                           int32_t num_pages, int32_t dtype, void* workspace,
+                           size_t workspace_bytes, const pkv_decode_opts* opts) {
+  return pkv::decode_common(true, false, "pkv_paged_decode_split", q, k_pages, v_pages,
+                            block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
+                            scale, out, stream, batch, max_blocks_per_seq, num_pages, dtype,
+                            workspace, workspace_bytes, opts);
+}
+
+int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens,
+                    int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, void* out, int32_t dtype,
+                    const pkv_decode_opts* opts, void* stream) {
+  return pkv::decode_common(false, true, "pkv_lse_combine", nullptr, nullptr, nullptr, nullptr,
+                            seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, 1.0f, out,
+                            stream, batch, max_blocks_per_seq, 1, dtype,
+                            const_cast<void*>(workspace), workspace_bytes, opts);
+}
+
+int pkv_decode_default_items(int32_t dtype, int32_t head_dim, int32_t group, int32_t* out) {
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "pkv_decode_default_items: out is NULL");
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "dtype");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim");
+  if (group < 1 || group > pkv::kMaxGroup) return fail(PKV_ERR_UNSUPPORTED, "group");
+  return pkv::default_items(dtype, head_dim, group, (1 + pkv::kWavesPerGroup) * sizeof(int32_t), out);
+}
+
+int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_blocks, void* stream) {
+  if (!buf || !sink || bytes % 16 != 0 || !pkv::aligned(buf, 16) || !pkv::aligned(sink, 4) ||
+      n_blocks < 1)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_hbm_read_probe: bad argument");
+  hipLaunchKernelGGL(pkv::read_probe_kernel, dim3(n_blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const pkv::u32x4*>(buf), bytes / 16,
+                     static_cast<uint32_t*>(sink));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::hip_fail("read probe launch", e);
+  return ok();
+}
+
+int pkv_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes % 16 != 0 || !pkv::aligned(dst, 16) || !pkv::aligned(src, 16))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_copy_probe: bad argument");
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return pkv::hip_fail("copy probe device query", e);
+  hipLaunchKernelGGL(pkv::copy_probe_kernel, dim3(n_cu * 8), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<pkv::u32x4*>(dst),
+                     static_cast<const pkv::u32x4*>(src), bytes / 16);
+  e = hipGetLastError();
+  if (e != hipSuccess) return pkv::hip_fail("copy probe launch", e);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+"""Thin torch-facing wrappers over the libpkv C ABI (argument marshalling only;
+every step runs in the library's HIP kernels or host C++)."""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _lib
+from ._lib import PKV_BF16, PKV_F32, DecodeOpts, check, lib
+
+BLOCK_SIZE = 16
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _opts(n_items: int = 0, min_chunk_pages: int = 0):
+    return ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages)))
+
+
+# ----------------------------------------------------------------- host side
+def kv_bytes_per_token(n_layers: int, n_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    return int(lib.pkv_kv_bytes_per_token(n_layers, n_kv_heads, head_dim, elem_bytes))
+
+
+def kv_cache_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes) -> int:
+    return int(lib.pkv_kv_cache_bytes(n_layers, n_kv_heads, head_dim, seq_len, batch, elem_bytes))
+
+
+class PagePool:
+    """The library's host page pool (C++), with a free list in the given order."""
+
+    def __init__(self, num_pages: int, free_order: Optional[Sequence[int]] = None):
+        self._h = ctypes.c_void_p()
+        if free_order is None:
+            check(lib.pkv_pool_create(num_pages, None, ctypes.byref(self._h)), "pkv_pool_create")
+        else:
+            arr = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            check(lib.pkv_pool_create(num_pages, arr.ctypes.data_as(_lib._pi32), ctypes.byref(self._h)),
+                  "pkv_pool_create")
+        self.num_pages = num_pages
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value:
+            lib.pkv_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def num_free(self) -> int:
+        return check(lib.pkv_pool_num_free(self._h), "pkv_pool_num_free")
+
+    def reserve(self, seq_id: int, n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
+        n = ctypes.c_int32()
+        check(lib.pkv_seq_reserve(self._h, seq_id, n_tokens, block_size, ctypes.byref(n)), "pkv_seq_reserve")
+        return n.value
+
+    def release(self, seq_id: int) -> None:
+        check(lib.pkv_seq_release(self._h, seq_id), "pkv_seq_release")
+
+    def fork(self, parent: int, child: int) -> None:
+        check(lib.pkv_seq_fork(self._h, parent, child), "pkv_seq_fork")
+
+    def reserve_for_write(self, seq_id: int, position: int, block_size: int = BLOCK_SIZE):
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        check(lib.pkv_seq_reserve_for_write(self._h, seq_id, position, block_size, ctypes.byref(src),
+                                            ctypes.byref(dst)), "pkv_seq_reserve_for_write")
+        return None if src.value < 0 else (src.value, dst.value)
+
+    def num_blocks(self, seq_id: int) -> int:
+        n = ctypes.c_int32()
+        check(lib.pkv_seq_num_blocks(self._h, seq_id, ctypes.byref(n)), "pkv_seq_num_blocks")
+        return n.value
+
+    def block_table(self, seq_ids: Sequence[int], max_blocks: int) -> np.ndarray:
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        out = np.empty((len(ids), max_blocks), dtype=np.int32)
+        check(lib.pkv_build_block_table(self._h, ids.ctypes.data_as(_lib._pi64), len(ids), max_blocks,
+                                        out.ctypes.data_as(_lib._pi32)), "pkv_build_block_table")
+        return out
+
+
+def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_items: int) -> int:
+    return check(int(lib.pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)),
+                 "pkv_decode_workspace_bytes")
+
+
+def decode_default_items(dtype_code: int, head_dim: int, group: int) -> int:
+    n = ctypes.c_int32()
+    check(lib.pkv_decode_default_items(dtype_code, head_dim, group, ctypes.byref(n)), "pkv_decode_default_items")
+    return n.value
+
+
+def decode_plan(seq_lens: Sequence[int], n_kv_heads: int, max_blocks: int, n_items: int,
+                min_chunk_pages: int = 0):
+    """(chunk_pages, first_chunk[B][Hkv], last_chunk[B][Hkv]) as the kernels compute them."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B = len(lens)
+    C = ctypes.c_int32()
+    first = np.empty((B, n_kv_heads), dtype=np.int32)
+    last = np.empty((B, n_kv_heads), dtype=np.int32)
+    check(lib.pkv_decode_plan(lens.ctypes.data_as(_lib._pi32), B, n_kv_heads, BLOCK_SIZE, max_blocks, n_items,
+                              min_chunk_pages, ctypes.byref(C), first.ctypes.data_as(_lib._pi32),
+                              last.ctypes.data_as(_lib._pi32)), "pkv_decode_plan")
+    return C.value, first, last
+
+
+# --------------------------------------------------------------- device side
+def kv_append(k_new, v_new, k_pages, v_pages, block_table, positions, stream=None) -> None:
+    B, n_kv, D = k_new.shape
+    check(lib.pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                            _ptr(positions), B, n_kv, D, BLOCK_SIZE, block_table.shape[1], k_pages.shape[0],
+                            _dtype_code(k_new), _stream(stream)), "pkv_kv_append")
+
+
+class Decoder:
+    """Holds the resolved work split and a workspace for one decode shape."""
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype,
+                 n_items: int = 0, min_chunk_pages: int = 0, device="cuda"):
+        import torch
+        code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+        if n_items <= 0:
+            n_items = decode_default_items(code, head_dim, n_q_heads // n_kv_heads)
+        self.n_items = n_items
+        self.min_chunk_pages = min_chunk_pages
+        self.ws_bytes = decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
+        self.workspace = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=device)
+        self.shape = (batch, n_q_heads, n_kv_heads, head_dim)
+
+    def _args(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream):
+        B, Hq, D = q.shape
+        return (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hq,
+                k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B,
+                block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
+                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages))
+
+    def __call__(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
+        check(lib.pkv_paged_decode_attn(*self._args(q, k_pages, v_pages, block_table, seq_lens, scale, out,
+                                                    stream)), "pkv_paged_decode_attn")
+        return out
+
+    def split(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
+        check(lib.pkv_paged_decode_split(*self._args(q, k_pages, v_pages, block_table, seq_lens, scale, out,
+                                                     stream)), "pkv_paged_decode_split")
+
+    def combine(self, seq_lens, out, max_blocks: int, stream=None):
+        B, Hq, Hkv, D = self.shape
+        check(lib.pkv_lse_combine(_ptr(self.workspace), self.workspace.numel(), _ptr(seq_lens), B, Hq, Hkv, D,
+                                  BLOCK_SIZE, max_blocks, _ptr(out), _dtype_code(out),
+                                  _opts(self.n_items, self.min_chunk_pages), _stream(stream)),
+              "pkv_lse_combine")
+
+    def partials(self):
+        """Views (partial_o [slots][G][D], partial_lse [slots][G]) into the workspace."""
+        import torch
+        B, Hq, Hkv, D = self.shape
+        G = Hq // Hkv
+        slots = self.n_items + B * Hkv
+        f = self.workspace[: self.ws_bytes].view(torch.float32)
+        return f[: slots * G * D].view(slots, G, D), f[slots * G * D: slots * G * (D + 1)].view(slots, G)
+
+
+def paged_decode_attn(q, k_pages, v_pages, block_table, seq_lens, scale, out=None, n_items: int = 0,
+                      min_chunk_pages: int = 0, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    dec = Decoder(q.shape[0], q.shape[1], k_pages.shape[1], q.shape[2], q.dtype, n_items, min_chunk_pages,
+                  device=q.device)
+    return dec(q, k_pages, v_pages, block_table, seq_lens, scale, out, stream)
+
+
+def hbm_read_probe(buf, sink, n_blocks: int, stream=None) -> None:
+    check(lib.pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), n_blocks,
+                                 _stream(stream)), "pkv_hbm_read_probe")
+
+
+def copy_probe(dst, src, stream=None) -> None:
+    check(lib.pkv_copy_probe(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream)),
+          "pkv_copy_probe")

@@ -1,0 +1,258 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Small shapes are checked element by element; the full-size workloads are run
+in the launch configuration the benchmark times and checked on sampled rows
+(oracle computes them one by one) plus properties that hold at any size."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as OA
+
+from . import helpers as H
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_254_amd as m
+    return m
+
+
+def _run_step(pkv, c, n_items=0, min_chunk=0, out=None):
+    w = c.w
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), n_items, min_chunk)
+    out = torch.empty_like(c.q) if out is None else out
+    dec(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out)
+    torch.cuda.synchronize()
+    return out, dec
+
+
+# --------------------------------------------------------------- kv_append
+@pytest.mark.parametrize("name,dtype,D", [("append_f32_64", "f32", 64), ("append_bf16_128", "bf16", 128),
+                                          ("append_bf16_64", "bf16", 64), ("append_f32_128", "f32", 128)])
+def test_kv_append_bit_exact(pkv, name, dtype, D):
+    w = W.custom(name, 5, 8, 4, D, dtype, [0, 15, 16, 37, 100], pool_pages=40, seed=11)
+    c = H.setup(w, device="cuda", gen_device="cpu", poison=False)
+    H.log(f"append {name}")
+    k0, v0 = H.bits(c.k_pages), H.bits(c.v_pages)
+    ek, ev = OA.append(k0, v0, c.bt_np, c.cached, H.bits(c.k_new), H.bits(c.v_new), H.BS)
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bits(c.k_pages), ek)
+    assert np.array_equal(H.bits(c.v_pages), ev)
+
+
+def test_kv_append_skips_out_of_range(pkv):
+    w = W.custom("append_oob", 3, 2, 2, 64, "bf16", [3, 4, 5], pool_pages=4, seed=12)
+    c = H.setup(w, device="cuda", gen_device="cpu", poison=False)
+    before_k, before_v = H.bits(c.k_pages), H.bits(c.v_pages)
+    pos = torch.tensor([-1, 16 * c.max_blocks, 2], dtype=torch.int32, device="cuda")
+    bt = c.bt.clone()
+    bt[2, 0] = 99  # outside the 4-page pool
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, bt, pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bits(c.k_pages), before_k) and np.array_equal(H.bits(c.v_pages), before_v)
+
+
+# ------------------------------------------------------------ small parity
+SMALL = [
+    # name, B, Hq, Hkv, D, dtype, cached lengths, n_items, min_chunk
+    ("mha_f32_64", 3, 2, 2, 64, "f32", [0, 16, 40], 3, 1),
+    ("gqa2_f32_64", 2, 4, 2, 64, "f32", [37, 100], 0, 0),
+    ("gqa4_bf16_128", 4, 8, 2, 128, "bf16", [14, 15, 31, 300], 5, 2),
+    ("mqa16_bf16_128", 2, 16, 1, 128, "bf16", [200, 33], 4, 1),
+    ("g8_bf16_64", 3, 16, 2, 64, "bf16", [1, 65, 129], 7, 1),
+    ("g3_f32_128", 2, 6, 2, 128, "f32", [77, 5], 2, 4),
+    ("g24_bf16_128", 2, 48, 2, 128, "bf16", [50, 70], 3, 1),
+    ("g64_bf16_128", 1, 64, 1, 128, "bf16", [333], 6, 1),
+    ("g32_f32_64", 2, 32, 1, 64, "f32", [20, 90], 5, 1),
+    ("mha_bf16_128_one_chunk", 3, 4, 4, 128, "bf16", [10, 47, 90], 1, 64),
+    ("ragged_many", 9, 8, 4, 128, "bf16", [0, 1, 2, 15, 16, 17, 63, 64, 250], 11, 1),
+]
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached,n_items,min_chunk", SMALL, ids=[s[0] for s in SMALL])
+def test_small_parity(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, min_chunk):
+    P = sum((n + 16) // 16 for n in cached) + 5
+    w = W.custom(name, B, Hq, Hkv, D, dtype, cached, pool_pages=P, seed=zlib.crc32(name.encode()) % 1000)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    H.log(f"small {name}")
+    ref = H.oracle_full(c)
+    out, _ = _run_step(pkv, c, n_items, min_chunk)
+    H.assert_close(H.f64(out), ref, dtype, name)
+
+
+def test_tiny_f32_workload(pkv):
+    w = W.get("tiny_f32")
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    ref = H.oracle_full(c)
+    for n_items in (0, 1, 2, 3, 10):
+        c2 = H.setup(w, device="cuda", gen_device="cpu")
+        out, _ = _run_step(pkv, c2, n_items, 1)
+        mx, _, _ = H.assert_close(H.f64(out), ref, "f32", f"tiny n_items={n_items}")
+        H.log(f"tiny_f32 n_items={n_items} max abs {mx:.2e}")
+
+
+def test_split_partials_match_oracle(pkv):
+    w = W.custom("partials", 3, 8, 2, 128, "bf16", [70, 0, 200], pool_pages=25, seed=21)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    k, v = OA.append(H.f64(c.k_pages), H.f64(c.v_pages), c.bt_np, c.cached, H.f64(c.k_new),
+                     H.f64(c.v_new), H.BS)
+    qh = H.f64(c.q)
+    n_items = 7
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, n_items, 1)
+    dec.workspace.fill_(255)
+    out = torch.full_like(c.q, float("nan"))
+    dec.split(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out)
+    torch.cuda.synchronize()
+    po, pl = dec.partials()
+    po, pl = po.cpu().double().numpy(), pl.cpu().double().numpy()
+    C, first, last = pkv.decode_plan(c.attended, w.n_kv_heads, c.max_blocks, n_items, 1)
+    pages = [(int(n) + 15) // 16 for n in c.attended]
+    checked = 0
+    f = 0
+    for b in range(w.batch):
+        K, V = OA.gather(k, v, c.bt_np[b], int(c.attended[b]), H.BS)
+        for h in range(w.n_kv_heads):
+            n = pages[b]
+            for ch in range(first[b, h], last[b, h] + 1):
+                if first[b, h] == last[b, h] or first[b, h] < 0:
+                    continue
+                p0 = max(ch * C, f) - f
+                p1 = min((ch + 1) * C, f + n) - f
+                t0, t1 = 16 * p0, min(16 * p1, int(c.attended[b]))
+                slot = ch + b * w.n_kv_heads + h
+                for g in range(w.group):
+                    hq = h * w.group + g
+                    o_ref, lse_ref = OA.partial(qh[b, hq], K[t0:t1, h], V[t0:t1, h], w.scale)
+                    assert abs(pl[slot, g] - lse_ref) < 1e-3, (b, h, ch, g)
+                    assert np.abs(po[slot, g] - o_ref).max() < 1.5e-2
+                    checked += 1
+            f += n
+    assert checked > 20
+
+
+def test_invariances_and_determinism(pkv):
+    w = W.custom("inv", 4, 8, 2, 128, "bf16", [90, 3, 250, 40], pool_pages=40, seed=31)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    out1, _ = _run_step(pkv, c, 5, 1)
+    # same inputs again: bit-identical (no atomics, fixed reduction order)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, 5, 1)
+    out2 = torch.empty_like(c.q)
+    dec(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    # page relabelling: move every page's contents and rewrite the table
+    P = c.k_pages.shape[0]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(3)).to("cuda")
+    k2 = torch.empty_like(c.k_pages)
+    v2 = torch.empty_like(c.v_pages)
+    k2[perm] = c.k_pages
+    v2[perm] = c.v_pages
+    bt2 = torch.where(c.bt >= 0, perm[c.bt.clamp(min=0).long()].int(), c.bt)
+    out3 = torch.empty_like(c.q)
+    dec(c.q, k2, v2, bt2, c.seq_lens, w.scale, out3)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out3)
+    # batch independence: other sequences' queries changed -> sequence 2 unchanged
+    q4 = c.q.clone()
+    q4[[0, 1, 3]] = torch.randn_like(q4[[0, 1, 3]])
+    out4 = torch.empty_like(c.q)
+    dec(q4, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out4)
+    torch.cuda.synchronize()
+    assert torch.equal(out4[2], out1[2])
+    # a different split gives the same result within fp32 rounding of the combine
+    for n_items, mc in ((1, 1), (64, 1), (3, 4)):
+        dec2 = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, n_items, mc)
+        out5 = torch.empty_like(c.q)
+        dec2(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out5)
+        torch.cuda.synchronize()
+        d = (out5.float() - out1.float()).abs().max().item()
+        assert d <= 2 ** -7 * out1.float().abs().max().item(), (n_items, d)
+
+
+def test_closed_forms_on_gpu(pkv):
+    # constant V -> that constant; one-token sequence -> its V row; zero length -> zeros
+    w = W.custom("closed", 3, 4, 2, 128, "f32", [0, 0, 50], pool_pages=8, seed=41)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    c.seq_lens[0] = 0          # attend to nothing
+    c.v_pages[:] = 0.375       # every value row constant
+    c.v_new[:] = 0.375
+    out, _ = _run_step(pkv, c, 3, 1)
+    o = out.cpu().numpy()
+    assert (o[0] == 0).all()
+    np.testing.assert_allclose(o[1:], 0.375, rtol=0, atol=1e-6)
+    # sequence 1 attends only its appended token -> exactly v_new
+    w2 = W.custom("closed2", 2, 4, 2, 64, "bf16", [0, 7], pool_pages=4, seed=42)
+    c2 = H.setup(w2, device="cuda", gen_device="cpu")
+    out2, _ = _run_step(pkv, c2, 2, 1)
+    vn = c2.v_new[0].repeat_interleave(2, dim=0)
+    assert torch.equal(out2[0], vn)
+
+
+def test_invalid_inputs_give_nan_rows(pkv):
+    w = W.custom("bad", 3, 4, 2, 64, "bf16", [20, 20, 20], pool_pages=8, seed=51)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
+    bt = c.bt.clone()
+    bt[1, 1] = 1000                                  # page outside the pool
+    lens = c.seq_lens.clone()
+    lens[2] = 16 * c.max_blocks + 1                  # longer than the table
+    out = torch.zeros_like(c.q)
+    pkv.paged_decode_attn(c.q, c.k_pages, c.v_pages, bt, lens, w.scale, out=out, n_items=2, min_chunk_pages=1)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert torch.isfinite(o[0]).all() and torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
+
+
+# ------------------------------------------------------------- full sizes
+FULL = ["llama2_7b_mha", "llama3_8b_gqa", "long_70b_gqa", "long_70b_mqa", "llama3_8b_step"]
+
+
+def _sample_rows(w, attended, rng):
+    B, Hq, G = w.batch, w.n_q_heads, w.group
+    bs = sorted({0, B - 1, int(np.argmax(attended)), int(np.argmin(attended))} |
+                set(rng.integers(0, B, 2).tolist()))
+    rows = []
+    for b in bs:
+        for hq in sorted({0, Hq - 1, G - 1, min(Hq - 1, G), int(rng.integers(Hq))}):
+            rows.append((b, hq))
+    return rows
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(pkv, name):
+    w = W.get(name)
+    layers = [0, w.n_layers - 1] if w.n_layers > 1 else [0]
+    for layer in layers:
+        H.log(f"full {name} layer {layer}: setup")
+        c = H.setup(w, layer=layer, device="cuda", poison=True)
+        rng = np.random.default_rng(layer + 7)
+        rows = _sample_rows(w, c.attended, rng)
+        refs = H.oracle_rows(c, rows)
+        vmax = float(torch.nan_to_num(c.v_pages.float(), nan=0.0).abs().max())
+        vmax = max(vmax, float(c.v_new.float().abs().max()))
+        H.log(f"full {name} layer {layer}: oracle rows done ({len(rows)})")
+        out, dec = _run_step(pkv, c)
+        got = np.stack([H.f64(out[b, hq]) for b, hq in rows])
+        mx, mean, rel = H.assert_close(got, np.stack(refs), w.dtype, name)
+        H.log(f"full {name} layer {layer}: n_items={dec.n_items} max {mx:.2e} mean {mean:.2e} rel {rel:.2e}")
+        o = out.float()
+        assert torch.isfinite(o).all()
+        assert o.abs().max().item() <= vmax * (1 + 2 ** -7)   # a convex combination of values
+        out2 = torch.empty_like(out)
+        dec(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out2)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2)
+        del c, out, out2, dec
+        torch.cuda.empty_cache()
