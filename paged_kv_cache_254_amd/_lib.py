@@ -34,6 +34,15 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
                       " or `python paged_kv_cache_254_amd/build.py`")
 
+# One HIP runtime per process: torch ships its own libamdhip64 (same SONAME as
+# the system one libpkv.so links against).  Loading torch first makes the
+# dynamic loader satisfy libpkv.so's dependency with torch's already-loaded
+# runtime, so device pointers and streams from torch are valid in the library.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
+
 lib = ctypes.CDLL(LIB_PATH)
 
 _i32, _i64, _u64, _f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,

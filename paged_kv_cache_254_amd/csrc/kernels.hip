@@ -63,6 +63,15 @@ __device__ inline uint32_t f32_to_bf16(float f) {
 
 __device__ inline float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
+// Element i of a 4 x 32-bit register group, reinterpreted as float.  The
+// element is copied to a scalar before the reinterpretation: applying
+// __builtin_bit_cast to a vector swizzle (v.y) directly compiles to element 0.
+template <int I>
+__device__ inline float lane_f32(u32x4 v) {
+  const uint32_t u = v[I];
+  return __builtin_bit_cast(float, u);
+}
+
 // ---------------------------------------------------------------------------
 // Per-dtype operand handling.
 //   NK: 16-byte K (and Q) registers per lane per page; NV: V registers per lane
@@ -133,14 +142,14 @@ struct Ops<false, D> {  // float32
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].x),
-                                                __builtin_bit_cast(float, q[i].x), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].y),
-                                                __builtin_bit_cast(float, q[i].y), s1, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].z),
-                                                __builtin_bit_cast(float, q[i].z), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, k[i].w),
-                                                __builtin_bit_cast(float, q[i].w), s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<0>(k[i]),
+                                                lane_f32<0>(q[i]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<1>(k[i]),
+                                                lane_f32<1>(q[i]), s1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<2>(k[i]),
+                                                lane_f32<2>(q[i]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<3>(k[i]),
+                                                lane_f32<3>(q[i]), s1, 0, 0, 0);
     }
     return s0 + s1;
   }
@@ -158,13 +167,13 @@ struct Ops<false, D> {  // float32
     l += (p[0] + p[1]) + (p[2] + p[3]);
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb) {
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].x), p[0],
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<0>(v[nb]), p[0],
                                                      acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].y), p[1],
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<1>(v[nb]), p[1],
                                                      acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].z), p[2],
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<2>(v[nb]), p[2],
                                                      acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, v[nb].w), p[3],
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<3>(v[nb]), p[3],
                                                      acc[nb], 0, 0, 0);
     }
   }

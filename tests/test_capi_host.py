@@ -228,3 +228,17 @@ def test_append_rejects_bad_arguments():
     assert f(0, *base[1:]) == _lib.PKV_ERR_INVALID_ARG
     assert f(*base[:12], 3, None) == _lib.PKV_ERR_UNSUPPORTED
     assert f(*base[:6], 0, *base[7:]) == _lib.PKV_OK  # empty batch: nothing to do
+
+
+def test_single_hip_runtime_in_process():
+    # libpkv.so must share torch's HIP runtime (two runtimes cannot exchange
+    # device pointers or streams).  Run in a fresh interpreter that imports the
+    # package before torch, the order that used to load two runtimes.
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import paged_kv_cache_254_amd; import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'amdhip64' in l}))"
+            % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    libs = eval(out.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
