@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the copy kernel on 1 GiB three times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -182,6 +184,14 @@ def main():
 
     device = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            pkv.copy_probe(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "launches": 3}))
+        return
     w = W.get(args.workload)
     log(f"setup {w.name}")
     S = setup(w, device)
