@@ -39,6 +39,11 @@
 
 #include "pkv_internal.h"
 
+// Pages each wavefront keeps in flight ahead of the one it computes.
+#ifndef PKV_PREFETCH_PAGES
+#define PKV_PREFETCH_PAGES 2
+#endif
+
 namespace pkv {
 namespace {
 
@@ -47,21 +52,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.693147180559945309417232121458176568f;
 constexpr float kLog2e = 1.442695040888963407359924681001892137f;
-
-// float -> bfloat16 bits, round to nearest even (NaN kept quiet): add half an
-// ulp of the 16 kept bits, minus one when the kept part is already even, and
-// truncate.
-__device__ inline uint32_t f32_to_bf16(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ inline float bf16_to_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
 // Element i of a 4 x 32-bit register group, reinterpreted as float.  The
 // element is copied to a scalar before the reinterpretation: applying
@@ -113,21 +107,21 @@ struct Ops<true, D> {  // bfloat16
   // are applied) and runs acc[nb] += V^T[nb] * P^T.
   __device__ static void pv(const VReg (&v)[NV], const float (&p)[4], float& l,
                             f32x4 (&acc)[NV]) {
-    uint32_t b0 = f32_to_bf16(p[0]), b1 = f32_to_bf16(p[1]);
-    uint32_t b2 = f32_to_bf16(p[2]), b3 = f32_to_bf16(p[3]);
-    l += (bf16_to_f32(b0) + bf16_to_f32(b1)) + (bf16_to_f32(b2) + bf16_to_f32(b3));
-    u32x2 pk = {b0 | (b1 << 16), b2 | (b3 << 16)};
-    i16x4 pb = __builtin_bit_cast(i16x4, pk);
+    const bf16x4 pb = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                       static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+    l += (static_cast<float>(pb[0]) + static_cast<float>(pb[1])) +
+         (static_cast<float>(pb[2]) + static_cast<float>(pb[3]));
+    const i16x4 pk = __builtin_bit_cast(i16x4, pb);
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v[nb]), pb,
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v[nb]), pk,
                                                            acc[nb], 0, 0, 0);
   }
 
   __device__ static void store_out(void* out, size_t elem_off, f32x4 x) {
-    u32x2 w = {f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16),
-               f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + elem_off) = w;
+    const bf16x4 w = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1]),
+                      static_cast<__bf16>(x[2]), static_cast<__bf16>(x[3])};
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + elem_off) = w;
   }
 };
 
@@ -241,27 +235,14 @@ __device__ inline int find_seq(const int32_t* s_prefix, int batch, int n_kv, int
   return lo;
 }
 
-// Sliding window of 64 block-table entries held one per lane, with the next 64
-// already requested; get(j) returns the page of logical block j (wave-uniform).
-struct BtWindow {
-  const int32_t* row;
-  int end, jw, cur, nxt;
-  __device__ void init(const int32_t* r, int j0, int j1, int lane) {
-    row = r;
-    end = j1;
-    jw = j0;
-    cur = (j0 + lane < j1) ? row[j0 + lane] : 0;
-    nxt = (j0 + kWave + lane < j1) ? row[j0 + kWave + lane] : 0;
-  }
-  __device__ int get(int j, int lane) {
-    if (j - jw >= kWave) {
-      jw += kWave;
-      cur = nxt;
-      nxt = (jw + kWave + lane < end) ? row[jw + kWave + lane] : 0;
-    }
-    return __builtin_amdgcn_readlane(cur, j - jw);
-  }
-};
+// Wave-uniform value in a scalar register (every lane holds the same value).
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The block table is read-only during a launch; reading it through the
+// constant address space with a wave-uniform index makes every page-id read a
+// scalar load (scalar cache, its own counter), so it never waits behind the
+// vector loads of K/V tiles in flight.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
 
 template <bool kBf16, int D>
 struct PageRegs {
@@ -270,23 +251,58 @@ struct PageRegs {
   typename O::VReg v[O::NV];
 };
 
+// Buffer-resource word 3 for raw (untyped) buffer loads on CDNA: 32-bit data
+// format, no swizzle, no index stride.
+#ifndef PKV_RSRC_WORD3
+#define PKV_RSRC_WORD3 0x00020000
+#endif
+// Cache-policy bits of the K/V tile loads: non-temporal (each tile is read
+// once per launch, so it should not displace other lines; ~10% faster than
+// the default policy on the 16 x 4096 MHA layer).
+#ifndef PKV_KV_LOAD_AUX
+#define PKV_KV_LOAD_AUX 2
+#endif
+
+// Issues the loads of one (page, KV head) tile.  kbase/vbase are wave-uniform
+// and become the base of a buffer resource whose range is exactly one tile, so
+// the per-lane offsets (koff = 16 * lane, voff = elem * (16 n + 4 c)) stay in
+// one register and an offset past the tile reads zero instead of faulting.
 template <bool kBf16, int D>
 __device__ inline void load_page(PageRegs<kBf16, D>& r, const char* kbase, const char* vbase,
-                                 int lane) {
+                                 uint32_t koff, uint32_t voff) {
   using O = Ops<kBf16, D>;
-  const u32x4* kp = reinterpret_cast<const u32x4*>(kbase) + lane;
+  constexpr int kTileBytes = kBlock * D * O::ES;
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), 0, kTileBytes, PKV_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), 0, kTileBytes, PKV_RSRC_WORD3);
 #pragma unroll
-  for (int i = 0; i < O::NK; ++i) r.k[i] = kp[i * kWave];
-  const int c = lane >> 4, n = lane & 15;
+  for (int i = 0; i < O::NK; ++i)
+    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 1024 * i, 0, PKV_KV_LOAD_AUX);
 #pragma unroll
-  for (int nb = 0; nb < O::NV; ++nb)
-    r.v[nb] = *reinterpret_cast<const typename O::VReg*>(
-        vbase + O::ES * ((16 * nb + n) * kBlock + 4 * c));
+  for (int nb = 0; nb < O::NV; ++nb) {
+    if constexpr (kBf16)
+      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + O::ES * 16 * kBlock * nb, 0,
+                                                     PKV_KV_LOAD_AUX);
+    else
+      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + O::ES * 16 * kBlock * nb, 0,
+                                                      PKV_KV_LOAD_AUX);
+  }
 }
 
+// Largest growth of a score (log2 units) over the running maximum that is
+// accepted without rescaling: exponentials stay <= 2^8, far from overflow in
+// fp32 accumulation and exactly representable in range for bf16.
+constexpr float kLazyRescale = 8.0f;
+
 // One page of the online softmax for the 16 query heads of this wavefront.
+// The running maximum m of a query head is shared by the four lanes of its
+// column; it is raised (and the sum and accumulator rescaled) only when some
+// score of the page exceeds it by more than kLazyRescale, which one wave-wide
+// vote detects.  Between raises, m is an upper bound minus at most 8, so
+// exp2(x - m) <= 2^8, and the final division by the sum is unchanged.
 template <bool kBf16, int D>
-__device__ inline void compute_page(const PageRegs<kBf16, D>& r, int valid,
+__device__ inline void compute_page(PageRegs<kBf16, D>& r, int valid,
                                     const u32x4 (&qreg)[Ops<kBf16, D>::NK], float scale_log2,
                                     int c, float& m, float& l,
                                     f32x4 (&acc)[Ops<kBf16, D>::NV]) {
@@ -295,35 +311,37 @@ __device__ inline void compute_page(const PageRegs<kBf16, D>& r, int valid,
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = s[i] * scale_log2;
-  typename O::VReg v[O::NV];
-#pragma unroll
-  for (int nb = 0; nb < O::NV; ++nb) v[nb] = r.v[nb];
   if (valid < kBlock) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (4 * c + i < valid) ? x[i] : -INFINITY;
 #pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb) v[nb] = O::mask_v(v[nb], c, valid);
+    for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::mask_v(r.v[nb], c, valid);
   }
-  float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  pm = fmaxf(pm, __shfl_xor(pm, 16));
-  pm = fmaxf(pm, __shfl_xor(pm, 32));
-  const float mn = fmaxf(m, pm);
-  const float alpha = __builtin_amdgcn_exp2f(m - mn);
+  const float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__builtin_amdgcn_ballot_w64(pm > m + kLazyRescale) != 0) {
+    float cm = fmaxf(pm, __shfl_xor(pm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    const float mn = fmaxf(m, cm);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) acc[nb] *= alpha;
+    m = mn;
+  }
   float p[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mn);
-  l *= alpha;
-#pragma unroll
-  for (int nb = 0; nb < O::NV; ++nb) acc[nb] *= alpha;
-  m = mn;
-  O::pv(v, p, l, acc);
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m);
+  O::pv(r.v, p, l, acc);
 }
 
-template <bool kBf16, int D>
+// Pages [j0, j1) of the (b, h) pair for query heads gblk*16 .. gblk*16+15.
+// kDepth pages are in flight ahead of the one being computed.
+template <bool kBf16, int D, int kDepth>
 __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j1, int n_pages,
                                 int seg_start, int chunk, int C, int gblk, int lane) {
   using O = Ops<kBf16, D>;
   constexpr int kTileBytes = kBlock * D * O::ES;
+  constexpr int kBufs = kDepth + 1;
   const int c = lane >> 4, n = lane & 15;
   const int g = gblk * 16 + n;
   const bool g_ok = g < a.group;
@@ -342,57 +360,57 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
     }
   }
 
-  const char* kpool = static_cast<const char*>(a.k_pages);
-  const char* vpool = static_cast<const char*>(a.v_pages);
-  const size_t head_stride = static_cast<size_t>(kTileBytes);
-  const size_t page_stride = head_stride * a.n_kv;
-  BtWindow bw;
-  bw.init(a.block_table + static_cast<size_t>(b) * a.max_blocks, j0, j1, lane);
+  const size_t head_off = static_cast<size_t>(h) * kTileBytes;
+  const size_t page_stride = static_cast<size_t>(kTileBytes) * a.n_kv;
+  const char* kpool = static_cast<const char*>(a.k_pages) + head_off;
+  const char* vpool = static_cast<const char*>(a.v_pages) + head_off;
+  const const_i32* bt_row =
+      (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
+  const uint32_t koff = 16u * lane;
+  const uint32_t voff = O::ES * (n * kBlock + 4 * c);
   bool bad = false;
+  // Page of logical block j (clamped to the range's last block), checked
+  // against the pool: an entry outside it is never dereferenced.
+  auto issue = [&](PageRegs<kBf16, D>& r, int j) {
+    int pg = bt_row[min(j, j1 - 1)];
+    if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) {
+      bad = true;
+      pg = 0;
+    }
+    const size_t off = static_cast<size_t>(pg) * page_stride;
+    load_page(r, kpool + off, vpool + off, koff, voff);
+  };
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc[O::NV];
 #pragma unroll
   for (int nb = 0; nb < O::NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  PageRegs<kBf16, D> A, B;
-  {
-    int pg = bw.get(j0, lane);
-    if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) { bad = true; pg = 0; }
-    load_page(A, kpool + pg * page_stride + h * head_stride,
-              vpool + pg * page_stride + h * head_stride, lane);
-  }
+  PageRegs<kBf16, D> buf[kBufs];
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) issue(buf[s], j0 + s);
   const int last = n_pages - 1;
   int j = j0;
-  // Double-buffered: the next page's loads are in flight while this page is
-  // computed.  At the end of the range the last page is requested again
-  // (cache hit) so that every iteration issues the same loads.
-  while (true) {
-    {
-      int jn = (j + 1 < j1) ? j + 1 : j;
-      int pg = bw.get(jn, lane);
-      if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) { bad = true; pg = 0; }
-      load_page(B, kpool + pg * page_stride + h * head_stride,
-                vpool + pg * page_stride + h * head_stride, lane);
+  // Ring of kDepth + 1 register buffers: every step requests page j + kDepth
+  // (the range's last page again near the end: a cache hit) and computes page
+  // j, so every step issues the same loads.
+  while (j < j1) {
+#pragma unroll
+    for (int s = 0; s < kBufs; ++s) {
+      // Keep the compiler from sinking these loads below the compute: the
+      // requests must be in flight while this page is processed.
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[(s + kDepth) % kBufs], j + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_page<kBf16, D>(buf[s], j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c,
+                             m, l, acc);
+      if (++j >= j1) break;
     }
-    compute_page<kBf16, D>(A, j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c, m,
-                           l, acc);
-    if (++j >= j1) break;
-    {
-      int jn = (j + 1 < j1) ? j + 1 : j;
-      int pg = bw.get(jn, lane);
-      if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) { bad = true; pg = 0; }
-      load_page(A, kpool + pg * page_stride + h * head_stride,
-                vpool + pg * page_stride + h * head_stride, lane);
-    }
-    compute_page<kBf16, D>(B, j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c, m,
-                           l, acc);
-    if (++j >= j1) break;
   }
 
   float lt = l + __shfl_xor(l, 16);
   lt += __shfl_xor(lt, 32);
-  float inv = bad ? NAN : 1.0f / lt;
+  const float inv = bad ? NAN : 1.0f / lt;
   const int first_chunk = seg_start / C;
   const int last_chunk = (seg_start + n_pages - 1) / C;
   if (!g_ok) return;
@@ -410,8 +428,15 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
   }
 }
 
-template <bool kBf16, int D>
+// Minimum wavefronts per SIMD the split kernel is compiled for (caps its
+// registers at 512 / N per lane).
+#ifndef PKV_SPLIT_WAVES_PER_EU
+#define PKV_SPLIT_WAVES_PER_EU 2
+#endif
+
+template <bool kBf16, int D, int kDepth>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
 split_kernel(DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
@@ -419,27 +444,28 @@ split_kernel(DecodeArgs a) {
   build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = uni(threadIdx.x / kWave);
   const int wpc = a.waves_per_chunk;
   const int chunk = blockIdx.x * (kWavesPerGroup / wpc) + wave / wpc;
   const int gblk = wave % wpc;
   if (chunk >= a.n_items || gblk * 16 >= a.group) return;
-  const int total = a.n_kv * s_prefix[a.batch];
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
   const int C = chunk_pages(total, a.n_items, a.min_chunk);
   const int64_t f64 = static_cast<int64_t>(chunk) * C;
   if (f64 >= total) return;
   int f = static_cast<int>(f64);
   const int fend = static_cast<int>(min(f64 + C, static_cast<int64_t>(total)));
 
-  int b = find_seq(s_prefix, a.batch, a.n_kv, f);
-  int n = s_prefix[b + 1] - s_prefix[b];
-  int off = f - a.n_kv * s_prefix[b];
+  int b = uni(find_seq(s_prefix, a.batch, a.n_kv, f));
+  int pb = uni(s_prefix[b]);
+  int n = uni(s_prefix[b + 1]) - pb;
+  int off = f - a.n_kv * pb;
   int h = off / n;
   int j = off - h * n;
   while (true) {
     const int cnt = min(n - j, fend - f);
-    const int seg_start = a.n_kv * s_prefix[b] + h * n;
-    process_segment<kBf16, D>(a, b, h, j, j + cnt, n, seg_start, chunk, C, gblk, lane);
+    const int seg_start = a.n_kv * pb + h * n;
+    process_segment<kBf16, D, kDepth>(a, b, h, j, j + cnt, n, seg_start, chunk, C, gblk, lane);
     f += cnt;
     if (f >= fend) break;
     j = 0;
@@ -447,33 +473,44 @@ split_kernel(DecodeArgs a) {
       h = 0;
       do {
         ++b;
-        n = s_prefix[b + 1] - s_prefix[b];
+        pb = uni(s_prefix[b]);
+        n = uni(s_prefix[b + 1]) - pb;
       } while (n == 0);
     }
   }
 }
 
-// Merge the partials of every (sequence, KV head) pair that spans several
-// chunks; write zero rows for empty sequences and NaN rows for invalid lengths.
+// Merge the partials of one output row (sequence b, query head hq) whose KV
+// pair spans several chunks: out = sum_i w_i o_i / sum_i w_i with
+// w_i = exp(lse_i - max lse).  One workgroup per row: a block-wide maximum of
+// the lse, then 256 / D slices of threads each accumulate every (256/D)-th
+// partial for all D features, and the slices are summed through LDS.  Rows of
+// empty sequences become zeros, rows of invalid lengths NaN.
 template <bool kBf16>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
   int32_t* s_wsum = smem + a.batch + 1;
+  __shared__ float s_red[256];
+  __shared__ float s_den[256];
   build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
-  const int pair = blockIdx.x;
-  const int b = pair / a.n_kv;
-  const int h = pair - b * a.n_kv;
-  const int n = s_prefix[b + 1] - s_prefix[b];
   const int G = a.group;
-  const size_t row0 = (static_cast<size_t>(b) * a.n_q + static_cast<size_t>(h) * G) * D;
+  const int row = blockIdx.x;                 // b * n_q + hq
+  const int b = row / a.n_q;
+  const int hq = row - b * a.n_q;
+  const int h = hq / G;
+  const int g = hq - h * G;
+  const int pair = b * a.n_kv + h;
+  const int n = s_prefix[b + 1] - s_prefix[b];
+  const size_t row0 = static_cast<size_t>(row) * D;
+  const int tid = threadIdx.x;
+  auto store = [&](int d, float x) {
+    if (kBf16) static_cast<__bf16*>(a.out)[row0 + d] = static_cast<__bf16>(x);
+    else static_cast<float*>(a.out)[row0 + d] = x;
+  };
   if (n == 0) {
-    const int len = a.seq_lens[b];
-    const float fill = (len == 0) ? 0.f : NAN;
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-      if (kBf16) static_cast<uint16_t*>(a.out)[row0 + i] = static_cast<uint16_t>(f32_to_bf16(fill));
-      else static_cast<float*>(a.out)[row0 + i] = fill;
-    }
+    const float fill = (a.seq_lens[b] == 0) ? 0.f : NAN;
+    for (int d = tid; d < D; d += blockDim.x) store(d, fill);
     return;
   }
   const int total = a.n_kv * s_prefix[a.batch];
@@ -484,20 +521,42 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   if (c0 == c1) return;
   const size_t slot0 = static_cast<size_t>(c0) + pair;
   const int nparts = c1 - c0 + 1;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int g = i / D;
-    const int d = i - g * D;
-    float mx = -INFINITY;
-    for (int s = 0; s < nparts; ++s) mx = fmaxf(mx, a.part_lse[(slot0 + s) * G + g]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nparts; ++s) {
-      const float w = __expf(a.part_lse[(slot0 + s) * G + g] - mx);
-      num += w * a.part_o[((slot0 + s) * G + g) * D + d];
-      den += w;
+  const float* lse = a.part_lse + slot0 * G + g;
+  const float* po = a.part_o + (slot0 * G + g) * D;
+  const size_t stride_o = static_cast<size_t>(G) * D;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < nparts; s += blockDim.x) mx = fmaxf(mx, lse[static_cast<size_t>(s) * G]);
+  s_red[tid] = mx;
+  __syncthreads();
+  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+    __syncthreads();
+  }
+  mx = s_red[0];
+  __syncthreads();
+
+  const int n_slices = blockDim.x / D;
+  const int d = tid % D;
+  const int slice = tid / D;
+  float acc = 0.f, den = 0.f;
+  if (slice < n_slices) {
+    for (int s = slice; s < nparts; s += n_slices) {
+      const float wgt = __expf(lse[static_cast<size_t>(s) * G] - mx);
+      acc += wgt * po[static_cast<size_t>(s) * stride_o + d];
+      den += wgt;
     }
-    const float r = num / den;
-    if (kBf16) static_cast<uint16_t*>(a.out)[row0 + i] = static_cast<uint16_t>(f32_to_bf16(r));
-    else static_cast<float*>(a.out)[row0 + i] = r;
+  }
+  s_red[tid] = acc;
+  s_den[tid] = den;
+  __syncthreads();
+  if (tid < D) {
+    float num = 0.f, dsum = 0.f;
+    for (int sl = 0; sl < n_slices; ++sl) {
+      num += s_red[sl * D + tid];
+      dsum += s_den[sl * D];
+    }
+    store(tid, num / dsum);
   }
 }
 
@@ -574,9 +633,12 @@ struct Resolved {
 
 using SplitFn = void (*)(DecodeArgs);
 
+constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
+
 SplitFn split_fn(int dtype, int head_dim) {
-  if (dtype == PKV_BF16) return head_dim == 128 ? split_kernel<true, 128> : split_kernel<true, 64>;
-  return head_dim == 128 ? split_kernel<false, 128> : split_kernel<false, 64>;
+  if (dtype == PKV_BF16)
+    return head_dim == 128 ? split_kernel<true, 128, kPrefetchPages> : split_kernel<true, 64, kPrefetchPages>;
+  return head_dim == 128 ? split_kernel<false, 128, kPrefetchPages> : split_kernel<false, 64, kPrefetchPages>;
 }
 
 int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
@@ -688,7 +750,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   }
   if (do_combine) {
     auto fn_c = dtype == PKV_BF16 ? combine_kernel<true> : combine_kernel<false>;
-    hipLaunchKernelGGL(fn_c, dim3(batch * n_kv_heads), dim3(256), r.lds, s, a, head_dim);
+    hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), r.lds, s, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
