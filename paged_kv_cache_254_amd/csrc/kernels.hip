@@ -482,16 +482,18 @@ split_kernel(DecodeArgs a) {
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
 // pair spans several chunks: out = sum_i w_i o_i / sum_i w_i with
-// w_i = exp(lse_i - max lse).  One workgroup per row: a block-wide maximum of
-// the lse, then 256 / D slices of threads each accumulate every (256/D)-th
-// partial for all D features, and the slices are summed through LDS.  Rows of
-// empty sequences become zeros, rows of invalid lengths NaN.
+// w_i = exp(lse_i - max lse).  One workgroup per row.  After a block-wide
+// maximum of the lse, the 256 threads form 256 / (D / 8) slices of D / 8
+// threads; thread (slice, t) accumulates features 8t .. 8t+7 (two 16-byte
+// loads) of every n_slices-th partial, and the slices are summed through
+// LDS.  Rows of empty sequences become zeros, rows of invalid lengths NaN.
 template <bool kBf16>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
   int32_t* s_wsum = smem + a.batch + 1;
   __shared__ float s_red[256];
+  __shared__ f32x4 s_acc[2 * 256];
   __shared__ float s_den[256];
   build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
   const int G = a.group;
@@ -534,27 +536,31 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
     __syncthreads();
   }
   mx = s_red[0];
-  __syncthreads();
 
-  const int n_slices = blockDim.x / D;
-  const int d = tid % D;
-  const int slice = tid / D;
-  float acc = 0.f, den = 0.f;
-  if (slice < n_slices) {
-    for (int s = slice; s < nparts; s += n_slices) {
-      const float wgt = __expf(lse[static_cast<size_t>(s) * G] - mx);
-      acc += wgt * po[static_cast<size_t>(s) * stride_o + d];
-      den += wgt;
-    }
+  const int per_slice = D / 8;              // threads per slice
+  const int n_slices = blockDim.x / per_slice;
+  const int t = tid % per_slice;
+  const int slice = tid / per_slice;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s = slice; s < nparts; s += n_slices) {
+    const float wgt = __expf(lse[static_cast<size_t>(s) * G] - mx);
+    const f32x4* src = reinterpret_cast<const f32x4*>(po + static_cast<size_t>(s) * stride_o + 8 * t);
+    acc0 += wgt * src[0];
+    acc1 += wgt * src[1];
+    den += wgt;
   }
-  s_red[tid] = acc;
+  s_acc[2 * tid] = acc0;
+  s_acc[2 * tid + 1] = acc1;
   s_den[tid] = den;
   __syncthreads();
   if (tid < D) {
+    const int tt = tid / 8, e = tid % 8;
     float num = 0.f, dsum = 0.f;
     for (int sl = 0; sl < n_slices; ++sl) {
-      num += s_red[sl * D + tid];
-      dsum += s_den[sl * D];
+      const f32x4 v = s_acc[2 * (sl * per_slice + tt) + e / 4];
+      num += v[e % 4];
+      dsum += s_den[sl * per_slice];
     }
     store(tid, num / dsum);
   }
