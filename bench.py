@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append, split and combine as three launches instead of the fused step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the copy kernel on 1 GiB three times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -205,15 +207,20 @@ def main():
     rot = [0]
 
     def step(ev=None):
-        """One step; ev (optional) holds 3 events per layer: before split,
-        after split, after combine."""
+        """One step; ev (optional) holds 3 events per layer: before the decode
+        kernel, after it, after the combine."""
         for li in range(n_layers):
             L = layers[rot[0] % len(layers)]
             rot[0] += 1
-            pkv.kv_append(L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["positions"], stream)
+            if args.unfused:
+                pkv.kv_append(L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["positions"], stream)
             if ev is not None:
                 ev[3 * li].record(stream)
-            dec.split(L.q, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+            if args.unfused:
+                dec.split(L.q, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+            else:
+                dec.step_split(L.q, L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale,
+                               L.out, stream)
             if ev is not None:
                 ev[3 * li + 1].record(stream)
             dec.combine(S["seq_lens"], L.out, S["mb"], stream)
@@ -274,6 +281,7 @@ def main():
             "head_dim": w.head_dim, "block_size": 16, "layers": n_layers,
             "attended_tokens": int(S["att"].sum()), "kv_bytes_per_step": kv_step,
             "accumulate": "fp32", "n_items": dec.n_items, "pool_copies": len(layers),
+            "append": "separate kernel" if args.unfused else "fused into the decode kernel",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.batch / (ms_per_step / 1e3), 1),

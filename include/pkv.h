@@ -195,6 +195,35 @@ int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_page
                           int32_t dtype, void* workspace, size_t workspace_bytes,
                           const pkv_decode_opts* opts);
 
+/* One decode step in one pass over the cache: kv_append of every sequence's
+ * new token followed by paged_decode_attn, with the append done inside the
+ * decode kernel.  The new token is the last attended one: sequence b's
+ * k_new[b]/v_new[b] (device [batch][n_kv_heads][head_dim], dtype) are written
+ * to position seq_lens[b] - 1 (slot (seq_lens[b] - 1) % 16 of page
+ * block_table[b][(seq_lens[b] - 1) / 16]) and attended together with the
+ * seq_lens[b] - 1 tokens already cached.  The wavefront that computes a
+ * sequence's last page uses the new token from registers and stores it to
+ * the pool, so the result and the pool equal pkv_kv_append with positions =
+ * seq_lens - 1 followed by pkv_paged_decode_attn.  Sequences with seq_lens 0
+ * append nothing; an invalid last-page id skips the store (NaN row as above).
+ * Same shapes, workspace and options as pkv_paged_decode_attn. */
+int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                    void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                    float scale, void* out, void* stream, int32_t batch,
+                    int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
+                    size_t workspace_bytes, const pkv_decode_opts* opts);
+
+/* The split half of pkv_decode_step alone (same arguments): the fused append
+ * and the decode kernel, leaving multi-chunk rows to pkv_lse_combine exactly
+ * as pkv_paged_decode_split does. */
+int pkv_decode_step_split(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                          void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_size, float scale, void* out, void* stream, int32_t batch,
+                          int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
+
 /* The split half of pkv_paged_decode_attn alone (same arguments): writes the
  * rows of single-chunk (sequence, KV head) pairs into out and every other
  * chunk's partial into the workspace:

@@ -102,6 +102,14 @@ struct Ops<true, D> {  // bfloat16
     return v;
   }
 
+  // Replaces the element of token 4c + e (e = 0..3) held by this lane.
+  __device__ static VReg insert_v(VReg v, int e, uint32_t bits) {
+    const uint32_t w = (e & 2) ? v.y : v.x;
+    const uint32_t nw = (e & 1) ? ((w & 0x0000ffffu) | (bits << 16)) : ((w & 0xffff0000u) | bits);
+    if (e & 2) v.y = nw; else v.x = nw;
+    return v;
+  }
+
   // Rounds the four probabilities to the MFMA input type, accumulates the
   // rounded values into l (so the weights that are summed are the weights that
   // are applied) and runs acc[nb] += V^T[nb] * P^T.
@@ -148,6 +156,14 @@ struct Ops<false, D> {  // float32
     return s0 + s1;
   }
 
+  __device__ static VReg insert_v(VReg v, int e, uint32_t bits) {
+    v.x = e == 0 ? bits : v.x;
+    v.y = e == 1 ? bits : v.y;
+    v.z = e == 2 ? bits : v.z;
+    v.w = e == 3 ? bits : v.w;
+    return v;
+  }
+
   __device__ static VReg mask_v(VReg v, int c, int valid) {
     v.x = 4 * c + 0 < valid ? v.x : 0u;
     v.y = 4 * c + 1 < valid ? v.y : 0u;
@@ -179,8 +195,10 @@ struct Ops<false, D> {  // float32
 
 struct DecodeArgs {
   const void* q;
-  const void* k_pages;
-  const void* v_pages;
+  void* k_pages;           // written only by the fused append
+  void* v_pages;
+  const void* k_new;       // non-null: fused append of each sequence's last token
+  const void* v_new;
   const int32_t* block_table;
   const int32_t* seq_lens;
   void* out;
@@ -362,8 +380,8 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
 
   const size_t head_off = static_cast<size_t>(h) * kTileBytes;
   const size_t page_stride = static_cast<size_t>(kTileBytes) * a.n_kv;
-  const char* kpool = static_cast<const char*>(a.k_pages) + head_off;
-  const char* vpool = static_cast<const char*>(a.v_pages) + head_off;
+  char* kpool = static_cast<char*>(a.k_pages) + head_off;
+  char* vpool = static_cast<char*>(a.v_pages) + head_off;
   const const_i32* bt_row =
       (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
   const uint32_t koff = 16u * lane;
@@ -386,10 +404,68 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
 #pragma unroll
   for (int nb = 0; nb < O::NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Fused append: the range holding the pair's last page also holds the new
+  // token (slot (len - 1) % 16 of that page).  Its K and V are loaded here in
+  // the lanes that hold that slot in the tile registers, patched into the
+  // tile when the last page is computed, and written to the pool.
+  const int last = n_pages - 1;
+  const bool append = a.k_new != nullptr && j1 == n_pages;
+  const int s_new = (len - 1) & (kBlock - 1);
+  u32x4 knew[O::NK];
+  uint32_t vnew[O::NV];
+  if (append) {
+    const size_t row = (static_cast<size_t>(b) * a.n_kv + h) * D;
+    const char* kn = static_cast<const char*>(a.k_new) + row * O::ES;
+#pragma unroll
+    for (int i = 0; i < O::NK; ++i) knew[i] = *reinterpret_cast<const u32x4*>(kn + 16 * (4 * i + c));
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) {
+      if constexpr (kBf16)
+        vnew[nb] = static_cast<const uint16_t*>(a.v_new)[row + 16 * nb + n];
+      else
+        vnew[nb] = static_cast<const uint32_t*>(a.v_new)[row + 16 * nb + n];
+    }
+  }
+  auto patch = [&](PageRegs<kBf16, D>& r) {
+    if (n == s_new) {
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i) r.k[i] = knew[i];
+    }
+    if (c == (s_new >> 2)) {
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::insert_v(r.v[nb], s_new & 3, vnew[nb]);
+    }
+    // One wavefront per pair writes the token to the pool (the query-head
+    // blocks of a large group all patch their registers the same way).
+    const int pg = bt_row[last];
+    if (gblk == 0 && static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages)) {
+      const size_t off = static_cast<size_t>(pg) * page_stride;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc(kpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc(vpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
+      if (n == s_new) {
+#pragma unroll
+        for (int i = 0; i < O::NK; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(knew[i], kr, koff + 1024 * i, 0, 0);
+      }
+      if (c == (s_new >> 2)) {
+        const uint32_t vo = O::ES * (n * kBlock + s_new);
+#pragma unroll
+        for (int nb = 0; nb < O::NV; ++nb) {
+          if constexpr (kBf16)
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(vnew[nb]), vr,
+                                                  vo + O::ES * 16 * kBlock * nb, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(vnew[nb], vr, vo + O::ES * 16 * kBlock * nb, 0, 0);
+        }
+      }
+    }
+  };
+
   PageRegs<kBf16, D> buf[kBufs];
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) issue(buf[s], j0 + s);
-  const int last = n_pages - 1;
   int j = j0;
   // Ring of kDepth + 1 register buffers: every step requests page j + kDepth
   // (the range's last page again near the end: a cache hit) and computes page
@@ -402,6 +478,7 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
       __builtin_amdgcn_sched_barrier(0);
       issue(buf[(s + kDepth) % kBufs], j + kDepth);
       __builtin_amdgcn_sched_barrier(0);
+      if (append && j == last) patch(buf[s]);
       compute_page<kBf16, D>(buf[s], j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c,
                              m, l, acc);
       if (++j >= j1) break;
@@ -428,15 +505,15 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
   }
 }
 
-// Minimum wavefronts per SIMD the split kernel is compiled for (caps its
-// registers at 512 / N per lane).
-#ifndef PKV_SPLIT_WAVES_PER_EU
-#define PKV_SPLIT_WAVES_PER_EU 2
-#endif
+// At least two wavefronts per SIMD: caps registers at 256 per lane, which the
+// bf16 kernel fits without spilling; fp32 at head_dim 128 needs more and runs
+// one wavefront per SIMD.
+template <bool kBf16, int D>
+constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
 
 template <bool kBf16, int D, int kDepth>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu<kBf16, D>)))
 split_kernel(DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
@@ -639,12 +716,15 @@ struct Resolved {
 
 using SplitFn = void (*)(DecodeArgs);
 
+// bf16 tiles are 4 KiB per (page, head) at head_dim 128: two pages ahead fit
+// beside the accumulators at two wavefronts per SIMD.  fp32 tiles are twice
+// as large, so fp32 keeps one page ahead.
 constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
 
 SplitFn split_fn(int dtype, int head_dim) {
   if (dtype == PKV_BF16)
     return head_dim == 128 ? split_kernel<true, 128, kPrefetchPages> : split_kernel<true, 64, kPrefetchPages>;
-  return head_dim == 128 ? split_kernel<false, 128, kPrefetchPages> : split_kernel<false, 64, kPrefetchPages>;
+  return head_dim == 128 ? split_kernel<false, 128, 1> : split_kernel<false, 64, 1>;
 }
 
 int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
@@ -699,6 +779,7 @@ int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch,
 }
 
 int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
+                  const void* k_new, const void* v_new,
                   const void* k_pages, const void* v_pages, const int32_t* block_table,
                   const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                   int32_t block_size, float scale, void* out, void* stream, int32_t batch,
@@ -716,6 +797,9 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                    !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(block_table, 4)))
     return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned q/k_pages/v_pages/block_table");
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, f + ": scale is not finite");
+  if ((k_new != nullptr) != (v_new != nullptr) ||
+      (k_new && (!aligned(k_new, 16) || !aligned(v_new, 4))))
+    return fail(PKV_ERR_INVALID_ARG, f + ": k_new/v_new must both be given, 16/4-byte aligned");
   const int group = n_q_heads / n_kv_heads;
   Resolved r;
   st = resolve_opts(dtype, head_dim, group, batch, opts, &r);
@@ -728,8 +812,11 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   const int64_t slots = decode_slots(batch, n_kv_heads, r.n_items);
   DecodeArgs a;
   a.q = q;
-  a.k_pages = k_pages;
-  a.v_pages = v_pages;
+  // The pools are written only when the new token is appended in the same launch.
+  a.k_pages = const_cast<void*>(k_pages);
+  a.v_pages = const_cast<void*>(v_pages);
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = out;
@@ -811,7 +898,8 @@ int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_page
                           void* out, void* stream, int32_t batch, int32_t max_blocks_per_seq,
                           int32_t num_pages, int32_t dtype, void* workspace,
                           size_t workspace_bytes, const pkv_decode_opts* opts) {
-  return pkv::decode_common(true, true, "pkv_paged_decode_attn", q, k_pages, v_pages, block_table,
+  return pkv::decode_common(true, true, "pkv_paged_decode_attn", q, nullptr, nullptr, k_pages, v_pages,
+                            block_table,
                             seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out,
                             stream, batch, max_blocks_per_seq, num_pages, dtype, workspace,
                             workspace_bytes, opts);
@@ -823,17 +911,46 @@ int pkv_paged_decode_split(const void* q, const void* k_pages, const void* v_pag
                            void* out, void* stream, int32_t batch, int32_t max_blocks_per_seq,
                            int32_t num_pages, int32_t dtype, void* workspace,
                            size_t workspace_bytes, const pkv_decode_opts* opts) {
-  return pkv::decode_common(true, false, "pkv_paged_decode_split", q, k_pages, v_pages,
+  return pkv::decode_common(true, false, "pkv_paged_decode_split", q, nullptr, nullptr, k_pages,
+                            v_pages, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
+                            scale, out, stream, batch, max_blocks_per_seq, num_pages, dtype,
+                            workspace, workspace_bytes, opts);
+}
+
+int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                    void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                    float scale, void* out, void* stream, int32_t batch,
+                    int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
+                    size_t workspace_bytes, const pkv_decode_opts* opts) {
+  if (batch > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step: k_new and v_new are required");
+  return pkv::decode_common(true, true, "pkv_decode_step", q, k_new, v_new, k_pages, v_pages,
                             block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
                             scale, out, stream, batch, max_blocks_per_seq, num_pages, dtype,
                             workspace, workspace_bytes, opts);
+}
+
+int pkv_decode_step_split(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                          void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                          int32_t block_size, float scale, void* out, void* stream, int32_t batch,
+                          int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts) {
+  if (batch > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_split: k_new and v_new are required");
+  return pkv::decode_common(true, false, "pkv_decode_step_split", q, k_new, v_new, k_pages,
+                            v_pages, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim,
+                            block_size, scale, out, stream, batch, max_blocks_per_seq, num_pages,
+                            dtype, workspace, workspace_bytes, opts);
 }
 
 int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens,
                     int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, void* out, int32_t dtype,
                     const pkv_decode_opts* opts, void* stream) {
-  return pkv::decode_common(false, true, "pkv_lse_combine", nullptr, nullptr, nullptr, nullptr,
+  return pkv::decode_common(false, true, "pkv_lse_combine", nullptr, nullptr, nullptr, nullptr, nullptr,
+                            nullptr,
                             seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, 1.0f, out,
                             stream, batch, max_blocks_per_seq, 1, dtype,
                             const_cast<void*>(workspace), workspace_bytes, opts);

@@ -157,6 +157,24 @@ class Decoder:
                                                     stream)), "pkv_paged_decode_attn")
         return out
 
+    def _step_args(self, q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, out, stream):
+        B, Hq, D = q.shape
+        return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                _ptr(seq_lens), Hq, k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream),
+                B, block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
+                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages))
+
+    def step(self, q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
+        """Append each sequence's new token at seq_lens - 1 and attend, in one pass."""
+        check(lib.pkv_decode_step(*self._step_args(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens,
+                                                   scale, out, stream)), "pkv_decode_step")
+        return out
+
+    def step_split(self, q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
+        """The split half of step(); follow with combine()."""
+        check(lib.pkv_decode_step_split(*self._step_args(q, k_new, v_new, k_pages, v_pages, block_table,
+                                                         seq_lens, scale, out, stream)), "pkv_decode_step_split")
+
     def split(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
         check(lib.pkv_paged_decode_split(*self._args(q, k_pages, v_pages, block_table, seq_lens, scale, out,
                                                      stream)), "pkv_paged_decode_split")

@@ -256,3 +256,34 @@ def test_full_size_sampled(pkv, name):
         assert torch.equal(out, out2)
         del c, out, out2, dec
         torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ fused decode step
+STEP = [
+    # name, B, Hq, Hkv, D, dtype, cached lengths, n_items, min_chunk
+    ("step_f32_64", 3, 4, 2, 64, "f32", [0, 15, 37], 3, 1),
+    ("step_bf16_128", 5, 8, 2, 128, "bf16", [0, 15, 16, 31, 200], 7, 1),
+    ("step_mha_bf16", 3, 4, 4, 128, "bf16", [47, 100, 3], 0, 0),
+    ("step_mqa64_bf16", 2, 64, 1, 128, "bf16", [150, 17], 5, 1),
+    ("step_g3_f32_128", 2, 6, 2, 128, "f32", [64, 5], 2, 2),
+]
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached,n_items,min_chunk", STEP, ids=[s[0] for s in STEP])
+def test_fused_step(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, min_chunk):
+    P = sum((n + 16) // 16 for n in cached) + 4
+    w = W.custom(name, B, Hq, Hkv, D, dtype, cached, pool_pages=P, seed=zlib.crc32(name.encode()) % 1000)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    H.log(f"fused step {name}")
+    ref = H.oracle_full(c)
+    ek, ev = OA.append(H.bits(c.k_pages), H.bits(c.v_pages), c.bt_np, c.cached, H.bits(c.k_new),
+                       H.bits(c.v_new), H.BS)
+    kp, vp = c.k_pages.clone(), c.v_pages.clone()
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), n_items, min_chunk)
+    out = torch.empty_like(c.q)
+    dec.step(c.q, c.k_new, c.v_new, kp, vp, c.bt, c.seq_lens, w.scale, out)
+    torch.cuda.synchronize()
+    H.assert_close(H.f64(out), ref, dtype, name)
+    assert np.array_equal(H.bits(kp), ek) and np.array_equal(H.bits(vp), ev)
+    out2, _ = _run_step(pkv, c, n_items, min_chunk)       # separate append, then decode
+    assert torch.equal(out, out2)
