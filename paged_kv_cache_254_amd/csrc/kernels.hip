@@ -285,15 +285,16 @@ struct PageRegs {
 // and become the base of a buffer resource whose range is exactly one tile, so
 // the per-lane offsets (koff = 16 * lane, voff = elem * (16 n + 4 c)) stay in
 // one register and an offset past the tile reads zero instead of faulting.
+// range = 0 issues the same loads without touching memory (they return
+// zeros): used past the end of a range and for page ids outside the pool.
 template <bool kBf16, int D>
 __device__ inline void load_page(PageRegs<kBf16, D>& r, const char* kbase, const char* vbase,
-                                 uint32_t koff, uint32_t voff) {
+                                 uint32_t koff, uint32_t voff, int range) {
   using O = Ops<kBf16, D>;
-  constexpr int kTileBytes = kBlock * D * O::ES;
   const __amdgpu_buffer_rsrc_t kr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), 0, kTileBytes, PKV_RSRC_WORD3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), 0, range, PKV_RSRC_WORD3);
   const __amdgpu_buffer_rsrc_t vr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), 0, kTileBytes, PKV_RSRC_WORD3);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), 0, range, PKV_RSRC_WORD3);
 #pragma unroll
   for (int i = 0; i < O::NK; ++i)
     r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 1024 * i, 0, PKV_KV_LOAD_AUX);
@@ -387,16 +388,18 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
   const uint32_t koff = 16u * lane;
   const uint32_t voff = O::ES * (n * kBlock + 4 * c);
   bool bad = false;
-  // Page of logical block j (clamped to the range's last block), checked
-  // against the pool: an entry outside it is never dereferenced.
+  // Loads of logical block j.  Past the range's end (the ring runs kDepth
+  // pages ahead) the loads are issued with an empty range, so every ring
+  // step issues the same instructions but nothing is read; a page id outside
+  // the pool is never dereferenced either (and poisons the result).
   auto issue = [&](PageRegs<kBf16, D>& r, int j) {
+    const bool in_range = j < j1;
     int pg = bt_row[min(j, j1 - 1)];
-    if (static_cast<unsigned>(pg) >= static_cast<unsigned>(a.num_pages)) {
-      bad = true;
-      pg = 0;
-    }
+    const bool pg_ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    bad |= in_range && !pg_ok;
+    if (!pg_ok) pg = 0;
     const size_t off = static_cast<size_t>(pg) * page_stride;
-    load_page(r, kpool + off, vpool + off, koff, voff);
+    load_page(r, kpool + off, vpool + off, koff, voff, in_range && pg_ok ? kTileBytes : 0);
   };
 
   float m = -INFINITY, l = 0.f;
