@@ -198,7 +198,7 @@ def main():
     log(f"setup {w.name}")
     S = setup(w, device)
     dt = W.torch_dtype(w)
-    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, args.n_items, args.min_chunk,
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, S["mb"], args.n_items, args.min_chunk,
                       device=device)
     layers = S["layers"]
     n_layers = w.n_layers
@@ -280,7 +280,8 @@ def main():
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
             "head_dim": w.head_dim, "block_size": 16, "layers": n_layers,
             "attended_tokens": int(S["att"].sum()), "kv_bytes_per_step": kv_step,
-            "accumulate": "fp32", "n_items": dec.n_items, "pool_copies": len(layers),
+            "accumulate": "fp32", "n_items": dec.n_items, "min_chunk_pages": dec.min_chunk_pages,
+            "pool_copies": len(layers),
             "append": "separate kernel" if args.unfused else "fused into the decode kernel",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

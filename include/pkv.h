@@ -179,8 +179,9 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  * workspace: device, 256-byte aligned, at least
  * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
  * bytes (n_items after defaults are applied).  Contents on entry are ignored.
- * opts (nullable): n_items <= 0 means one chunk per wavefront the device can
- * hold at once; min_chunk_pages <= 0 means 8.
+ * opts (nullable): n_items <= 0 means one chunk per wavefront (groups <= 16)
+ * or per workgroup (larger groups) the device can hold at once;
+ * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups).
  * ------------------------------------------------------------------------ */
 typedef struct pkv_decode_opts {
   int32_t n_items;
@@ -255,14 +256,20 @@ int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t
 int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                    int32_t head_dim, int32_t n_items);
 
-/* The n_items the device calls use when opts->n_items <= 0, for this device
- * (the current HIP device), dtype, head_dim and group (host query; needs a GPU). */
-int pkv_decode_default_items(int32_t dtype, int32_t head_dim, int32_t group, int32_t* out);
+/* The options the device calls use for these shapes (opts nullable: fields
+ * <= 0 take their defaults, given above; the default n_items is also capped
+ * at the number of min_chunk_pages chunks in batch * max_blocks_per_seq *
+ * n_kv_heads pages), and the workspace they need.  Queries the current HIP
+ * device when n_items must be defaulted (needs a GPU). */
+int pkv_decode_resolve(int32_t dtype, int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t batch, int32_t max_blocks_per_seq, const pkv_decode_opts* opts,
+                       pkv_decode_opts* resolved, int64_t* workspace_bytes);
 
 /* Host mirror of the split plan, for callers that size or inspect partials:
  * seq_lens (host int32 [batch]) -> *chunk_pages (C above), and for every pair
  * (b, h) first_chunk[b * n_kv + h] and last_chunk[b * n_kv + h] (host int32,
- * nullable; -1 for empty sequences).  n_items must already be resolved. */
+ * nullable; -1 for empty sequences).  n_items and min_chunk_pages (>= 1) must
+ * already be resolved. */
 int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t n_items,
                     int32_t min_chunk_pages, int32_t* chunk_pages, int32_t* first_chunk,

@@ -82,7 +82,8 @@ SIGNATURES = {
     "pkv_lse_combine": (ctypes.c_int, [_vp, _sz, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32,
                                        ctypes.POINTER(DecodeOpts), _vp]),
     "pkv_decode_workspace_bytes": (_i64, [_i32, _i32, _i32, _i32, _i32]),
-    "pkv_decode_default_items": (ctypes.c_int, [_i32, _i32, _i32, _pi32]),
+    "pkv_decode_resolve": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(DecodeOpts),
+                                          ctypes.POINTER(DecodeOpts), ctypes.POINTER(ctypes.c_int64)]),
     "pkv_decode_plan": (ctypes.c_int, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32]),
     "pkv_hbm_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "pkv_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),

@@ -242,7 +242,8 @@ int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
     return fail(PKV_ERR_INVALID_ARG, "pkv_decode_plan: bad argument");
   if (block_size != pkv::kBlock)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_decode_plan: block_size must be 16");
-  int min_chunk = min_chunk_pages > 0 ? min_chunk_pages : pkv::kDefaultMinChunk;
+  int min_chunk = min_chunk_pages;
+  if (min_chunk < 1) return fail(PKV_ERR_INVALID_ARG, "pkv_decode_plan: min_chunk_pages must be resolved (>= 1)");
   std::vector<int64_t> prefix(batch + 1, 0);
   for (int32_t b = 0; b < batch; ++b)
     prefix[b + 1] = prefix[b] + pkv::pages_of_len(seq_lens[b], max_blocks_per_seq);

@@ -33,6 +33,7 @@
 // for all query heads of the group from registers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -353,23 +354,34 @@ __device__ inline void compute_page(PageRegs<kBf16, D>& r, int valid,
   O::pv(r.v, p, l, acc);
 }
 
-// Pages [j0, j1) of the (b, h) pair for query heads gblk*16 .. gblk*16+15.
-// kDepth pages are in flight ahead of the one being computed.
-template <bool kBf16, int D, int kDepth>
-__device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j1, int n_pages,
-                                int seg_start, int chunk, int C, int gblk, int lane) {
+// One segment: the pages of one (sequence b, KV head h) pair that one chunk
+// covers, for the 16 query heads gblk*16 .. gblk*16+15 (lane column n = head
+// gblk*16 + n).  Holds the query operand, the online-softmax state and, when
+// the segment ends with the pair's last page and the step appends, the new
+// token's K/V in the lanes that hold its slot.
+template <bool kBf16, int D>
+struct Segment {
   using O = Ops<kBf16, D>;
-  constexpr int kTileBytes = kBlock * D * O::ES;
-  constexpr int kBufs = kDepth + 1;
-  const int c = lane >> 4, n = lane & 15;
-  const int g = gblk * 16 + n;
-  const bool g_ok = g < a.group;
-  const int hq = h * a.group + g;
-  const int len = a.seq_lens[b];
-
-  // Query operand: lane (c, n) holds q[hq][(4i + c) * X .. +X) for each i.
+  static constexpr int kTileBytes = kBlock * D * O::ES;
+  int b, h, g, hq, len, n_pages, s_new;
+  bool g_ok, append;
   u32x4 qreg[O::NK];
-  {
+  u32x4 knew[O::NK];
+  uint32_t vnew[O::NV];
+  float m, l;
+  f32x4 acc[O::NV];
+
+  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, bool ends_pair, int gblk,
+                        int lane) {
+    const int c = lane >> 4, n = lane & 15;
+    b = b_;
+    h = h_;
+    n_pages = n_pages_;
+    g = gblk * 16 + n;
+    g_ok = g < a.group;
+    hq = h * a.group + g;
+    len = a.seq_lens[b];
+    // Query operand: lane (c, n) holds q[hq][(4i + c) * X .. +X) for each i.
     const char* qb = static_cast<const char*>(a.q) +
                      (static_cast<size_t>(b) * a.n_q + (g_ok ? hq : 0)) * D * O::ES;
 #pragma unroll
@@ -377,7 +389,115 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
       u32x4 t = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * i + c));
       qreg[i] = g_ok ? t : u32x4{0u, 0u, 0u, 0u};
     }
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Fused append: the segment holding the pair's last page also holds the
+    // new token (slot (len - 1) % 16 of that page).
+    append = a.k_new != nullptr && ends_pair;
+    s_new = (len - 1) & (kBlock - 1);
+    if (append) {
+      const size_t row = (static_cast<size_t>(b) * a.n_kv + h) * D;
+      const char* kn = static_cast<const char*>(a.k_new) + row * O::ES;
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i) knew[i] = *reinterpret_cast<const u32x4*>(kn + 16 * (4 * i + c));
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) {
+        if constexpr (kBf16)
+          vnew[nb] = static_cast<const uint16_t*>(a.v_new)[row + 16 * nb + n];
+        else
+          vnew[nb] = static_cast<const uint32_t*>(a.v_new)[row + 16 * nb + n];
+      }
+    }
   }
+
+  // Puts the new token into the tile registers of the pair's last page: the
+  // lanes whose K pieces belong to slot s_new (lane % 16 == s_new) and whose V
+  // elements are tokens 4c..4c+3 with c = s_new / 4.
+  __device__ void patch(PageRegs<kBf16, D>& r, int lane) const {
+    const int c = lane >> 4, n = lane & 15;
+    if (n == s_new) {
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i) r.k[i] = knew[i];
+    }
+    if (c == (s_new >> 2)) {
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::insert_v(r.v[nb], s_new & 3, vnew[nb]);
+    }
+  }
+
+  // Writes the new token into page pg of the pool (the same bytes the patched
+  // lanes hold).  kpool/vpool point at head h of page 0.
+  __device__ void store_new_token(char* kpool, char* vpool, size_t page_stride, int pg,
+                                  int lane) const {
+    const int c = lane >> 4, n = lane & 15;
+    const size_t off = static_cast<size_t>(pg) * page_stride;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc(kpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc(vpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
+    if (n == s_new) {
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(knew[i], kr, 16u * lane + 1024 * i, 0, 0);
+    }
+    if (c == (s_new >> 2)) {
+      const uint32_t vo = O::ES * (n * kBlock + s_new);
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) {
+        if constexpr (kBf16)
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(vnew[nb]), vr,
+                                                vo + O::ES * 16 * kBlock * nb, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(vnew[nb], vr, vo + O::ES * 16 * kBlock * nb, 0, 0);
+      }
+    }
+  }
+
+  __device__ void page(PageRegs<kBf16, D>& r, int j, float scale_log2, int lane) {
+    compute_page<kBf16, D>(r, j == n_pages - 1 ? len - kBlock * j : kBlock, qreg, scale_log2,
+                           lane >> 4, m, l, acc);
+  }
+
+  // Normalises and writes the result: the output row when the pair lies in a
+  // single chunk, otherwise this chunk's partial (o, natural-log lse).
+  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad,
+                         int lane) const {
+    const int c = lane >> 4;
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = bad ? NAN : 1.0f / lt;
+    const int first_chunk = seg_start / C;
+    const int last_chunk = (seg_start + n_pages - 1) / C;
+    if (!g_ok) return;
+    if (first_chunk == last_chunk) {
+      const size_t row = (static_cast<size_t>(b) * a.n_q + hq) * D;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, acc[nb] * inv);
+    } else {
+      const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
+      float* po = a.part_o + (slot * a.group + g) * D;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb)
+        *reinterpret_cast<f32x4*>(po + 16 * nb + 4 * c) = acc[nb] * inv;
+      if (c == 0) a.part_lse[slot * a.group + g] = bad ? NAN : (m + __log2f(lt)) * kLn2;
+    }
+  }
+};
+
+// Pages [j0, j1) of the (b, h) pair for query heads gblk*16 .. gblk*16+15,
+// streamed through a ring of kDepth + 1 register buffers: kDepth pages are
+// in flight ahead of the one being computed.
+template <bool kBf16, int D, int kDepth>
+__device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j1, int n_pages,
+                                int seg_start, int chunk, int C, int gblk, int lane) {
+  using O = Ops<kBf16, D>;
+  constexpr int kTileBytes = kBlock * D * O::ES;
+  constexpr int kBufs = kDepth + 1;
+  const int c = lane >> 4, n = lane & 15;
+  Segment<kBf16, D> seg;
+  seg.begin(a, b, h, n_pages, j1 == n_pages, gblk, lane);
 
   const size_t head_off = static_cast<size_t>(h) * kTileBytes;
   const size_t page_stride = static_cast<size_t>(kTileBytes) * a.n_kv;
@@ -401,78 +521,20 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
     const size_t off = static_cast<size_t>(pg) * page_stride;
     load_page(r, kpool + off, vpool + off, koff, voff, in_range && pg_ok ? kTileBytes : 0);
   };
-
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc[O::NV];
-#pragma unroll
-  for (int nb = 0; nb < O::NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Fused append: the range holding the pair's last page also holds the new
-  // token (slot (len - 1) % 16 of that page).  Its K and V are loaded here in
-  // the lanes that hold that slot in the tile registers, patched into the
-  // tile when the last page is computed, and written to the pool.
   const int last = n_pages - 1;
-  const bool append = a.k_new != nullptr && j1 == n_pages;
-  const int s_new = (len - 1) & (kBlock - 1);
-  u32x4 knew[O::NK];
-  uint32_t vnew[O::NV];
-  if (append) {
-    const size_t row = (static_cast<size_t>(b) * a.n_kv + h) * D;
-    const char* kn = static_cast<const char*>(a.k_new) + row * O::ES;
-#pragma unroll
-    for (int i = 0; i < O::NK; ++i) knew[i] = *reinterpret_cast<const u32x4*>(kn + 16 * (4 * i + c));
-#pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb) {
-      if constexpr (kBf16)
-        vnew[nb] = static_cast<const uint16_t*>(a.v_new)[row + 16 * nb + n];
-      else
-        vnew[nb] = static_cast<const uint32_t*>(a.v_new)[row + 16 * nb + n];
-    }
-  }
-  auto patch = [&](PageRegs<kBf16, D>& r) {
-    if (n == s_new) {
-#pragma unroll
-      for (int i = 0; i < O::NK; ++i) r.k[i] = knew[i];
-    }
-    if (c == (s_new >> 2)) {
-#pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::insert_v(r.v[nb], s_new & 3, vnew[nb]);
-    }
+  auto patch_and_store = [&](PageRegs<kBf16, D>& r) {
+    seg.patch(r, lane);
     // One wavefront per pair writes the token to the pool (the query-head
     // blocks of a large group all patch their registers the same way).
     const int pg = bt_row[last];
-    if (gblk == 0 && static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages)) {
-      const size_t off = static_cast<size_t>(pg) * page_stride;
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc(kpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc(vpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
-      if (n == s_new) {
-#pragma unroll
-        for (int i = 0; i < O::NK; ++i)
-          __builtin_amdgcn_raw_buffer_store_b128(knew[i], kr, koff + 1024 * i, 0, 0);
-      }
-      if (c == (s_new >> 2)) {
-        const uint32_t vo = O::ES * (n * kBlock + s_new);
-#pragma unroll
-        for (int nb = 0; nb < O::NV; ++nb) {
-          if constexpr (kBf16)
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(vnew[nb]), vr,
-                                                  vo + O::ES * 16 * kBlock * nb, 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(vnew[nb], vr, vo + O::ES * 16 * kBlock * nb, 0, 0);
-        }
-      }
-    }
+    if (gblk == 0 && static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages))
+      seg.store_new_token(kpool, vpool, page_stride, pg, lane);
   };
 
   PageRegs<kBf16, D> buf[kBufs];
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) issue(buf[s], j0 + s);
   int j = j0;
-  // Ring of kDepth + 1 register buffers: every step requests page j + kDepth
-  // (the range's last page again near the end: a cache hit) and computes page
-  // j, so every step issues the same loads.
   while (j < j1) {
 #pragma unroll
     for (int s = 0; s < kBufs; ++s) {
@@ -481,31 +543,12 @@ __device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j
       __builtin_amdgcn_sched_barrier(0);
       issue(buf[(s + kDepth) % kBufs], j + kDepth);
       __builtin_amdgcn_sched_barrier(0);
-      if (append && j == last) patch(buf[s]);
-      compute_page<kBf16, D>(buf[s], j == last ? len - kBlock * j : kBlock, qreg, a.scale_log2, c,
-                             m, l, acc);
+      if (seg.append && j == last) patch_and_store(buf[s]);
+      seg.page(buf[s], j, a.scale_log2, lane);
       if (++j >= j1) break;
     }
   }
-
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
-  const float inv = bad ? NAN : 1.0f / lt;
-  const int first_chunk = seg_start / C;
-  const int last_chunk = (seg_start + n_pages - 1) / C;
-  if (!g_ok) return;
-  if (first_chunk == last_chunk) {
-    const size_t row = (static_cast<size_t>(b) * a.n_q + hq) * D;
-#pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, acc[nb] * inv);
-  } else {
-    const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
-    float* po = a.part_o + (slot * a.group + g) * D;
-#pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb)
-      *reinterpret_cast<f32x4*>(po + 16 * nb + 4 * c) = acc[nb] * inv;
-    if (c == 0) a.part_lse[slot * a.group + g] = bad ? NAN : (m + __log2f(lt)) * kLn2;
-  }
+  seg.finish(a, seg_start, chunk, C, bad, lane);
 }
 
 // At least two wavefronts per SIMD: caps registers at 256 per lane, which the
@@ -558,6 +601,187 @@ split_kernel(DecodeArgs a) {
       } while (n == 0);
     }
   }
+}
+
+// Position in the flattened (sequence, KV head, page) order of all pages:
+// flat index f, sequence b (with pb = pages before b and n = pages of b),
+// KV head h, page j of the pair.
+struct FlatCursor {
+  int f, b, h, j, n, pb;
+  __device__ void seek(const int32_t* s_prefix, int batch, int n_kv, int f0) {
+    f = f0;
+    b = uni(find_seq(s_prefix, batch, n_kv, f0));
+    pb = uni(s_prefix[b]);
+    n = uni(s_prefix[b + 1]) - pb;
+    const int off = f0 - n_kv * pb;
+    h = off / n;
+    j = off - h * n;
+  }
+  // Next page; must not be called on the last page of all.
+  __device__ void next(const int32_t* s_prefix, int n_kv) {
+    ++f;
+    if (++j == n) {
+      j = 0;
+      if (++h == n_kv) {
+        h = 0;
+        do {
+          ++b;
+          pb = uni(s_prefix[b]);
+          n = uni(s_prefix[b + 1]) - pb;
+        } while (n == 0);
+      }
+    }
+  }
+};
+
+// LDS offset of the tile ring, after the length prefix (16-byte aligned).
+__host__ __device__ inline size_t shared_tiles_offset(int batch) {
+  return ((static_cast<size_t>(batch) + 1 + kWavesPerGroup) * sizeof(int32_t) + 15) & ~size_t{15};
+}
+
+// Split-KV decode for groups above 16 query heads per KV head (MQA): one
+// chunk per workgroup, whose four wavefronts take the 16-head blocks
+// 0..ceil(G/16)-1 of the group and share every K/V tile through LDS.  The
+// 256 threads load each page's two tiles cooperatively (16-byte pieces)
+// kStage pages ahead into a register ring, write the next page into a 3-slot
+// LDS ring, meet at one barrier per page, and each computing wavefront reads
+// its MFMA operands from LDS (same layout as in HBM).  A slot written at step
+// p was last read at step p - 2, before the barrier of step p - 1.
+#ifndef PKV_SHARED_WAVES_PER_EU
+#define PKV_SHARED_WAVES_PER_EU 2
+#endif
+template <bool kBf16, int D>
+constexpr int kSharedWavesPerEu = (kBf16 || D == 64) ? PKV_SHARED_WAVES_PER_EU : 1;
+
+template <bool kBf16, int D, int kStage>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(kSharedWavesPerEu<kBf16, D>)))
+split_kernel_shared(DecodeArgs a) {
+  using O = Ops<kBf16, D>;
+  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int kThreads = kWave * kWavesPerGroup;
+  constexpr int kPieces = 2 * kTile / (kThreads * 16);
+  constexpr int kSlots = 3;
+  static_assert(kPieces >= 1 && 2 * kTile == kPieces * kThreads * 16, "tile split");
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  int32_t* s_wsum = smem + a.batch + 1;
+  char* s_tiles = reinterpret_cast<char*>(smem) + shared_tiles_offset(a.batch);
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = uni(tid / kWave);
+  const int chunk = blockIdx.x;
+  if (chunk >= a.n_items) return;
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int64_t f64 = static_cast<int64_t>(chunk) * C;
+  if (f64 >= total) return;
+  const int f0 = static_cast<int>(f64);
+  const int cnt = static_cast<int>(min(f64 + C, static_cast<int64_t>(total))) - f0;
+  const bool computes = wave * 16 < a.group;
+  const size_t page_stride = static_cast<size_t>(kTile) * a.n_kv;
+  char* kp0 = static_cast<char*>(a.k_pages);
+  char* vp0 = static_cast<char*>(a.v_pages);
+  auto bt_row = [&](int b) {
+    return (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
+  };
+
+  // ---- loader: pages of the chunk in order, kStage ahead of the compute.
+  FlatCursor ld;
+  ld.seek(s_prefix, a.batch, a.n_kv, f0);
+  int issued = 0;
+  u32x4 ring[kStage][kPieces];
+  auto issue = [&](u32x4 (&dst)[kPieces]) {
+    const bool in = issued < cnt;
+    int pg = bt_row(ld.b)[ld.j];
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
+    const int range = in && ok ? kTile : 0;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(kp0 + off, 0, range, PKV_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(vp0 + off, 0, range, PKV_RSRC_WORD3);
+#pragma unroll
+    for (int e = 0; e < kPieces; ++e) {
+      const uint32_t byte = 16u * (tid + kThreads * e);
+      if (byte < static_cast<uint32_t>(kTile))
+        dst[e] = __builtin_amdgcn_raw_buffer_load_b128(kr, byte, 0, PKV_KV_LOAD_AUX);
+      else
+        dst[e] = __builtin_amdgcn_raw_buffer_load_b128(vr, byte - kTile, 0, PKV_KV_LOAD_AUX);
+    }
+    if (in) {
+      ++issued;
+      if (issued < cnt) ld.next(s_prefix, a.n_kv);
+    }
+  };
+  auto to_lds = [&](const u32x4 (&src)[kPieces], int slot) {
+    char* base = s_tiles + static_cast<size_t>(slot) * 2 * kTile;
+#pragma unroll
+    for (int e = 0; e < kPieces; ++e)
+      *reinterpret_cast<u32x4*>(base + 16 * (tid + kThreads * e)) = src[e];
+  };
+
+  // ---- compute: one 16-head block per wavefront, segments as in split_kernel.
+  FlatCursor cp;
+  cp.seek(s_prefix, a.batch, a.n_kv, f0);
+  Segment<kBf16, D> seg;
+  bool open = false, bad = false;
+  int seg_start = 0;
+  const int c = lane >> 4, n = lane & 15;
+  const uint32_t voff = O::ES * (n * kBlock + 4 * c);
+  auto compute = [&](int slot, int p) {
+    if (open && (cp.b != seg.b || cp.h != seg.h)) {
+      seg.finish(a, seg_start, chunk, C, bad, lane);
+      open = false;
+    }
+    if (!open) {
+      const bool ends_pair = cp.j + (cnt - p) >= cp.n;
+      seg.begin(a, cp.b, cp.h, cp.n, ends_pair, wave, lane);
+      seg_start = a.n_kv * cp.pb + cp.h * cp.n;
+      bad = false;
+      open = true;
+    }
+    const int pg = bt_row(cp.b)[cp.j];
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    bad |= !ok;
+    const char* base = s_tiles + static_cast<size_t>(slot) * 2 * kTile;
+    PageRegs<kBf16, D> r;
+#pragma unroll
+    for (int i = 0; i < O::NK; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(base + 1024 * i + 16 * lane);
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb)
+      r.v[nb] = *reinterpret_cast<const typename O::VReg*>(base + kTile + voff + O::ES * 16 * kBlock * nb);
+    if (seg.append && cp.j == cp.n - 1) {
+      seg.patch(r, lane);
+      if (wave == 0 && ok) {
+        const size_t head_off = static_cast<size_t>(cp.h) * kTile;
+        seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+      }
+    }
+    seg.page(r, cp.j, a.scale_log2, lane);
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStage; ++s) issue(ring[s]);
+  to_lds(ring[0], 0);
+  issue(ring[0]);
+  __syncthreads();
+  int p = 0;
+  // Step p: stage page p + 1 into LDS, request page p + 1 + kStage into the
+  // register slot it frees, barrier, compute page p.
+  while (p < cnt) {
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const int rs = (s + 1) % kStage;
+      if (p + 1 < cnt) to_lds(ring[rs], (p + 1) % kSlots);
+      issue(ring[rs]);
+      __syncthreads();
+      if (computes) compute(p % kSlots, p);
+      if (++p >= cnt) break;
+      cp.next(s_prefix, a.n_kv);
+    }
+  }
+  if (computes && open) seg.finish(a, seg_start, chunk, C, bad, lane);
 }
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
@@ -623,12 +847,28 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   const int slice = tid / per_slice;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = slice; s < nparts; s += n_slices) {
-    const float wgt = __expf(lse[static_cast<size_t>(s) * G] - mx);
-    const f32x4* src = reinterpret_cast<const f32x4*>(po + static_cast<size_t>(s) * stride_o + 8 * t);
-    acc0 += wgt * src[0];
-    acc1 += wgt * src[1];
-    den += wgt;
+  // Four partials per iteration, so each thread has eight 16-byte loads in
+  // flight; partials past the end weigh zero and are not read.
+  constexpr int kUnroll = 4;
+  for (int s0 = slice; s0 < nparts; s0 += kUnroll * n_slices) {
+    float wgt[kUnroll];
+    f32x4 v0[kUnroll], v1[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = s0 + u * n_slices;
+      const bool ok = s < nparts;
+      const int sc = ok ? s : slice;
+      const f32x4* src = reinterpret_cast<const f32x4*>(po + static_cast<size_t>(sc) * stride_o + 8 * t);
+      wgt[u] = ok ? __expf(lse[static_cast<size_t>(sc) * G] - mx) : 0.f;
+      v0[u] = src[0];
+      v1[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      acc0 += wgt[u] * v0[u];
+      acc1 += wgt[u] * v1[u];
+      den += wgt[u];
+    }
   }
   s_acc[2 * tid] = acc0;
   s_acc[2 * tid + 1] = acc1;
@@ -719,6 +959,34 @@ struct Resolved {
 
 using SplitFn = void (*)(DecodeArgs);
 
+// Register-ring depth of the shared-tile kernel (pages ahead per thread):
+// 16 bytes per piece, so kStage * pieces * 4 registers.
+#ifndef PKV_SHARED_STAGE
+#define PKV_SHARED_STAGE 8
+#endif
+template <bool kBf16, int D>
+constexpr int kSharedStage = (!kBf16 && D == 128) ? 4 : PKV_SHARED_STAGE;
+
+SplitFn shared_fn(int dtype, int head_dim) {
+  if (dtype == PKV_BF16)
+    return head_dim == 128 ? split_kernel_shared<true, 128, kSharedStage<true, 128>>
+                           : split_kernel_shared<true, 64, kSharedStage<true, 64>>;
+  return head_dim == 128 ? split_kernel_shared<false, 128, kSharedStage<false, 128>>
+                         : split_kernel_shared<false, 64, kSharedStage<false, 64>>;
+}
+
+// Groups above 16 query heads per KV head use the shared-tile kernel (one
+// chunk per workgroup); others the register-ring kernel (one chunk per
+// wavefront).
+inline bool use_shared(int group) { return waves_per_chunk(group) > 1; }
+
+size_t split_lds_bytes(int batch, int dtype, int head_dim, int group) {
+  const size_t prefix = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
+  if (!use_shared(group)) return prefix;
+  const size_t tile = static_cast<size_t>(kBlock) * head_dim * (dtype == PKV_BF16 ? 2 : 4);
+  return shared_tiles_offset(batch) + 3 * 2 * tile;
+}
+
 // bf16 tiles are 4 KiB per (page, head) at head_dim 128: two pages ahead fit
 // beside the accumulators at two wavefronts per SIMD.  fp32 tiles are twice
 // as large, so fp32 keeps one page ahead.
@@ -731,6 +999,7 @@ SplitFn split_fn(int dtype, int head_dim) {
 }
 
 int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
+  const bool shared = use_shared(group);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
@@ -739,10 +1008,12 @@ int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
   if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(split_fn(dtype, head_dim)), kWave * kWavesPerGroup, lds);
+      &per_cu,
+      reinterpret_cast<const void*>(shared ? shared_fn(dtype, head_dim) : split_fn(dtype, head_dim)),
+      kWave * kWavesPerGroup, lds);
   if (e != hipSuccess) return hip_fail("hipOccupancyMaxActiveBlocksPerMultiprocessor", e);
   if (per_cu < 1) per_cu = 1;
-  *out = n_cu * per_cu * (kWavesPerGroup / waves_per_chunk(group));
+  *out = n_cu * per_cu * (shared ? 1 : kWavesPerGroup / waves_per_chunk(group));
   return ok();
 }
 
@@ -767,18 +1038,26 @@ int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, i
   return PKV_OK;
 }
 
-int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch,
-                 const pkv_decode_opts* opts, Resolved* r) {
+int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, int32_t max_blocks,
+                 int32_t n_kv, const pkv_decode_opts* opts, Resolved* r) {
   r->wpc = waves_per_chunk(group);
-  r->lds = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
-  r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages : kDefaultMinChunk;
+  r->lds = split_lds_bytes(batch, dtype, head_dim, group);
+  r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages
+                                                     : default_min_chunk(group);
   if (opts && opts->n_items > 0) {
     if (opts->n_items > kMaxItems)
       return fail(PKV_ERR_INVALID_ARG, "decode: n_items above 2^22");
     r->n_items = opts->n_items;
     return PKV_OK;
   }
-  return default_items(dtype, head_dim, group, r->lds, &r->n_items);
+  int st = default_items(dtype, head_dim, group, r->lds, &r->n_items);
+  if (st != PKV_OK) return st;
+  // No more chunks than the largest possible cache (every sequence at
+  // max_blocks_per_seq pages) has chunks of min_chunk pages.
+  const int64_t max_pages = static_cast<int64_t>(batch) * max_blocks * n_kv;
+  const int64_t cap = std::max<int64_t>(1, (max_pages + r->min_chunk - 1) / r->min_chunk);
+  r->n_items = static_cast<int>(std::min<int64_t>(r->n_items, cap));
+  return PKV_OK;
 }
 
 int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
@@ -805,8 +1084,11 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
     return fail(PKV_ERR_INVALID_ARG, f + ": k_new/v_new must both be given, 16/4-byte aligned");
   const int group = n_q_heads / n_kv_heads;
   Resolved r;
-  st = resolve_opts(dtype, head_dim, group, batch, opts, &r);
+  st = resolve_opts(dtype, head_dim, group, batch, max_blocks_per_seq, n_kv_heads, opts, &r);
   if (st != PKV_OK) return st;
+  if (do_split && r.lds > kMaxLdsBytes)
+    return fail(PKV_ERR_UNSUPPORTED, f + ": batch too large for this group size (LDS " +
+                                         std::to_string(r.lds) + " bytes)");
   const int64_t need = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
   if (need < 0) return static_cast<int>(need);
   if (workspace_bytes < static_cast<size_t>(need))
@@ -837,16 +1119,18 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
-    const int chunks_per_group = kWavesPerGroup / r.wpc;
+    const bool shared = use_shared(group);
+    const int chunks_per_group = shared ? 1 : kWavesPerGroup / r.wpc;
     const int grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
-    hipLaunchKernelGGL(split_fn(dtype, head_dim), dim3(grid), dim3(kWave * kWavesPerGroup), r.lds,
-                       s, a);
+    hipLaunchKernelGGL(shared ? shared_fn(dtype, head_dim) : split_fn(dtype, head_dim), dim3(grid),
+                       dim3(kWave * kWavesPerGroup), r.lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
   }
   if (do_combine) {
     auto fn_c = dtype == PKV_BF16 ? combine_kernel<true> : combine_kernel<false>;
-    hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), r.lds, s, a, head_dim);
+    const size_t prefix_lds = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
+    hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), prefix_lds, s, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
@@ -959,12 +1243,22 @@ int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t
                             const_cast<void*>(workspace), workspace_bytes, opts);
 }
 
-int pkv_decode_default_items(int32_t dtype, int32_t head_dim, int32_t group, int32_t* out) {
-  if (!out) return fail(PKV_ERR_INVALID_ARG, "pkv_decode_default_items: out is NULL");
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "dtype");
-  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim");
-  if (group < 1 || group > pkv::kMaxGroup) return fail(PKV_ERR_UNSUPPORTED, "group");
-  return pkv::default_items(dtype, head_dim, group, (1 + pkv::kWavesPerGroup) * sizeof(int32_t), out);
+int pkv_decode_resolve(int32_t dtype, int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t batch, int32_t max_blocks_per_seq, const pkv_decode_opts* opts,
+                       pkv_decode_opts* resolved, int64_t* workspace_bytes) {
+  if (!resolved || !workspace_bytes)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_resolve: NULL output");
+  int st = pkv::check_decode_shapes("pkv_decode_resolve", n_q_heads, n_kv_heads, head_dim, 16, batch,
+                                    max_blocks_per_seq, 1, dtype);
+  if (st != PKV_OK) return st;
+  pkv::Resolved r;
+  st = pkv::resolve_opts(dtype, head_dim, n_q_heads / n_kv_heads, batch, max_blocks_per_seq,
+                         n_kv_heads, opts, &r);
+  if (st != PKV_OK) return st;
+  resolved->n_items = r.n_items;
+  resolved->min_chunk_pages = r.min_chunk;
+  *workspace_bytes = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
+  return *workspace_bytes < 0 ? static_cast<int>(*workspace_bytes) : ok();
 }
 
 int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_blocks, void* stream) {

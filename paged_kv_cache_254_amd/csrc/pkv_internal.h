@@ -20,8 +20,16 @@ constexpr int kWave = 64;           // CDNA wavefront
 constexpr int kWavesPerGroup = 4;   // wavefronts per workgroup of the decode kernels
 constexpr int kMaxBatch = 16000;    // keeps the per-workgroup length prefix in 64 KiB of LDS
 constexpr int kMaxGroup = 64;       // query heads per KV head
-constexpr int kDefaultMinChunk = 8; // pages
+// Default lower bound on pages per chunk.  Chunks are otherwise sized to
+// give one per resident wavefront (groups <= 16) or workgroup (larger
+// groups); on long sequences that makes them short, and each chunk pays a
+// start-up latency and one partial per query head.  Measured on MI355X: 64
+// pages for the one-wavefront-per-chunk kernel (131072-token GQA layer: 1024
+// chunks of 64 pages beat 2048 of 32 by 10%), 32 for the shared-tile kernel
+// (131072-token MQA: one chunk per CU is best).
+__host__ __device__ inline int default_min_chunk(int group) { return group > 16 ? 32 : 64; }
 constexpr int kMaxItems = 1 << 22;  // work items per decode launch
+constexpr size_t kMaxLdsBytes = 64 * 1024;  // LDS one decode workgroup may use
 
 __host__ __device__ inline int pages_of_len(int64_t len, int64_t max_blocks) {
   if (len <= 0 || len > max_blocks * kBlock) return 0;

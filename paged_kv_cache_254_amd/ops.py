@@ -102,14 +102,19 @@ def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim
                  "pkv_decode_workspace_bytes")
 
 
-def decode_default_items(dtype_code: int, head_dim: int, group: int) -> int:
-    n = ctypes.c_int32()
-    check(lib.pkv_decode_default_items(dtype_code, head_dim, group, ctypes.byref(n)), "pkv_decode_default_items")
-    return n.value
+def decode_resolve(dtype_code: int, head_dim: int, n_q_heads: int, n_kv_heads: int, batch: int,
+                   max_blocks: int, n_items: int = 0, min_chunk_pages: int = 0):
+    """(n_items, min_chunk_pages, workspace_bytes) the device calls use for these shapes."""
+    res = DecodeOpts()
+    ws = ctypes.c_int64()
+    check(lib.pkv_decode_resolve(dtype_code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks,
+                                 ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages))), ctypes.byref(res),
+                                 ctypes.byref(ws)), "pkv_decode_resolve")
+    return res.n_items, res.min_chunk_pages, ws.value
 
 
 def decode_plan(seq_lens: Sequence[int], n_kv_heads: int, max_blocks: int, n_items: int,
-                min_chunk_pages: int = 0):
+                min_chunk_pages: int):
     """(chunk_pages, first_chunk[B][Hkv], last_chunk[B][Hkv]) as the kernels compute them."""
     lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
     B = len(lens)
@@ -131,19 +136,18 @@ def kv_append(k_new, v_new, k_pages, v_pages, block_table, positions, stream=Non
 
 
 class Decoder:
-    """Holds the resolved work split and a workspace for one decode shape."""
+    """Holds the resolved work split and a workspace for one decode shape
+    (batch, heads, head_dim, dtype and the block-table width max_blocks)."""
 
-    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype,
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype, max_blocks: int,
                  n_items: int = 0, min_chunk_pages: int = 0, device="cuda"):
         import torch
         code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
-        if n_items <= 0:
-            n_items = decode_default_items(code, head_dim, n_q_heads // n_kv_heads)
-        self.n_items = n_items
-        self.min_chunk_pages = min_chunk_pages
-        self.ws_bytes = decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
+        self.n_items, self.min_chunk_pages, self.ws_bytes = decode_resolve(
+            code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks, n_items, min_chunk_pages)
         self.workspace = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=device)
         self.shape = (batch, n_q_heads, n_kv_heads, head_dim)
+        self.max_blocks = max_blocks
 
     def _args(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream):
         B, Hq, D = q.shape
@@ -201,8 +205,8 @@ def paged_decode_attn(q, k_pages, v_pages, block_table, seq_lens, scale, out=Non
     import torch
     if out is None:
         out = torch.empty_like(q)
-    dec = Decoder(q.shape[0], q.shape[1], k_pages.shape[1], q.shape[2], q.dtype, n_items, min_chunk_pages,
-                  device=q.device)
+    dec = Decoder(q.shape[0], q.shape[1], k_pages.shape[1], q.shape[2], q.dtype, block_table.shape[1], n_items,
+                  min_chunk_pages, device=q.device)
     return dec(q, k_pages, v_pages, block_table, seq_lens, scale, out, stream)
 
 

@@ -29,7 +29,8 @@ def pkv():
 def _run_step(pkv, c, n_items=0, min_chunk=0, out=None):
     w = c.w
     pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
-    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), n_items, min_chunk)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), c.max_blocks, n_items,
+                      min_chunk)
     out = torch.empty_like(c.q) if out is None else out
     dec(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out)
     torch.cuda.synchronize()
@@ -77,6 +78,8 @@ SMALL = [
     ("g32_f32_64", 2, 32, 1, 64, "f32", [20, 90], 5, 1),
     ("mha_bf16_128_one_chunk", 3, 4, 4, 128, "bf16", [10, 47, 90], 1, 64),
     ("ragged_many", 9, 8, 4, 128, "bf16", [0, 1, 2, 15, 16, 17, 63, 64, 250], 11, 1),
+    ("g32_ragged_pairs", 6, 64, 2, 128, "bf16", [0, 1, 15, 16, 40, 300], 5, 1),
+    ("g48_f32_64_ragged", 4, 96, 2, 64, "f32", [3, 33, 0, 70], 3, 2),
 ]
 
 
@@ -110,7 +113,7 @@ def test_split_partials_match_oracle(pkv):
     qh = H.f64(c.q)
     n_items = 7
     pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
-    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, n_items, 1)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, c.max_blocks, n_items, 1)
     dec.workspace.fill_(255)
     out = torch.full_like(c.q, float("nan"))
     dec.split(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out)
@@ -147,7 +150,7 @@ def test_invariances_and_determinism(pkv):
     c = H.setup(w, device="cuda", gen_device="cpu")
     out1, _ = _run_step(pkv, c, 5, 1)
     # same inputs again: bit-identical (no atomics, fixed reduction order)
-    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, 5, 1)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, c.max_blocks, 5, 1)
     out2 = torch.empty_like(c.q)
     dec(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out2)
     torch.cuda.synchronize()
@@ -173,7 +176,7 @@ def test_invariances_and_determinism(pkv):
     assert torch.equal(out4[2], out1[2])
     # a different split gives the same result within fp32 rounding of the combine
     for n_items, mc in ((1, 1), (64, 1), (3, 4)):
-        dec2 = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, n_items, mc)
+        dec2 = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.bfloat16, c.max_blocks, n_items, mc)
         out5 = torch.empty_like(c.q)
         dec2(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out5)
         torch.cuda.synchronize()
@@ -266,6 +269,7 @@ STEP = [
     ("step_mha_bf16", 3, 4, 4, 128, "bf16", [47, 100, 3], 0, 0),
     ("step_mqa64_bf16", 2, 64, 1, 128, "bf16", [150, 17], 5, 1),
     ("step_g3_f32_128", 2, 6, 2, 128, "f32", [64, 5], 2, 2),
+    ("step_g32_ragged", 5, 64, 2, 128, "bf16", [0, 15, 16, 47, 130], 4, 1),
 ]
 
 
@@ -279,7 +283,8 @@ def test_fused_step(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, min_chunk)
     ek, ev = OA.append(H.bits(c.k_pages), H.bits(c.v_pages), c.bt_np, c.cached, H.bits(c.k_new),
                        H.bits(c.v_new), H.BS)
     kp, vp = c.k_pages.clone(), c.v_pages.clone()
-    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), n_items, min_chunk)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), c.max_blocks, n_items,
+                      min_chunk)
     out = torch.empty_like(c.q)
     dec.step(c.q, c.k_new, c.v_new, kp, vp, c.bt, c.seq_lens, w.scale, out)
     torch.cuda.synchronize()
