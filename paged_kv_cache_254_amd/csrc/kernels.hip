@@ -486,123 +486,6 @@ struct Segment {
   }
 };
 
-// Pages [j0, j1) of the (b, h) pair for query heads gblk*16 .. gblk*16+15,
-// streamed through a ring of kDepth + 1 register buffers: kDepth pages are
-// in flight ahead of the one being computed.
-template <bool kBf16, int D, int kDepth>
-__device__ void process_segment(const DecodeArgs& a, int b, int h, int j0, int j1, int n_pages,
-                                int seg_start, int chunk, int C, int gblk, int lane) {
-  using O = Ops<kBf16, D>;
-  constexpr int kTileBytes = kBlock * D * O::ES;
-  constexpr int kBufs = kDepth + 1;
-  const int c = lane >> 4, n = lane & 15;
-  Segment<kBf16, D> seg;
-  seg.begin(a, b, h, n_pages, j1 == n_pages, gblk, lane);
-
-  const size_t head_off = static_cast<size_t>(h) * kTileBytes;
-  const size_t page_stride = static_cast<size_t>(kTileBytes) * a.n_kv;
-  char* kpool = static_cast<char*>(a.k_pages) + head_off;
-  char* vpool = static_cast<char*>(a.v_pages) + head_off;
-  const const_i32* bt_row =
-      (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
-  const uint32_t koff = 16u * lane;
-  const uint32_t voff = O::ES * (n * kBlock + 4 * c);
-  bool bad = false;
-  // Loads of logical block j.  Past the range's end (the ring runs kDepth
-  // pages ahead) the loads are issued with an empty range, so every ring
-  // step issues the same instructions but nothing is read; a page id outside
-  // the pool is never dereferenced either (and poisons the result).
-  auto issue = [&](PageRegs<kBf16, D>& r, int j) {
-    const bool in_range = j < j1;
-    int pg = bt_row[min(j, j1 - 1)];
-    const bool pg_ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-    bad |= in_range && !pg_ok;
-    if (!pg_ok) pg = 0;
-    const size_t off = static_cast<size_t>(pg) * page_stride;
-    load_page(r, kpool + off, vpool + off, koff, voff, in_range && pg_ok ? kTileBytes : 0);
-  };
-  const int last = n_pages - 1;
-  auto patch_and_store = [&](PageRegs<kBf16, D>& r) {
-    seg.patch(r, lane);
-    // One wavefront per pair writes the token to the pool (the query-head
-    // blocks of a large group all patch their registers the same way).
-    const int pg = bt_row[last];
-    if (gblk == 0 && static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages))
-      seg.store_new_token(kpool, vpool, page_stride, pg, lane);
-  };
-
-  PageRegs<kBf16, D> buf[kBufs];
-#pragma unroll
-  for (int s = 0; s < kDepth; ++s) issue(buf[s], j0 + s);
-  int j = j0;
-  while (j < j1) {
-#pragma unroll
-    for (int s = 0; s < kBufs; ++s) {
-      // Keep the compiler from sinking these loads below the compute: the
-      // requests must be in flight while this page is processed.
-      __builtin_amdgcn_sched_barrier(0);
-      issue(buf[(s + kDepth) % kBufs], j + kDepth);
-      __builtin_amdgcn_sched_barrier(0);
-      if (seg.append && j == last) patch_and_store(buf[s]);
-      seg.page(buf[s], j, a.scale_log2, lane);
-      if (++j >= j1) break;
-    }
-  }
-  seg.finish(a, seg_start, chunk, C, bad, lane);
-}
-
-// At least two wavefronts per SIMD: caps registers at 256 per lane, which the
-// bf16 kernel fits without spilling; fp32 at head_dim 128 needs more and runs
-// one wavefront per SIMD.
-template <bool kBf16, int D>
-constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
-
-template <bool kBf16, int D, int kDepth>
-__global__ void __launch_bounds__(kWave * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu<kBf16, D>)))
-split_kernel(DecodeArgs a) {
-  extern __shared__ int32_t smem[];
-  int32_t* s_prefix = smem;
-  int32_t* s_wsum = smem + a.batch + 1;
-  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = uni(threadIdx.x / kWave);
-  const int wpc = a.waves_per_chunk;
-  const int chunk = blockIdx.x * (kWavesPerGroup / wpc) + wave / wpc;
-  const int gblk = wave % wpc;
-  if (chunk >= a.n_items || gblk * 16 >= a.group) return;
-  const int total = uni(a.n_kv * s_prefix[a.batch]);
-  const int C = chunk_pages(total, a.n_items, a.min_chunk);
-  const int64_t f64 = static_cast<int64_t>(chunk) * C;
-  if (f64 >= total) return;
-  int f = static_cast<int>(f64);
-  const int fend = static_cast<int>(min(f64 + C, static_cast<int64_t>(total)));
-
-  int b = uni(find_seq(s_prefix, a.batch, a.n_kv, f));
-  int pb = uni(s_prefix[b]);
-  int n = uni(s_prefix[b + 1]) - pb;
-  int off = f - a.n_kv * pb;
-  int h = off / n;
-  int j = off - h * n;
-  while (true) {
-    const int cnt = min(n - j, fend - f);
-    const int seg_start = a.n_kv * pb + h * n;
-    process_segment<kBf16, D, kDepth>(a, b, h, j, j + cnt, n, seg_start, chunk, C, gblk, lane);
-    f += cnt;
-    if (f >= fend) break;
-    j = 0;
-    if (++h == a.n_kv) {
-      h = 0;
-      do {
-        ++b;
-        pb = uni(s_prefix[b]);
-        n = uni(s_prefix[b + 1]) - pb;
-      } while (n == 0);
-    }
-  }
-}
-
 // Position in the flattened (sequence, KV head, page) order of all pages:
 // flat index f, sequence b (with pb = pages before b and n = pages of b),
 // KV head h, page j of the pair.
@@ -633,6 +516,121 @@ struct FlatCursor {
     }
   }
 };
+
+// At least two wavefronts per SIMD: caps registers at 256 per lane, which the
+// bf16 kernel fits without spilling; fp32 at head_dim 128 needs more and runs
+// one wavefront per SIMD.
+template <bool kBf16, int D>
+constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
+
+// Split-KV decode for groups of at most 16 query heads per KV head: one chunk
+// of the flattened (sequence, KV head, page) order per wavefront, all query
+// heads of the group in the lanes' MFMA columns.  A loader cursor runs kDepth
+// pages ahead of the compute cursor through a ring of kDepth + 1 register
+// buffers, across pair boundaries, so the stream of tile loads never drains
+// inside a chunk; the compute cursor closes a segment (writes its output row
+// or partial) and opens the next one when the pair changes.
+template <bool kBf16, int D, int kDepth>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu<kBf16, D>)))
+split_kernel(DecodeArgs a) {
+  using O = Ops<kBf16, D>;
+  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int kBufs = kDepth + 1;
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  int32_t* s_wsum = smem + a.batch + 1;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uni(threadIdx.x / kWave);
+  const int chunk = blockIdx.x * kWavesPerGroup + wave;
+  if (chunk >= a.n_items) return;
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int64_t f64 = static_cast<int64_t>(chunk) * C;
+  if (f64 >= total) return;
+  const int f0 = static_cast<int>(f64);
+  const int cnt = static_cast<int>(min(f64 + C, static_cast<int64_t>(total))) - f0;
+  const size_t page_stride = static_cast<size_t>(kTile) * a.n_kv;
+  char* kp0 = static_cast<char*>(a.k_pages);
+  char* vp0 = static_cast<char*>(a.v_pages);
+  const int c = lane >> 4, n = lane & 15;
+  const uint32_t koff = 16u * lane;
+  const uint32_t voff = O::ES * (n * kBlock + 4 * c);
+  auto bt_row = [&](int b) {
+    return (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
+  };
+
+  // ---- loader.  Past the chunk's end the loads are issued with an empty
+  // range, so every ring step issues the same instructions but nothing is
+  // read; a page id outside the pool is never dereferenced either.
+  FlatCursor ld;
+  ld.seek(s_prefix, a.batch, a.n_kv, f0);
+  int issued = 0;
+  PageRegs<kBf16, D> buf[kBufs];
+  int page_of[kBufs];   // page id of each buffer (scalar), for the compute side
+  auto issue = [&](PageRegs<kBf16, D>& r, int& pg_out) {
+    const bool in = issued < cnt;
+    const int pg = bt_row(ld.b)[ld.j];
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
+    load_page(r, kp0 + off, vp0 + off, koff, voff, in && ok ? kTile : 0);
+    pg_out = pg;
+    if (in) {
+      ++issued;
+      if (issued < cnt) ld.next(s_prefix, a.n_kv);
+    }
+  };
+
+  // ---- compute.
+  FlatCursor cp;
+  cp.seek(s_prefix, a.batch, a.n_kv, f0);
+  Segment<kBf16, D> seg;
+  bool open = false, bad = false;
+  int seg_start = 0;
+  auto compute = [&](PageRegs<kBf16, D>& r, int pg, int p) {
+    if (open && (cp.b != seg.b || cp.h != seg.h)) {
+      seg.finish(a, seg_start, chunk, C, bad, lane);
+      open = false;
+    }
+    if (!open) {
+      const bool ends_pair = cp.j + (cnt - p) >= cp.n;
+      seg.begin(a, cp.b, cp.h, cp.n, ends_pair, 0, lane);
+      seg_start = a.n_kv * cp.pb + cp.h * cp.n;
+      bad = false;
+      open = true;
+    }
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    bad |= !ok;
+    if (seg.append && cp.j == cp.n - 1) {
+      seg.patch(r, lane);
+      if (ok) {
+        const size_t head_off = static_cast<size_t>(cp.h) * kTile;
+        seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+      }
+    }
+    seg.page(r, cp.j, a.scale_log2, lane);
+  };
+
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s]);
+  int p = 0;
+  while (p < cnt) {
+#pragma unroll
+    for (int s = 0; s < kBufs; ++s) {
+      // Keep the compiler from sinking these loads below the compute: the
+      // requests must be in flight while this page is processed.
+      __builtin_amdgcn_sched_barrier(0);
+      issue(buf[(s + kDepth) % kBufs], page_of[(s + kDepth) % kBufs]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf[s], page_of[s], p);
+      if (++p >= cnt) break;
+      cp.next(s_prefix, a.n_kv);
+    }
+  }
+  if (open) seg.finish(a, seg_start, chunk, C, bad, lane);
+}
 
 // LDS offset of the tile ring, after the length prefix (16-byte aligned).
 __host__ __device__ inline size_t shared_tiles_offset(int batch) {
