@@ -1,0 +1,135 @@
+"""Plants plausible mistakes in the oracle (CPU only) and checks that the pins
+catch each one: a pin that cannot fail proves nothing."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import kv_bytes as KB
+
+from . import test_oracle_attention as T
+from . import test_oracle_kv_bytes as TB
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def _sdpa_cases():
+    return [(4, 2, 64, 4, [38, 101]), (2, 2, 16, 8, [1, 16, 17]), (8, 1, 32, 8, [33, 5])]
+
+
+def test_interleaved_head_map_is_caught(monkeypatch):
+    def decode_interleaved(q, k_pages, v_pages, block_table, seq_lens, n_q_heads, n_kv_heads, block_size, scale):
+        q = np.asarray(q, dtype=np.float64)
+        out = np.zeros(q.shape)
+        for b in range(q.shape[0]):
+            K, V = A.gather(k_pages, v_pages, block_table[b], int(seq_lens[b]), block_size)
+            for hq in range(n_q_heads):
+                h = hq % n_kv_heads                     # planted: interleaved groups
+                out[b, hq] = A.attend(q[b, hq], K[:, h], V[:, h], scale)
+        return out
+    monkeypatch.setattr(A, "decode", decode_interleaved)
+    assert _fails(T.test_gqa_equals_mha_with_repeated_kv_heads)
+    assert any(_fails(T.test_matches_torch_sdpa_float64, *c) for c in _sdpa_cases())
+
+
+def test_missing_scale_is_caught(monkeypatch):
+    orig = A.attend
+    monkeypatch.setattr(A, "attend", lambda q, K, V, scale: orig(q, K, V, 1.0))
+    assert any(_fails(T.test_matches_torch_sdpa_float64, *c) for c in _sdpa_cases())
+    assert _fails(T.test_brute_force_python_loops)
+
+
+def test_dropped_last_token_is_caught(monkeypatch):
+    orig = A.gather
+    monkeypatch.setattr(A, "gather", lambda k, v, row, n, bs: orig(k, v, row, max(n - 1, 0), bs))
+    assert any(_fails(T.test_matches_torch_sdpa_float64, *c) for c in _sdpa_cases())
+    assert _fails(T.test_single_token_returns_its_value)
+
+
+def test_untransposed_value_tile_is_caught(monkeypatch):
+    def gather_bad_v(k_pages, v_pages, block_table_row, n_tokens, block_size):
+        K, _ = A_gather(k_pages, v_pages, block_table_row, n_tokens, block_size)
+        n_blocks = (n_tokens + block_size - 1) // block_size
+        pages = np.asarray(block_table_row[:n_blocks], dtype=np.int64)
+        vp = np.asarray(v_pages[pages])              # [blk][Hkv][D][bs] read as if [blk][bs][Hkv][D]
+        V = vp.reshape(n_blocks * block_size, k_pages.shape[1], -1)[:n_tokens]
+        return K, np.asarray(V, dtype=np.float64)
+    A_gather = A.gather
+    monkeypatch.setattr(A, "gather", gather_bad_v)
+    assert _fails(T.test_single_token_returns_its_value) or \
+        any(_fails(T.test_matches_torch_sdpa_float64, *c) for c in _sdpa_cases())
+
+
+def test_wrong_key_chunk_order_is_caught(monkeypatch):
+    def key_tile_swapped(k_pages, page, head):
+        chunks, bs, x = k_pages.shape[2], k_pages.shape[3], k_pages.shape[4]
+        return k_pages[page, head].transpose(1, 2, 0).reshape(bs, chunks * x)   # planted: x-major
+    def gather_swapped(k_pages, v_pages, row, n, bs):
+        n_blocks = (n + bs - 1) // bs
+        K = np.concatenate([key_tile_swapped(k_pages, int(p), h)[None] for p in row[:n_blocks]
+                            for h in range(k_pages.shape[1])]) if n_blocks else np.zeros((0, bs, 1))
+        K = K.reshape(n_blocks, k_pages.shape[1], bs, -1).transpose(0, 2, 1, 3).reshape(n_blocks * bs,
+                                                                                         k_pages.shape[1], -1)[:n]
+        _, V = A_gather(k_pages, v_pages, row, n, bs)
+        return np.asarray(K, dtype=np.float64), V
+    A_gather = A.gather
+    monkeypatch.setattr(A, "gather", gather_swapped)
+    assert any(_fails(T.test_matches_torch_sdpa_float64, *c) for c in _sdpa_cases())
+
+
+def test_lse_without_max_is_caught(monkeypatch):
+    def partial_bad(q, K, V, scale):
+        o, lse = orig(q, K, V, scale)
+        if not math.isfinite(lse):
+            return o, lse
+        s = scale * (np.asarray(K, dtype=np.float64) @ np.asarray(q, dtype=np.float64))
+        return o, float(lse - s.max())                  # planted: forgot to add the max back
+    orig = A.partial
+    monkeypatch.setattr(A, "partial", partial_bad)
+    assert _fails(T.test_partial_lse_closed_form) or _fails(T.test_partials_combine_to_full_attention)
+
+
+def test_combine_without_reweighting_is_caught(monkeypatch):
+    def combine_plain(outs, lses):
+        outs = [np.asarray(o, dtype=np.float64) for o in outs if True]
+        lses = np.asarray(lses, dtype=np.float64)
+        keep = [o for o, l in zip(outs, lses) if np.isfinite(l)]
+        return np.mean(keep, axis=0) if keep else np.zeros_like(outs[0])   # planted: plain average
+    monkeypatch.setattr(A, "lse_combine", combine_plain)
+    assert _fails(T.test_partials_combine_to_full_attention)
+
+
+def test_append_slot_index_mistake_is_caught(monkeypatch):
+    def append_bad(k_pages, v_pages, block_table, positions, k_new, v_new, block_size):
+        k_out = np.array(k_pages, copy=True)
+        v_out = np.array(v_pages, copy=True)
+        x = k_pages.shape[4]
+        for b in range(k_new.shape[0]):
+            pos = int(positions[b])
+            page = int(block_table[b][pos // block_size])
+            slot = (pos + 1) % block_size                 # planted: off by one slot
+            for h in range(k_new.shape[1]):
+                for i in range(k_new.shape[2]):
+                    k_out[page, h, i // x, slot, i % x] = k_new[b, h, i]
+                    v_out[page, h, i, slot] = v_new[b, h, i]
+        return k_out, v_out
+    monkeypatch.setattr(A, "append", append_bad)
+    assert _fails(T.test_append_writes_exactly_the_slot_bits)
+
+
+def test_kv_formula_without_factor_two_is_caught(monkeypatch):
+    monkeypatch.setattr(KB, "kv_cache_bytes", lambda L, n_kv, d, s, b, p: L * n_kv * d * s * b * p)
+    assert any(_fails(TB.test_per_token_matches_pages, c) for c in TB.GOLDEN["per_token"])
+
+
+def test_kv_formula_with_query_heads_is_caught():
+    # Using n_q_heads (32 for Llama-3-8B) where n_kv_heads belongs gives 512 KiB, not the printed 128 KiB.
+    case = [c for c in TB.GOLDEN["per_token"] if c["model"] == "Llama-3-8B"][0]
+    assert KB.kv_bytes_per_token(case["n_layers"], 32, case["head_dim"], case["bytes_per_elem"]) != case["bytes"]
