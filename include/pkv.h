@@ -276,6 +276,20 @@ int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
                     int32_t* last_chunk);
 
 /* ------------------------------------------------------------------------ *
+ * copy_blocks (device): copy-on-write of shared blocks (prefix sharing with
+ * block-level copy-on-write, CS336 notes "PagedAttention (vLLM)").  For each
+ * i < n_pairs, the K and V tiles of every KV head of page src_pages[i] are
+ * copied bit for bit to page dst_pages[i] (device int32 arrays), typically
+ * the (old, new) pair returned by pkv_seq_reserve_for_write.  Pairs with an
+ * id outside [0, num_pages) or src == dst are skipped.  The destination pages
+ * must be distinct and must not be source pages of the same call.
+ * ------------------------------------------------------------------------ */
+int pkv_copy_blocks(void* k_pages, void* v_pages, const int32_t* src_pages,
+                    const int32_t* dst_pages, int32_t n_pairs, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_pages, int32_t dtype,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Bandwidth probes (device), for measuring what the HBM path can sustain.
  * pkv_hbm_read_probe streams `bytes` (multiple of 16, buf 16-byte aligned)
  * through 16-byte loads and writes one word per workgroup to sink (device,

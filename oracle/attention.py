@@ -155,6 +155,19 @@ def decode_one(q, k_pages, v_pages, block_table_row, seq_len: int, b: int, hq: i
     return attend(q[b, hq], K[:, 0, :], V[:, 0, :], scale)
 
 
+def copy_blocks(k_pages, v_pages, src_pages, dst_pages):
+    """Copies of the pools where page dst_pages[i] holds page src_pages[i]'s
+    contents (every KV head, K and V): the copy half of block-level
+    copy-on-write (CS336 lecture 10 notes, "PagedAttention (vLLM)": shared
+    blocks are split only when generations diverge)."""
+    k_out = np.array(k_pages, copy=True)
+    v_out = np.array(v_pages, copy=True)
+    for s, d in zip(src_pages, dst_pages):
+        k_out[int(d)] = k_pages[int(s)]
+        v_out[int(d)] = v_pages[int(s)]
+    return k_out, v_out
+
+
 def append(k_pages, v_pages, block_table, positions, k_new, v_new, block_size: int):
     """Copies of the pools with the step's new K/V written into their slots:
     for each sequence b and KV head h, token positions[b] goes to slot

@@ -85,6 +85,7 @@ SIGNATURES = {
     "pkv_decode_resolve": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(DecodeOpts),
                                           ctypes.POINTER(DecodeOpts), ctypes.POINTER(ctypes.c_int64)]),
     "pkv_decode_plan": (ctypes.c_int, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32]),
+    "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_hbm_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "pkv_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
 }

@@ -919,6 +919,28 @@ append_kernel(const void* k_new, const void* v_new, void* k_pages, void* v_pages
   }
 }
 
+// copy_blocks: one wavefront per (pair, KV head) copies the K tile and the V
+// tile of page src[i] to page dst[i] (copy-on-write of a shared block), 16
+// bytes per lane per instruction.  Pairs with an id outside the pool, or
+// src == dst, are skipped.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(char* k_pages, char* v_pages, const int32_t* src, const int32_t* dst,
+                   int n_pairs, int n_kv, int tile_bytes, int num_pages) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
+  if (item >= n_pairs * n_kv) return;
+  const int i = item / n_kv;
+  const int h = item - i * n_kv;
+  const int s = src[i], d = dst[i];
+  if (s < 0 || s >= num_pages || d < 0 || d >= num_pages || s == d) return;
+  const size_t so = (static_cast<size_t>(s) * n_kv + h) * tile_bytes;
+  const size_t dof = (static_cast<size_t>(d) * n_kv + h) * tile_bytes;
+  for (int off = 16 * lane; off < tile_bytes; off += 16 * kWave) {
+    *reinterpret_cast<u32x4*>(k_pages + dof + off) = *reinterpret_cast<const u32x4*>(k_pages + so + off);
+    *reinterpret_cast<u32x4*>(v_pages + dof + off) = *reinterpret_cast<const u32x4*>(v_pages + so + off);
+  }
+}
+
 __global__ void __launch_bounds__(256)
 read_probe_kernel(const u32x4* __restrict__ buf, size_t n16, uint32_t* sink) {
   uint32_t x = 0;
@@ -1257,6 +1279,31 @@ int pkv_decode_resolve(int32_t dtype, int32_t head_dim, int32_t n_q_heads, int32
   resolved->min_chunk_pages = r.min_chunk;
   *workspace_bytes = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
   return *workspace_bytes < 0 ? static_cast<int>(*workspace_bytes) : ok();
+}
+
+int pkv_copy_blocks(void* k_pages, void* v_pages, const int32_t* src_pages,
+                    const int32_t* dst_pages, int32_t n_pairs, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_pages, int32_t dtype,
+                    void* stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_blocks: dtype");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_blocks: head_dim must be 64 or 128");
+  if (block_size != pkv::kBlock) return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_blocks: block_size must be 16");
+  if (n_pairs < 0 || n_kv_heads < 1 || num_pages < 1 ||
+      static_cast<int64_t>(n_pairs) * n_kv_heads >= (int64_t{1} << 31))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: bad n_pairs/n_kv_heads/num_pages");
+  if (n_pairs == 0) return ok();
+  if (!k_pages || !v_pages || !src_pages || !dst_pages || !pkv::aligned(k_pages, 16) ||
+      !pkv::aligned(v_pages, 16) || !pkv::aligned(src_pages, 4) || !pkv::aligned(dst_pages, 4))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_copy_blocks: NULL or misaligned pointer");
+  const int tile = pkv::kBlock * head_dim * (dtype == PKV_BF16 ? 2 : 4);
+  const int items = n_pairs * n_kv_heads;
+  hipLaunchKernelGGL(pkv::copy_blocks_kernel, dim3((items + pkv::kWavesPerGroup - 1) / pkv::kWavesPerGroup),
+                     dim3(256), 0, static_cast<hipStream_t>(stream), static_cast<char*>(k_pages),
+                     static_cast<char*>(v_pages), src_pages, dst_pages, n_pairs, n_kv_heads, tile, num_pages);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::hip_fail("copy_blocks launch", e);
+  return ok();
 }
 
 int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_blocks, void* stream) {

@@ -135,6 +135,17 @@ def kv_append(k_new, v_new, k_pages, v_pages, block_table, positions, stream=Non
                             _dtype_code(k_new), _stream(stream)), "pkv_kv_append")
 
 
+def copy_blocks(k_pages, v_pages, src_pages, dst_pages, stream=None) -> None:
+    """Copy every KV head's K and V tile of page src_pages[i] to dst_pages[i]."""
+    import torch
+    if src_pages.shape != dst_pages.shape or src_pages.dtype != torch.int32 or dst_pages.dtype != torch.int32:
+        raise ValueError("src_pages and dst_pages must be int32 tensors of one shape")
+    n = src_pages.numel()
+    check(lib.pkv_copy_blocks(_ptr(k_pages), _ptr(v_pages), _ptr(src_pages), _ptr(dst_pages), n,
+                              k_pages.shape[1], k_pages.shape[2] * k_pages.shape[4], BLOCK_SIZE, k_pages.shape[0],
+                              _dtype_code(k_pages), _stream(stream)), "pkv_copy_blocks")
+
+
 class Decoder:
     """Holds the resolved work split and a workspace for one decode shape
     (batch, heads, head_dim, dtype and the block-table width max_blocks)."""

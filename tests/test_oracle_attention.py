@@ -283,3 +283,18 @@ def test_append_writes_exactly_the_slot_bits():
                 exp_k[p, h, d // x, s, d % x] = kn[b, h, d] != k[p, h, d // x, s, d % x]
                 exp_v[p, h, d, s] = vn[b, h, d] != v[p, h, d, s]
     assert np.array_equal(kd, exp_k) and np.array_equal(vd, exp_v)
+
+
+def test_copy_blocks_then_fork_decode_equals_unshared_cache():
+    # Three sequences sharing a 40-token prefix (pages shared through the block
+    # table) give the same outputs as three private copies of that prefix.
+    rng = np.random.default_rng(21)
+    Hkv, G, D, x = 2, 3, 16, 4
+    k, v = _pools(rng, 12, Hkv, D, x)
+    shared = np.array([[5, 9, 2]] * 3, dtype=np.int32)
+    q = rng.standard_normal((3, Hkv * G, D))
+    out_shared = A.decode(q, k, v, shared, [40] * 3, Hkv * G, Hkv, BS, 0.3)
+    k2, v2 = A.copy_blocks(k, v, [5, 9, 2, 5, 9, 2], [0, 1, 3, 4, 6, 7])
+    private = np.array([[5, 9, 2], [0, 1, 3], [4, 6, 7]], dtype=np.int32)
+    assert np.array_equal(A.decode(q, k2, v2, private, [40] * 3, Hkv * G, Hkv, BS, 0.3), out_shared)
+    assert np.array_equal(k2[0], k[5]) and np.array_equal(v2[7], v[2]) and np.array_equal(k2[8], k[8])
