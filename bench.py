@@ -82,10 +82,13 @@ def setup(w, device):
         seq_lens=torch.from_numpy(att.astype(np.int32)).to(device),
     )
     kv_bytes_layer = int(att.sum()) * w.n_kv_heads * w.head_dim * 2 * w.elem_bytes
-    # Small caches fit in the last-level cache: rotate enough copies that one
-    # step streams at least 4x its size from HBM.
-    n_copies = max(w.n_layers, math.ceil(4 * MALL_BYTES / kv_bytes_layer)) if kv_bytes_layer < 2 * MALL_BYTES \
-        else w.n_layers
+    # Rotate pool copies so that between two reads of one copy at least twice
+    # the last-level cache's size of other KV streams through it, and small
+    # caches stream at least 4x that cache per step: no launch can be served
+    # from data the previous launches left in the last-level cache.
+    n_copies = max(w.n_layers, 1 + math.ceil(2 * MALL_BYTES / kv_bytes_layer))
+    if kv_bytes_layer < 2 * MALL_BYTES:
+        n_copies = max(n_copies, math.ceil(4 * MALL_BYTES / kv_bytes_layer))
     layers = []
     for i in range(n_copies):
         L = Layer()
@@ -292,6 +295,7 @@ def main():
             "kernel": "split_kernel", "avg_launch_ms": round(split_avg, 5),
             "algorithmic_bytes_per_launch": S["kv_bytes_layer"],
         },
+        "split_median_ms": round(float(np.median(split_ms)), 5),
         "combine_avg_ms": round(float(np.mean(comb_ms)), 5),
         "hbm_read_probe_gbs": None if probe is None else round(probe, 1),
         "cpu_baseline": cpu,

@@ -170,8 +170,9 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  *
  * Work split: the pages of all (sequence, KV head) pairs, taken in that order,
  * are cut into n_items equal chunks of C = max(min_chunk_pages,
- * ceil(total / n_items)) pages.  Each chunk is processed by one wavefront (or
- * ceil(group / 16) wavefronts for groups above 16).  A (sequence, KV head)
+ * ceil(total / n_items)) pages.  Each chunk is processed by one wavefront per
+ * block of 16 query heads of the group (1, 2 or 4 wavefronts; a 3-block group
+ * uses 4, the last idle).  A (sequence, KV head)
  * whose pages fall in one chunk gets its output written directly; otherwise
  * each chunk writes a partial (normalised output and natural-log sum of
  * exponentials) and the combine merges them.
@@ -179,8 +180,8 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  * workspace: device, 256-byte aligned, at least
  * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
  * bytes (n_items after defaults are applied).  Contents on entry are ignored.
- * opts (nullable): n_items <= 0 means one chunk per wavefront (groups <= 16)
- * or per workgroup (larger groups) the device can hold at once;
+ * opts (nullable): n_items <= 0 means as many chunks as the device holds at
+ * once (resident wavefronts divided by the wavefronts per chunk);
  * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups).
  * ------------------------------------------------------------------------ */
 typedef struct pkv_decode_opts {

@@ -281,6 +281,12 @@ struct PageRegs {
 #ifndef PKV_KV_LOAD_AUX
 #define PKV_KV_LOAD_AUX 2
 #endif
+// Cache policy when several wavefronts (one per 16-head block of a large
+// group) read the same tiles at about the same time: default, so that the
+// first reader's lines serve the others from the caches.
+#ifndef PKV_KV_LOAD_AUX_GROUPED
+#define PKV_KV_LOAD_AUX_GROUPED 0
+#endif
 
 // Issues the loads of one (page, KV head) tile.  kbase/vbase are wave-uniform
 // and become the base of a buffer resource whose range is exactly one tile, so
@@ -288,7 +294,7 @@ struct PageRegs {
 // one register and an offset past the tile reads zero instead of faulting.
 // range = 0 issues the same loads without touching memory (they return
 // zeros): used past the end of a range and for page ids outside the pool.
-template <bool kBf16, int D>
+template <bool kBf16, int D, int kAux = PKV_KV_LOAD_AUX>
 __device__ inline void load_page(PageRegs<kBf16, D>& r, const char* kbase, const char* vbase,
                                  uint32_t koff, uint32_t voff, int range) {
   using O = Ops<kBf16, D>;
@@ -298,15 +304,13 @@ __device__ inline void load_page(PageRegs<kBf16, D>& r, const char* kbase, const
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), 0, range, PKV_RSRC_WORD3);
 #pragma unroll
   for (int i = 0; i < O::NK; ++i)
-    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 1024 * i, 0, PKV_KV_LOAD_AUX);
+    r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 1024 * i, 0, kAux);
 #pragma unroll
   for (int nb = 0; nb < O::NV; ++nb) {
     if constexpr (kBf16)
-      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + O::ES * 16 * kBlock * nb, 0,
-                                                     PKV_KV_LOAD_AUX);
+      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b64(vr, voff + O::ES * 16 * kBlock * nb, 0, kAux);
     else
-      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + O::ES * 16 * kBlock * nb, 0,
-                                                      PKV_KV_LOAD_AUX);
+      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + O::ES * 16 * kBlock * nb, 0, kAux);
   }
 }
 
@@ -523,20 +527,38 @@ struct FlatCursor {
 template <bool kBf16, int D>
 constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
 
-// Split-KV decode for groups of at most 16 query heads per KV head: one chunk
-// of the flattened (sequence, KV head, page) order per wavefront, all query
-// heads of the group in the lanes' MFMA columns.  A loader cursor runs kDepth
-// pages ahead of the compute cursor through a ring of kDepth + 1 register
-// buffers, across pair boundaries, so the stream of tile loads never drains
-// inside a chunk; the compute cursor closes a segment (writes its output row
-// or partial) and opens the next one when the pair changes.
-template <bool kBf16, int D, int kDepth>
+// Sibling wavefronts of a large group read the same pages, so a CU has only
+// one wavefront's ring of distinct pages in flight: the grouped kernels run
+// a deeper ring at one wavefront per SIMD.
+#ifndef PKV_GROUPED_DEPTH
+#define PKV_GROUPED_DEPTH 2
+#endif
+#ifndef PKV_GROUPED_WAVES_PER_EU
+#define PKV_GROUPED_WAVES_PER_EU 2
+#endif
+template <bool kBf16, int D, int kNG>
+constexpr int kKernelWavesPerEu = kNG == 1 ? kSplitWavesPerEu<kBf16, D>
+                                           : ((kBf16 || D == 64) ? PKV_GROUPED_WAVES_PER_EU : 1);
+
+// Split-KV decode: one chunk of the flattened (sequence, KV head, page) order
+// per kNG wavefronts, each wavefront taking one 16-query-head block of the
+// group (kNG = 1 for groups of at most 16; 2 or 4 for larger groups, whose
+// sibling wavefronts read the same tiles, the first from HBM and the others
+// mostly from the caches).  A loader cursor runs kDepth pages ahead of the
+// compute cursor through a ring of kDepth + 1 register buffers, across pair
+// boundaries, so the stream of tile loads never drains inside a chunk; the
+// compute cursor closes a segment (writes its output rows or partial) and
+// opens the next one when the pair changes.  No barrier after the prefix:
+// wavefronts without work return early.
+template <bool kBf16, int D, int kDepth, int kNG>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu<kBf16, D>)))
+__attribute__((amdgpu_waves_per_eu(kKernelWavesPerEu<kBf16, D, kNG>)))
 split_kernel(DecodeArgs a) {
   using O = Ops<kBf16, D>;
   constexpr int kTile = kBlock * D * O::ES;
   constexpr int kBufs = kDepth + 1;
+  constexpr int kAux = kNG == 1 ? PKV_KV_LOAD_AUX : PKV_KV_LOAD_AUX_GROUPED;
+  static_assert(kWavesPerGroup % kNG == 0, "head blocks per chunk divide the workgroup");
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
   int32_t* s_wsum = smem + a.batch + 1;
@@ -544,8 +566,9 @@ split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uni(threadIdx.x / kWave);
-  const int chunk = blockIdx.x * kWavesPerGroup + wave;
-  if (chunk >= a.n_items) return;
+  const int chunk = blockIdx.x * (kWavesPerGroup / kNG) + wave / kNG;
+  const int gblk = wave % kNG;
+  if (chunk >= a.n_items || gblk * 16 >= a.group) return;
   const int total = uni(a.n_kv * s_prefix[a.batch]);
   const int C = chunk_pages(total, a.n_items, a.min_chunk);
   const int64_t f64 = static_cast<int64_t>(chunk) * C;
@@ -575,7 +598,7 @@ split_kernel(DecodeArgs a) {
     const int pg = bt_row(ld.b)[ld.j];
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
-    load_page(r, kp0 + off, vp0 + off, koff, voff, in && ok ? kTile : 0);
+    load_page<kBf16, D, kAux>(r, kp0 + off, vp0 + off, koff, voff, in && ok ? kTile : 0);
     pg_out = pg;
     if (in) {
       ++issued;
@@ -596,16 +619,17 @@ split_kernel(DecodeArgs a) {
     }
     if (!open) {
       const bool ends_pair = cp.j + (cnt - p) >= cp.n;
-      seg.begin(a, cp.b, cp.h, cp.n, ends_pair, 0, lane);
+      seg.begin(a, cp.b, cp.h, cp.n, ends_pair, gblk, lane);
       seg_start = a.n_kv * cp.pb + cp.h * cp.n;
       bad = false;
       open = true;
     }
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     bad |= !ok;
+    // Every head block patches its registers; the first stores the token.
     if (seg.append && cp.j == cp.n - 1) {
       seg.patch(r, lane);
-      if (ok) {
+      if (ok && gblk == 0) {
         const size_t head_off = static_cast<size_t>(cp.h) * kTile;
         seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
       }
@@ -615,6 +639,10 @@ split_kernel(DecodeArgs a) {
 
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s]);
+  // Whole turns of the ring, with the steps past the chunk's end skipped by
+  // uniform branches: an early exit from inside the unrolled turn makes the
+  // compiler's wait counters assume, at the loop head, that every buffer was
+  // just requested, and the ring would drain at every page.
   int p = 0;
   while (p < cnt) {
 #pragma unroll
@@ -624,162 +652,14 @@ split_kernel(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       issue(buf[(s + kDepth) % kBufs], page_of[(s + kDepth) % kBufs]);
       __builtin_amdgcn_sched_barrier(0);
-      compute(buf[s], page_of[s], p);
-      if (++p >= cnt) break;
-      cp.next(s_prefix, a.n_kv);
+      if (p < cnt) {
+        compute(buf[s], page_of[s], p);
+        if (p + 1 < cnt) cp.next(s_prefix, a.n_kv);
+      }
+      ++p;
     }
   }
   if (open) seg.finish(a, seg_start, chunk, C, bad, lane);
-}
-
-// LDS offset of the tile ring, after the length prefix (16-byte aligned).
-__host__ __device__ inline size_t shared_tiles_offset(int batch) {
-  return ((static_cast<size_t>(batch) + 1 + kWavesPerGroup) * sizeof(int32_t) + 15) & ~size_t{15};
-}
-
-// Split-KV decode for groups above 16 query heads per KV head (MQA): one
-// chunk per workgroup, whose four wavefronts take the 16-head blocks
-// 0..ceil(G/16)-1 of the group and share every K/V tile through LDS.  The
-// 256 threads load each page's two tiles cooperatively (16-byte pieces)
-// kStage pages ahead into a register ring, write the next page into a 3-slot
-// LDS ring, meet at one barrier per page, and each computing wavefront reads
-// its MFMA operands from LDS (same layout as in HBM).  A slot written at step
-// p was last read at step p - 2, before the barrier of step p - 1.
-#ifndef PKV_SHARED_WAVES_PER_EU
-#define PKV_SHARED_WAVES_PER_EU 2
-#endif
-template <bool kBf16, int D>
-constexpr int kSharedWavesPerEu = (kBf16 || D == 64) ? PKV_SHARED_WAVES_PER_EU : 1;
-
-template <bool kBf16, int D, int kStage>
-__global__ void __launch_bounds__(kWave * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(kSharedWavesPerEu<kBf16, D>)))
-split_kernel_shared(DecodeArgs a) {
-  using O = Ops<kBf16, D>;
-  constexpr int kTile = kBlock * D * O::ES;
-  constexpr int kThreads = kWave * kWavesPerGroup;
-  constexpr int kPieces = 2 * kTile / (kThreads * 16);
-  constexpr int kSlots = 3;
-  static_assert(kPieces >= 1 && 2 * kTile == kPieces * kThreads * 16, "tile split");
-  extern __shared__ int32_t smem[];
-  int32_t* s_prefix = smem;
-  int32_t* s_wsum = smem + a.batch + 1;
-  char* s_tiles = reinterpret_cast<char*>(smem) + shared_tiles_offset(a.batch);
-  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = uni(tid / kWave);
-  const int chunk = blockIdx.x;
-  if (chunk >= a.n_items) return;
-  const int total = uni(a.n_kv * s_prefix[a.batch]);
-  const int C = chunk_pages(total, a.n_items, a.min_chunk);
-  const int64_t f64 = static_cast<int64_t>(chunk) * C;
-  if (f64 >= total) return;
-  const int f0 = static_cast<int>(f64);
-  const int cnt = static_cast<int>(min(f64 + C, static_cast<int64_t>(total))) - f0;
-  const bool computes = wave * 16 < a.group;
-  const size_t page_stride = static_cast<size_t>(kTile) * a.n_kv;
-  char* kp0 = static_cast<char*>(a.k_pages);
-  char* vp0 = static_cast<char*>(a.v_pages);
-  auto bt_row = [&](int b) {
-    return (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
-  };
-
-  // ---- loader: pages of the chunk in order, kStage ahead of the compute.
-  FlatCursor ld;
-  ld.seek(s_prefix, a.batch, a.n_kv, f0);
-  int issued = 0;
-  u32x4 ring[kStage][kPieces];
-  auto issue = [&](u32x4 (&dst)[kPieces]) {
-    const bool in = issued < cnt;
-    int pg = bt_row(ld.b)[ld.j];
-    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-    const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
-    const int range = in && ok ? kTile : 0;
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(kp0 + off, 0, range, PKV_RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(vp0 + off, 0, range, PKV_RSRC_WORD3);
-#pragma unroll
-    for (int e = 0; e < kPieces; ++e) {
-      const uint32_t byte = 16u * (tid + kThreads * e);
-      if (byte < static_cast<uint32_t>(kTile))
-        dst[e] = __builtin_amdgcn_raw_buffer_load_b128(kr, byte, 0, PKV_KV_LOAD_AUX);
-      else
-        dst[e] = __builtin_amdgcn_raw_buffer_load_b128(vr, byte - kTile, 0, PKV_KV_LOAD_AUX);
-    }
-    if (in) {
-      ++issued;
-      if (issued < cnt) ld.next(s_prefix, a.n_kv);
-    }
-  };
-  auto to_lds = [&](const u32x4 (&src)[kPieces], int slot) {
-    char* base = s_tiles + static_cast<size_t>(slot) * 2 * kTile;
-#pragma unroll
-    for (int e = 0; e < kPieces; ++e)
-      *reinterpret_cast<u32x4*>(base + 16 * (tid + kThreads * e)) = src[e];
-  };
-
-  // ---- compute: one 16-head block per wavefront, segments as in split_kernel.
-  FlatCursor cp;
-  cp.seek(s_prefix, a.batch, a.n_kv, f0);
-  Segment<kBf16, D> seg;
-  bool open = false, bad = false;
-  int seg_start = 0;
-  const int c = lane >> 4, n = lane & 15;
-  const uint32_t voff = O::ES * (n * kBlock + 4 * c);
-  auto compute = [&](int slot, int p) {
-    if (open && (cp.b != seg.b || cp.h != seg.h)) {
-      seg.finish(a, seg_start, chunk, C, bad, lane);
-      open = false;
-    }
-    if (!open) {
-      const bool ends_pair = cp.j + (cnt - p) >= cp.n;
-      seg.begin(a, cp.b, cp.h, cp.n, ends_pair, wave, lane);
-      seg_start = a.n_kv * cp.pb + cp.h * cp.n;
-      bad = false;
-      open = true;
-    }
-    const int pg = bt_row(cp.b)[cp.j];
-    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-    bad |= !ok;
-    const char* base = s_tiles + static_cast<size_t>(slot) * 2 * kTile;
-    PageRegs<kBf16, D> r;
-#pragma unroll
-    for (int i = 0; i < O::NK; ++i) r.k[i] = *reinterpret_cast<const u32x4*>(base + 1024 * i + 16 * lane);
-#pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb)
-      r.v[nb] = *reinterpret_cast<const typename O::VReg*>(base + kTile + voff + O::ES * 16 * kBlock * nb);
-    if (seg.append && cp.j == cp.n - 1) {
-      seg.patch(r, lane);
-      if (wave == 0 && ok) {
-        const size_t head_off = static_cast<size_t>(cp.h) * kTile;
-        seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
-      }
-    }
-    seg.page(r, cp.j, a.scale_log2, lane);
-  };
-
-#pragma unroll
-  for (int s = 0; s < kStage; ++s) issue(ring[s]);
-  to_lds(ring[0], 0);
-  issue(ring[0]);
-  __syncthreads();
-  int p = 0;
-  // Step p: stage page p + 1 into LDS, request page p + 1 + kStage into the
-  // register slot it frees, barrier, compute page p.
-  while (p < cnt) {
-#pragma unroll
-    for (int s = 0; s < kStage; ++s) {
-      const int rs = (s + 1) % kStage;
-      if (p + 1 < cnt) to_lds(ring[rs], (p + 1) % kSlots);
-      issue(ring[rs]);
-      __syncthreads();
-      if (computes) compute(p % kSlots, p);
-      if (++p >= cnt) break;
-      cp.next(s_prefix, a.n_kv);
-    }
-  }
-  if (computes && open) seg.finish(a, seg_start, chunk, C, bad, lane);
 }
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
@@ -979,32 +859,10 @@ struct Resolved {
 
 using SplitFn = void (*)(DecodeArgs);
 
-// Register-ring depth of the shared-tile kernel (pages ahead per thread):
-// 16 bytes per piece, so kStage * pieces * 4 registers.
-#ifndef PKV_SHARED_STAGE
-#define PKV_SHARED_STAGE 8
-#endif
-template <bool kBf16, int D>
-constexpr int kSharedStage = (!kBf16 && D == 128) ? 4 : PKV_SHARED_STAGE;
-
-SplitFn shared_fn(int dtype, int head_dim) {
-  if (dtype == PKV_BF16)
-    return head_dim == 128 ? split_kernel_shared<true, 128, kSharedStage<true, 128>>
-                           : split_kernel_shared<true, 64, kSharedStage<true, 64>>;
-  return head_dim == 128 ? split_kernel_shared<false, 128, kSharedStage<false, 128>>
-                         : split_kernel_shared<false, 64, kSharedStage<false, 64>>;
-}
-
-// Groups above 16 query heads per KV head use the shared-tile kernel (one
-// chunk per workgroup); others the register-ring kernel (one chunk per
-// wavefront).
-inline bool use_shared(int group) { return waves_per_chunk(group) > 1; }
-
-size_t split_lds_bytes(int batch, int dtype, int head_dim, int group) {
-  const size_t prefix = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
-  if (!use_shared(group)) return prefix;
-  const size_t tile = static_cast<size_t>(kBlock) * head_dim * (dtype == PKV_BF16 ? 2 : 4);
-  return shared_tiles_offset(batch) + 3 * 2 * tile;
+// The split kernel's LDS: the per-sequence page prefix and the per-wave sums
+// used to build it.
+size_t split_lds_bytes(int batch) {
+  return static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
 }
 
 // bf16 tiles are 4 KiB per (page, head) at head_dim 128: two pages ahead fit
@@ -1012,14 +870,23 @@ size_t split_lds_bytes(int batch, int dtype, int head_dim, int group) {
 // as large, so fp32 keeps one page ahead.
 constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
 
-SplitFn split_fn(int dtype, int head_dim) {
+template <int kNG>
+SplitFn split_fn_ng(int dtype, int head_dim) {
+  constexpr int kDepth = kNG == 1 ? kPrefetchPages : PKV_GROUPED_DEPTH;
   if (dtype == PKV_BF16)
-    return head_dim == 128 ? split_kernel<true, 128, kPrefetchPages> : split_kernel<true, 64, kPrefetchPages>;
-  return head_dim == 128 ? split_kernel<false, 128, 1> : split_kernel<false, 64, 1>;
+    return head_dim == 128 ? split_kernel<true, 128, kDepth, kNG> : split_kernel<true, 64, kDepth, kNG>;
+  return head_dim == 128 ? split_kernel<false, 128, 1, kNG> : split_kernel<false, 64, 1, kNG>;
+}
+
+SplitFn split_fn(int dtype, int head_dim, int group) {
+  switch (waves_per_chunk(group)) {
+    case 1: return split_fn_ng<1>(dtype, head_dim);
+    case 2: return split_fn_ng<2>(dtype, head_dim);
+    default: return split_fn_ng<4>(dtype, head_dim);
+  }
 }
 
 int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
-  const bool shared = use_shared(group);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
@@ -1029,11 +896,11 @@ int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
       &per_cu,
-      reinterpret_cast<const void*>(shared ? shared_fn(dtype, head_dim) : split_fn(dtype, head_dim)),
+      reinterpret_cast<const void*>(split_fn(dtype, head_dim, group)),
       kWave * kWavesPerGroup, lds);
   if (e != hipSuccess) return hip_fail("hipOccupancyMaxActiveBlocksPerMultiprocessor", e);
   if (per_cu < 1) per_cu = 1;
-  *out = n_cu * per_cu * (shared ? 1 : kWavesPerGroup / waves_per_chunk(group));
+  *out = n_cu * per_cu * (kWavesPerGroup / waves_per_chunk(group));
   return ok();
 }
 
@@ -1061,7 +928,7 @@ int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, i
 int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, int32_t max_blocks,
                  int32_t n_kv, const pkv_decode_opts* opts, Resolved* r) {
   r->wpc = waves_per_chunk(group);
-  r->lds = split_lds_bytes(batch, dtype, head_dim, group);
+  r->lds = split_lds_bytes(batch);
   r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages
                                                      : default_min_chunk(group);
   if (opts && opts->n_items > 0) {
@@ -1139,10 +1006,9 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.scale_log2 = scale * kLog2e;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
-    const bool shared = use_shared(group);
-    const int chunks_per_group = shared ? 1 : kWavesPerGroup / r.wpc;
+    const int chunks_per_group = kWavesPerGroup / r.wpc;
     const int grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
-    hipLaunchKernelGGL(shared ? shared_fn(dtype, head_dim) : split_fn(dtype, head_dim), dim3(grid),
+    hipLaunchKernelGGL(split_fn(dtype, head_dim, group), dim3(grid),
                        dim3(kWave * kWavesPerGroup), r.lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
