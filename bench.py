@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--separate-combine", action="store_true",
+                    help="merge split partials with the combine kernel instead of inside the decode kernel")
     ap.add_argument("--unfused", action="store_true",
                     help="append, split and combine as three launches instead of the fused step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -202,7 +204,10 @@ def main():
     S = setup(w, device)
     dt = W.torch_dtype(w)
     dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, S["mb"], args.n_items, args.min_chunk,
-                      device=device)
+                      device=device, combine_mode=1 if args.separate_combine else 0)
+    # One kernel per layer when every pair can be merged inside the decode
+    # kernel (a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks).
+    one_kernel = not args.separate_combine and -(-S["mb"] // dec.min_chunk_pages) + 1 <= 64
     layers = S["layers"]
     n_layers = w.n_layers
     kv_step = S["kv_bytes_layer"] * n_layers
@@ -210,8 +215,11 @@ def main():
     rot = [0]
 
     def step(ev=None):
-        """One step; ev (optional) holds 3 events per layer: before the decode
-        kernel, after it, after the combine."""
+        """One step: per layer the library's full call (decode kernel, plus
+        the combine kernel where the library needs it).  With ev (3 events
+        per layer: before the decode kernel, after it, after the combine) the
+        two halves are called separately when the library launches two
+        kernels, so each can be timed; the kernels are the same."""
         for li in range(n_layers):
             L = layers[rot[0] % len(layers)]
             rot[0] += 1
@@ -219,16 +227,24 @@ def main():
                 pkv.kv_append(L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["positions"], stream)
             if ev is not None:
                 ev[3 * li].record(stream)
+            if ev is None or one_kernel:
+                if args.unfused:
+                    dec(L.q, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+                else:
+                    dec.step(L.q, L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale,
+                             L.out, stream)
+                if ev is not None:
+                    ev[3 * li + 1].record(stream)
+                    ev[3 * li + 2].record(stream)
+                continue
             if args.unfused:
                 dec.split(L.q, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale, L.out, stream)
             else:
                 dec.step_split(L.q, L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], w.scale,
                                L.out, stream)
-            if ev is not None:
-                ev[3 * li + 1].record(stream)
+            ev[3 * li + 1].record(stream)
             dec.combine(S["seq_lens"], L.out, S["mb"], stream)
-            if ev is not None:
-                ev[3 * li + 2].record(stream)
+            ev[3 * li + 2].record(stream)
 
     log(f"warmup {args.warmup} (n_items={dec.n_items}, copies={len(layers)})")
     for _ in range(args.warmup):
@@ -286,6 +302,7 @@ def main():
             "accumulate": "fp32", "n_items": dec.n_items, "min_chunk_pages": dec.min_chunk_pages,
             "pool_copies": len(layers),
             "append": "separate kernel" if args.unfused else "fused into the decode kernel",
+            "merge": "combine kernel" if not one_kernel else "inside the decode kernel",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.batch / (ms_per_step / 1e3), 1),
@@ -296,7 +313,7 @@ def main():
             "algorithmic_bytes_per_launch": S["kv_bytes_layer"],
         },
         "split_median_ms": round(float(np.median(split_ms)), 5),
-        "combine_avg_ms": round(float(np.mean(comb_ms)), 5),
+        "combine_avg_ms": None if one_kernel else round(float(np.mean(comb_ms)), 5),
         "hbm_read_probe_gbs": None if probe is None else round(probe, 1),
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),

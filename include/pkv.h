@@ -175,18 +175,31 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  * uses 4, the last idle).  A (sequence, KV head)
  * whose pages fall in one chunk gets its output written directly; otherwise
  * each chunk writes a partial (normalised output and natural-log sum of
- * exponentials) and the combine merges them.
+ * exponentials) and the partials are merged.  By default the chunk that
+ * finishes a pair last merges them in the same launch (arrival counted by
+ * one atomic per chunk; merge order is fixed, so results are run-to-run
+ * identical); pairs that may span more than 64 chunks (ceil(max_blocks_per_seq
+ * / min_chunk_pages) + 1 > 64) are merged by a second kernel, which is then
+ * launched on the same stream.
  *
  * workspace: device, 256-byte aligned, at least
  * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
- * bytes (n_items after defaults are applied).  Contents on entry are ignored.
+ * bytes (n_items after defaults are applied).  Its partials are overwritten
+ * by every call; its arrival counters (the last 16 * batch * n_kv_heads
+ * bytes) must be zero before the first pkv_paged_decode_attn or
+ * pkv_decode_step call that uses it (e.g. a zero-filled allocation), and
+ * every call leaves them zero.  Calls that overlap in time must not share a
+ * workspace.
  * opts (nullable): n_items <= 0 means as many chunks as the device holds at
  * once (resident wavefronts divided by the wavefronts per chunk);
- * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups).
+ * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups);
+ * combine_mode 0 merges in the decode kernel where the bound above allows,
+ * 1 always merges with the separate combine kernel (counters untouched).
  * ------------------------------------------------------------------------ */
 typedef struct pkv_decode_opts {
   int32_t n_items;
   int32_t min_chunk_pages;
+  int32_t combine_mode;
 } pkv_decode_opts;
 
 int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_pages,
@@ -226,9 +239,10 @@ int pkv_decode_step_split(const void* q, const void* k_new, const void* v_new, v
                           int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype,
                           void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
 
-/* The split half of pkv_paged_decode_attn alone (same arguments): writes the
- * rows of single-chunk (sequence, KV head) pairs into out and every other
- * chunk's partial into the workspace:
+/* The split half of pkv_paged_decode_attn alone (same arguments; never
+ * merges, never touches the counters): writes the rows of single-chunk
+ * (sequence, KV head) pairs into out and every other chunk's partial into
+ * the workspace:
  *   partial_o   float [slots][group][head_dim] at workspace offset 0
  *   partial_lse float [slots][group] right after partial_o
  * with slots = n_items + batch * n_kv_heads; chunk c's partial for pair

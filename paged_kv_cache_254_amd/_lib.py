@@ -27,7 +27,8 @@ class PkvError(RuntimeError):
 
 
 class DecodeOpts(ctypes.Structure):
-    _fields_ = [("n_items", ctypes.c_int32), ("min_chunk_pages", ctypes.c_int32)]
+    _fields_ = [("n_items", ctypes.c_int32), ("min_chunk_pages", ctypes.c_int32),
+                ("combine_mode", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):

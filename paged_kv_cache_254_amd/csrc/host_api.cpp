@@ -226,11 +226,9 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_k
   if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || head_dim < 1 || n_items < 1 ||
       n_q_heads % n_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_decode_workspace_bytes: bad argument");
-  int64_t group = n_q_heads / n_kv_heads;
-  int64_t slots = pkv::decode_slots(batch, n_kv_heads, n_items);
-  int64_t o_bytes = slots * group * head_dim * 4;
-  int64_t lse_bytes = slots * group * 4;
-  return o_bytes + lse_bytes;
+  const int64_t group = n_q_heads / n_kv_heads;
+  return pkv::decode_counters_offset(batch, group, n_kv_heads, head_dim, n_items) +
+         pkv::decode_counters_count(batch, n_kv_heads) * 4;
 }
 
 int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,

@@ -208,6 +208,10 @@ struct DecodeArgs {
   int32_t batch, n_q, n_kv, group, max_blocks, num_pages;
   int32_t n_items, min_chunk, waves_per_chunk;
   float scale_log2;
+  // Non-null: the chunk that finishes a pair of at most fuse_max_parts
+  // chunks last merges its partials (one counter per pair and head block).
+  int32_t* counters;
+  int32_t fuse_max_parts;
 };
 
 // Pages per sequence, exclusive prefix over the batch, into LDS (whole
@@ -275,6 +279,16 @@ struct PageRegs {
 #ifndef PKV_RSRC_WORD3
 #define PKV_RSRC_WORD3 0x00020000
 #endif
+// Cache-policy bits for device scope (SC1 set, SC0 clear): the access is
+// coherent across the XCDs, whose L2 caches are not coherent with each
+// other.  Used for the split partials that another workgroup merges in the
+// same launch.
+constexpr int kDeviceScope = 16;
+// s_waitcnt immediate (gfx9 layout) waiting for vmcnt = 0 only (expcnt and
+// lgkmcnt fields at their maxima): all of this wavefront's vector memory
+// operations, stores included, have completed.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Cache-policy bits of the K/V tile loads: non-temporal (each tile is read
 // once per launch, so it should not displace other lines; ~10% faster than
 // the default policy on the 16 x 4096 MHA layer).
@@ -358,6 +372,24 @@ __device__ inline void compute_page(PageRegs<kBf16, D>& r, int valid,
   O::pv(r.v, p, l, acc);
 }
 
+// Pairs whose partial this wavefront wrote and that it may have to merge:
+// only a chunk's first and last segments can belong to pairs that span
+// several chunks, so at most two.  Merged after the page loop, which keeps
+// the merge's registers out of it.
+struct PendingMerges {
+  int n = 0;
+  int b0 = 0, h0 = 0, first0 = 0, nparts0 = 0;
+  int b1 = 0, h1 = 0, first1 = 0, nparts1 = 0;
+  __device__ void add(int b, int h, int first, int nparts) {
+    if (n == 0) {
+      b0 = b; h0 = h; first0 = first; nparts0 = nparts;
+    } else {
+      b1 = b; h1 = h; first1 = first; nparts1 = nparts;
+    }
+    n = n < 2 ? n + 1 : 2;
+  }
+};
+
 // One segment: the pages of one (sequence b, KV head h) pair that one chunk
 // covers, for the 16 query heads gblk*16 .. gblk*16+15 (lane column n = head
 // gblk*16 + n).  Holds the query operand, the online-softmax state and, when
@@ -367,7 +399,7 @@ template <bool kBf16, int D>
 struct Segment {
   using O = Ops<kBf16, D>;
   static constexpr int kTileBytes = kBlock * D * O::ES;
-  int b, h, g, hq, len, n_pages, s_new;
+  int b, h, gb, g, hq, len, n_pages, s_new;
   bool g_ok, append;
   u32x4 qreg[O::NK];
   u32x4 knew[O::NK];
@@ -381,6 +413,7 @@ struct Segment {
     b = b_;
     h = h_;
     n_pages = n_pages_;
+    gb = gblk;
     g = gblk * 16 + n;
     g_ok = g < a.group;
     hq = h * a.group + g;
@@ -465,30 +498,163 @@ struct Segment {
   }
 
   // Normalises and writes the result: the output row when the pair lies in a
-  // single chunk, otherwise this chunk's partial (o, natural-log lse).
-  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad,
-                         int lane) const {
+  // single chunk, otherwise this chunk's partial (o, natural-log lse), which
+  // the last of the pair's chunks to finish then merges (if counters are on).
+  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
+                         PendingMerges& pending) const {
     const int c = lane >> 4;
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = bad ? NAN : 1.0f / lt;
     const int first_chunk = seg_start / C;
     const int last_chunk = (seg_start + n_pages - 1) / C;
-    if (!g_ok) return;
     if (first_chunk == last_chunk) {
+      if (!g_ok) return;
       const size_t row = (static_cast<size_t>(b) * a.n_q + hq) * D;
 #pragma unroll
       for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, acc[nb] * inv);
-    } else {
-      const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
-      float* po = a.part_o + (slot * a.group + g) * D;
-#pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb)
-        *reinterpret_cast<f32x4*>(po + 16 * nb + 4 * c) = acc[nb] * inv;
-      if (c == 0) a.part_lse[slot * a.group + g] = bad ? NAN : (m + __log2f(lt)) * kLn2;
+      return;
     }
+    // Device-scope stores: written through to the point where every XCD
+    // sees them, so the chunk that merges (possibly on another XCD) reads
+    // them without any cache-wide write-back or invalidation.  The row
+    // resource's range ends at the group's last head, which masks the lanes
+    // of heads past it.
+    const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
+    const int rows = min(16, a.group - gb * 16);
+    const size_t row0 = slot * a.group + gb * 16;
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, rows * D * 4, PKV_RSRC_WORD3);
+    const uint32_t n = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[nb] * inv), ro,
+                                             4 * (n * D + 16 * nb + 4 * c), 0, kDeviceScope);
+    if (c == 0) {
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc(a.part_lse + row0, 0, rows * 4, PKV_RSRC_WORD3);
+      const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), rl, 4 * n, 0, kDeviceScope);
+    }
+    const int nparts = last_chunk - first_chunk + 1;
+    if (a.counters != nullptr && nparts <= a.fuse_max_parts) pending.add(b, h, first_chunk, nparts);
   }
 };
+
+// Arrival of this wavefront's partials for (b, h, head block gb).  The
+// partials were written with device-scope stores; once they have completed
+// (vmcnt 0: every vector memory operation of this wavefront done), one lane
+// counts the arrival with a device-scope atomic.  The wavefront that brings
+// the count to nparts reads the nparts partials with device-scope loads,
+// merges them in chunk order (out = sum_i w_i o_i / sum_i w_i, w_i =
+// exp(lse_i - max lse), the combine kernel's formula) and resets the counter
+// for the next call.  No wavefront waits for another.
+__device__ inline int32_t* merge_counter(const DecodeArgs& a, int b, int h, int gb) {
+  return a.counters + (static_cast<size_t>(b) * a.n_kv + h) * kMaxWavesPerChunk + gb;
+}
+
+// Counts this wavefront's arrivals for its (at most two) pending pairs, both
+// atomics in flight together, after all its stores have completed; returns
+// a bit per pending pair for which it arrived last.
+__device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int gb, int lane) {
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  int o0 = 0, o1 = 0;
+  if (lane == 0) {
+    if (pm.n > 0)
+      o0 = __hip_atomic_fetch_add(merge_counter(a, pm.b0, pm.h0, gb), 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+    if (pm.n > 1)
+      o1 = __hip_atomic_fetch_add(merge_counter(a, pm.b1, pm.h1, gb), 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  }
+  o0 = __shfl(o0, 0);
+  o1 = __shfl(o1, 0);
+  return (pm.n > 0 && o0 == pm.nparts0 - 1 ? 1 : 0) | (pm.n > 1 && o1 == pm.nparts1 - 1 ? 2 : 0);
+}
+
+template <bool kBf16, int D>
+__device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_chunk, int nparts, int lane) {
+  using O = Ops<kBf16, D>;
+  int32_t* ctr = merge_counter(a, b, h, gb);
+  const uint32_t c = lane >> 4, n = lane & 15;
+  const int g = gb * 16 + static_cast<int>(n);
+  const bool g_ok = g < a.group;
+  const uint32_t G = a.group;
+  const size_t row0 = (static_cast<size_t>(first_chunk) + static_cast<size_t>(b) * a.n_kv + h) * G + gb * 16;
+  // One resource per array over the nparts slots' rows of this head block;
+  // part i is at scalar offset i * G rows.  Lanes past the group read
+  // neighbouring rows (or zeros past the range) and store nothing.
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, nparts * G * D * 4, PKV_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_lse + row0, 0, nparts * G * 4, PKV_RSRC_WORD3);
+  // One pass, kMergeGroup parts per round trip: all their loads are issued
+  // before any is used, and the running maximum rescales the sums (the same
+  // identity as the page loop).  Parts past nparts read zeros (outside the
+  // range) and weigh nothing.  32 f32x4 registers of loads per group.
+  constexpr int kMergeGroup = 32 / O::NV;
+  float mx = -INFINITY, den = 0.f;
+  f32x4 o[O::NV];
+#pragma unroll
+  for (int nb = 0; nb < O::NV; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nparts; i0 += kMergeGroup) {
+    float l[kMergeGroup];
+    f32x4 v[kMergeGroup][O::NV];
+#pragma unroll
+    for (int u = 0; u < kMergeGroup; ++u) {
+      const uint32_t i = i0 + u;
+      l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * n, 4 * G * i, kDeviceScope));
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb)
+        v[u][nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ro, 4 * (n * D + 16 * nb + 4 * c), 4 * G * D * i, kDeviceScope));
+    }
+    float gm = mx;
+#pragma unroll
+    for (int u = 0; u < kMergeGroup; ++u) gm = i0 + u < nparts ? fmaxf(gm, l[u]) : gm;
+    const float alpha = __expf(mx - gm);   // 0 on the first group (mx = -inf)
+    den *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) o[nb] *= alpha;
+#pragma unroll
+    for (int u = 0; u < kMergeGroup; ++u) {
+      const float w = i0 + u < nparts ? __expf(l[u] - gm) : 0.f;
+      den += w;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) o[nb] += w * v[u][nb];
+    }
+    mx = gm;
+  }
+  if (g_ok) {
+    const float inv = 1.0f / den;
+    const size_t row = (static_cast<size_t>(b) * a.n_q + h * a.group + g) * D;
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, o[nb] * inv);
+  }
+  if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Rows of sequences with no pages when the decode kernel merges its own
+// partials (no combine kernel runs for them): zeros for length 0, NaN for an
+// invalid length.  One wavefront; the empty sequences are found 64 at a time.
+__device__ void write_empty_rows(const DecodeArgs& a, const int32_t* s_prefix, int D, bool bf16, int lane) {
+  const size_t row_elems = static_cast<size_t>(a.n_q) * D;
+  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+    const int bl = b0 + lane;
+    const bool empty = bl < a.batch && s_prefix[bl + 1] == s_prefix[bl];
+    uint64_t mask = __builtin_amdgcn_ballot_w64(empty);
+    while (mask != 0) {
+      const int b = b0 + __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const float fill = a.seq_lens[b] == 0 ? 0.f : NAN;
+      const size_t base = static_cast<size_t>(b) * row_elems;
+      for (size_t e = lane; e < row_elems; e += kWave) {
+        if (bf16) static_cast<__bf16*>(a.out)[base + e] = static_cast<__bf16>(fill);
+        else static_cast<float*>(a.out)[base + e] = fill;
+      }
+    }
+  }
+}
 
 // Position in the flattened (sequence, KV head, page) order of all pages:
 // flat index f, sequence b (with pb = pages before b and n = pages of b),
@@ -566,6 +732,7 @@ split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uni(threadIdx.x / kWave);
+  if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, kBf16, lane);
   const int chunk = blockIdx.x * (kWavesPerGroup / kNG) + wave / kNG;
   const int gblk = wave % kNG;
   if (chunk >= a.n_items || gblk * 16 >= a.group) return;
@@ -610,11 +777,12 @@ split_kernel(DecodeArgs a) {
   FlatCursor cp;
   cp.seek(s_prefix, a.batch, a.n_kv, f0);
   Segment<kBf16, D> seg;
+  PendingMerges pending;
   bool open = false, bad = false;
   int seg_start = 0;
   auto compute = [&](PageRegs<kBf16, D>& r, int pg, int p) {
     if (open && (cp.b != seg.b || cp.h != seg.h)) {
-      seg.finish(a, seg_start, chunk, C, bad, lane);
+      seg.finish(a, seg_start, chunk, C, bad, lane, pending);
       open = false;
     }
     if (!open) {
@@ -659,7 +827,12 @@ split_kernel(DecodeArgs a) {
       ++p;
     }
   }
-  if (open) seg.finish(a, seg_start, chunk, C, bad, lane);
+  if (open) seg.finish(a, seg_start, chunk, C, bad, lane, pending);
+  if (pending.n > 0) {
+    const int last = arrive(a, pending, gblk, lane);
+    if (last & 1) merge_pair<kBf16, D>(a, pending.b0, pending.h0, gblk, pending.first0, pending.nparts0, lane);
+    if (last & 2) merge_pair<kBf16, D>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
+  }
 }
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
@@ -692,7 +865,11 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
     if (kBf16) static_cast<__bf16*>(a.out)[row0 + d] = static_cast<__bf16>(x);
     else static_cast<float*>(a.out)[row0 + d] = x;
   };
+  // With counters on, the decode kernel wrote the empty rows and merged the
+  // pairs of at most fuse_max_parts chunks.
+  const bool fused = a.counters != nullptr;
   if (n == 0) {
+    if (fused) return;
     const float fill = (a.seq_lens[b] == 0) ? 0.f : NAN;
     for (int d = tid; d < D; d += blockDim.x) store(d, fill);
     return;
@@ -705,6 +882,7 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   if (c0 == c1) return;
   const size_t slot0 = static_cast<size_t>(c0) + pair;
   const int nparts = c1 - c0 + 1;
+  if (fused && nparts <= a.fuse_max_parts) return;
   const float* lse = a.part_lse + slot0 * G + g;
   const float* po = a.part_o + (slot0 * G + g) * D;
   const size_t stride_o = static_cast<size_t>(G) * D;
@@ -853,6 +1031,7 @@ int hip_fail(const char* what, hipError_t e) {
 struct Resolved {
   int n_items;
   int min_chunk;
+  int combine_mode;
   int wpc;
   size_t lds;
 };
@@ -928,6 +1107,9 @@ int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, i
 int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, int32_t max_blocks,
                  int32_t n_kv, const pkv_decode_opts* opts, Resolved* r) {
   r->wpc = waves_per_chunk(group);
+  r->combine_mode = opts ? opts->combine_mode : 0;
+  if (r->combine_mode != 0 && r->combine_mode != 1)
+    return fail(PKV_ERR_INVALID_ARG, "decode: combine_mode must be 0 or 1");
   r->lds = split_lds_bytes(batch);
   r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages
                                                      : default_min_chunk(group);
@@ -1004,6 +1186,18 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.min_chunk = r.min_chunk;
   a.waves_per_chunk = r.wpc;
   a.scale_log2 = scale * kLog2e;
+  // Merge in the decode kernel when both halves run in this call; the
+  // combine kernel then runs only if some pair may span more than
+  // kFuseMaxParts chunks (C >= min_chunk, so a pair of at most
+  // max_blocks_per_seq pages spans at most ceil(max_blocks / min_chunk) + 1).
+  const bool fuse = do_split && do_combine && r.combine_mode == 0;
+  const int64_t max_parts = (static_cast<int64_t>(max_blocks_per_seq) + r.min_chunk - 1) / r.min_chunk + 1;
+  a.counters = fuse ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                 decode_counters_offset(batch, group, n_kv_heads, head_dim,
+                                                                        r.n_items))
+                    : nullptr;
+  a.fuse_max_parts = kFuseMaxParts;
+  const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
     const int chunks_per_group = kWavesPerGroup / r.wpc;
@@ -1013,7 +1207,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
   }
-  if (do_combine) {
+  if (run_combine) {
     auto fn_c = dtype == PKV_BF16 ? combine_kernel<true> : combine_kernel<false>;
     const size_t prefix_lds = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
     hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), prefix_lds, s, a, head_dim);
@@ -1143,6 +1337,7 @@ int pkv_decode_resolve(int32_t dtype, int32_t head_dim, int32_t n_q_heads, int32
   if (st != PKV_OK) return st;
   resolved->n_items = r.n_items;
   resolved->min_chunk_pages = r.min_chunk;
+  resolved->combine_mode = r.combine_mode;
   *workspace_bytes = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
   return *workspace_bytes < 0 ? static_cast<int>(*workspace_bytes) : ok();
 }

@@ -21,12 +21,11 @@ constexpr int kWavesPerGroup = 4;   // wavefronts per workgroup of the decode ke
 constexpr int kMaxBatch = 16000;    // keeps the per-workgroup length prefix in 64 KiB of LDS
 constexpr int kMaxGroup = 64;       // query heads per KV head
 // Default lower bound on pages per chunk.  Chunks are otherwise sized to
-// give one per resident wavefront (groups <= 16) or workgroup (larger
-// groups); on long sequences that makes them short, and each chunk pays a
-// start-up latency and one partial per query head.  Measured on MI355X: 64
-// pages for the one-wavefront-per-chunk kernel (131072-token GQA layer: 1024
-// chunks of 64 pages beat 2048 of 32 by 10%), 32 for the shared-tile kernel
-// (131072-token MQA: one chunk per CU is best).
+// give one per resident group of wavefronts; on long sequences that makes
+// them short, and each chunk pays a start-up latency and one partial per
+// query head.  Measured on MI355X: 64 pages for groups <= 16 (131072-token
+// GQA layer: 1024 chunks of 64 pages beat 2048 of 32 by 10%), 32 for larger
+// groups (131072-token MQA: one chunk per CU is best).
 __host__ __device__ inline int default_min_chunk(int group) { return group > 16 ? 32 : 64; }
 constexpr int kMaxItems = 1 << 22;  // work items per decode launch
 constexpr size_t kMaxLdsBytes = 64 * 1024;  // LDS one decode workgroup may use
@@ -49,6 +48,24 @@ __host__ __device__ inline int chunk_pages(int64_t total, int64_t n_items, int64
 
 __host__ __device__ inline int64_t decode_slots(int64_t batch, int64_t n_kv, int64_t n_items) {
   return n_items + batch * n_kv;
+}
+
+// Pairs whose pages span at most this many chunks are merged by the chunk
+// that finishes last, inside the decode kernel; longer ones by the combine
+// kernel (one wavefront would read all their partials).
+constexpr int kFuseMaxParts = 64;
+constexpr int kMaxWavesPerChunk = 4;
+
+// Workspace layout: partial outputs [slots][group][head_dim] f32, partial
+// lse [slots][group] f32, then (256-byte aligned) one arrival counter per
+// (sequence, KV head, head block), int32.
+__host__ __device__ inline int64_t decode_counters_offset(int64_t batch, int64_t group, int64_t n_kv,
+                                                          int64_t head_dim, int64_t n_items) {
+  const int64_t parts = decode_slots(batch, n_kv, n_items) * group * (head_dim + 1) * 4;
+  return (parts + 255) & ~int64_t{255};
+}
+__host__ __device__ inline int64_t decode_counters_count(int64_t batch, int64_t n_kv) {
+  return batch * n_kv * kMaxWavesPerChunk;
 }
 
 }  // namespace pkv

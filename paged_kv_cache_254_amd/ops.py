@@ -33,8 +33,8 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
-def _opts(n_items: int = 0, min_chunk_pages: int = 0):
-    return ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages)))
+def _opts(n_items: int = 0, min_chunk_pages: int = 0, combine_mode: int = 0):
+    return ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages), int(combine_mode)))
 
 
 # ----------------------------------------------------------------- host side
@@ -103,12 +103,12 @@ def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim
 
 
 def decode_resolve(dtype_code: int, head_dim: int, n_q_heads: int, n_kv_heads: int, batch: int,
-                   max_blocks: int, n_items: int = 0, min_chunk_pages: int = 0):
+                   max_blocks: int, n_items: int = 0, min_chunk_pages: int = 0, combine_mode: int = 0):
     """(n_items, min_chunk_pages, workspace_bytes) the device calls use for these shapes."""
     res = DecodeOpts()
     ws = ctypes.c_int64()
     check(lib.pkv_decode_resolve(dtype_code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks,
-                                 ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages))), ctypes.byref(res),
+                                 _opts(n_items, min_chunk_pages, combine_mode), ctypes.byref(res),
                                  ctypes.byref(ws)), "pkv_decode_resolve")
     return res.n_items, res.min_chunk_pages, ws.value
 
@@ -148,15 +148,18 @@ def copy_blocks(k_pages, v_pages, src_pages, dst_pages, stream=None) -> None:
 
 class Decoder:
     """Holds the resolved work split and a workspace for one decode shape
-    (batch, heads, head_dim, dtype and the block-table width max_blocks)."""
+    (batch, heads, head_dim, dtype and the block-table width max_blocks).
+    The workspace starts zero-filled, as the in-kernel merge's arrival
+    counters require; combine_mode 1 always merges with the combine kernel."""
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype, max_blocks: int,
-                 n_items: int = 0, min_chunk_pages: int = 0, device="cuda"):
+                 n_items: int = 0, min_chunk_pages: int = 0, device="cuda", combine_mode: int = 0):
         import torch
         code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
         self.n_items, self.min_chunk_pages, self.ws_bytes = decode_resolve(
-            code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks, n_items, min_chunk_pages)
-        self.workspace = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=device)
+            code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks, n_items, min_chunk_pages, combine_mode)
+        self.combine_mode = combine_mode
+        self.workspace = torch.zeros(max(256, self.ws_bytes), dtype=torch.uint8, device=device)
         self.shape = (batch, n_q_heads, n_kv_heads, head_dim)
         self.max_blocks = max_blocks
 
@@ -165,7 +168,7 @@ class Decoder:
         return (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hq,
                 k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B,
                 block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
-                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages))
+                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages, self.combine_mode))
 
     def __call__(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
         check(lib.pkv_paged_decode_attn(*self._args(q, k_pages, v_pages, block_table, seq_lens, scale, out,
@@ -177,7 +180,7 @@ class Decoder:
         return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                 _ptr(seq_lens), Hq, k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream),
                 B, block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
-                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages))
+                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages, self.combine_mode))
 
     def step(self, q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
         """Append each sequence's new token at seq_lens - 1 and attend, in one pass."""
@@ -198,7 +201,7 @@ class Decoder:
         B, Hq, Hkv, D = self.shape
         check(lib.pkv_lse_combine(_ptr(self.workspace), self.workspace.numel(), _ptr(seq_lens), B, Hq, Hkv, D,
                                   BLOCK_SIZE, max_blocks, _ptr(out), _dtype_code(out),
-                                  _opts(self.n_items, self.min_chunk_pages), _stream(stream)),
+                                  _opts(self.n_items, self.min_chunk_pages, self.combine_mode), _stream(stream)),
               "pkv_lse_combine")
 
     def partials(self):

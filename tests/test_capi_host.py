@@ -175,8 +175,15 @@ def test_plan_matches_flattened_chunking(lens, n_kv, n_items, min_chunk):
 
 
 def test_workspace_bytes():
-    assert pkv.decode_workspace_bytes(16, 32, 32, 128, 2048) == (2048 + 16 * 32) * 1 * 129 * 4
-    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4) == (4 + 4) * 2 * 65 * 4
+    # partials (slots x group x (head_dim + 1) floats), padded to 256 bytes,
+    # then 4 int32 arrival counters per (sequence, KV head)
+    def layout(batch, hq, hkv, d, n_items):
+        parts = (n_items + batch * hkv) * (hq // hkv) * (d + 1) * 4
+        return -(-parts // 256) * 256 + batch * hkv * 4 * 4
+    assert pkv.decode_workspace_bytes(16, 32, 32, 128, 2048) == (2048 + 16 * 32) * 1 * 129 * 4 + 16 * 32 * 16
+    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4) == 4352 + 64
+    for args in ((16, 32, 32, 128, 2048), (2, 4, 2, 64, 4), (3, 64, 1, 128, 7), (256, 32, 8, 128, 2048)):
+        assert pkv.decode_workspace_bytes(*args) == layout(*args)
     with pytest.raises(pkv.PkvError):
         pkv.decode_workspace_bytes(2, 5, 2, 64, 4)
 
@@ -189,7 +196,7 @@ def _decode(**kw):
              out=FAKE, stream=None, batch=2, mb=8, P=32, dtype=_lib.PKV_F32, ws=FAKE, wsb=1 << 30,
              n_items=4)
     a.update(kw)
-    opts = _lib.DecodeOpts(a["n_items"], 0)
+    opts = _lib.DecodeOpts(a["n_items"], 0, a.get("combine_mode", 0))
     return _lib.lib.pkv_paged_decode_attn(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["hq"], a["hkv"], a["d"],
                                           a["bs"], a["scale"], a["out"], a["stream"], a["batch"], a["mb"],
                                           a["P"], a["dtype"], a["ws"], a["wsb"], ctypes.byref(opts))
@@ -210,6 +217,7 @@ def _decode(**kw):
     (dict(sl=0), _lib.PKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.PKV_ERR_INVALID_ARG),
     (dict(wsb=100), _lib.PKV_ERR_WORKSPACE),
+    (dict(combine_mode=2), _lib.PKV_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
     assert _decode(**kw) == status
