@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step from a captured HIP graph (one graph per pool-rotation position)")
     ap.add_argument("--separate-combine", action="store_true",
                     help="merge split partials with the combine kernel instead of inside the decode kernel")
     ap.add_argument("--unfused", action="store_true",
@@ -220,6 +222,7 @@ def main():
         per layer: before the decode kernel, after it, after the combine) the
         two halves are called separately when the library launches two
         kernels, so each can be timed; the kernels are the same."""
+        stream = torch.cuda.current_stream()   # the capture stream while a graph is recorded
         for li in range(n_layers):
             L = layers[rot[0] % len(layers)]
             rot[0] += 1
@@ -251,11 +254,34 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    graphs = []
+    if args.graph:
+        # one captured step per rotation position, so replaying graph i % r
+        # walks the pool copies exactly as the eager loop does
+        positions = len(layers) // n_layers if len(layers) % n_layers == 0 else len(layers)
+        if positions > 64:
+            print(f"--graph: {positions} rotation positions is too many graphs for this workload",
+                  file=sys.stderr)
+            sys.exit(2)
+        rot[0] = 0
+        for _ in range(positions):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            graphs.append(g)
+        for g in graphs:     # replay once before timing
+            g.replay()
+        torch.cuda.synchronize()
+        log(f"captured {len(graphs)} graphs of {n_layers} layer(s)")
+
     # timed region: whole steps
     t_s, t_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_s.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step()
     t_e.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_s.elapsed_time(t_e) / args.steps
@@ -303,6 +329,7 @@ def main():
             "pool_copies": len(layers),
             "append": "separate kernel" if args.unfused else "fused into the decode kernel",
             "merge": "combine kernel" if not one_kernel else "inside the decode kernel",
+            "launch": "hip graph replay" if graphs else "eager",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.batch / (ms_per_step / 1e3), 1),
