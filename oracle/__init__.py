@@ -17,8 +17,13 @@ Modules:
 * ``page_pool``  - on-demand page allocation from a free list and the
                    per-request block table (pinned to its invariants and to
                    hand-worked tables).
+* ``kv_quant``   - 8-bit KV cache: per-(token, KV head) uniform quantization
+                   with a scale and a zero point, the quantizing append, and
+                   decode over the dequantized cache (pinned to hand-worked
+                   codes, exact grid round trips, the half-step bound, and the
+                   decode above run on explicitly dequantized pools).
 
 Parity status: every function here has at least one pin in
 ``tests/test_oracle_*.py``; none is "parity unpinned".
 """
-from . import attention, kv_bytes, page_pool  # noqa: F401
+from . import attention, kv_bytes, kv_quant, page_pool  # noqa: F401

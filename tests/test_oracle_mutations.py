@@ -133,3 +133,55 @@ def test_kv_formula_with_query_heads_is_caught():
     # Using n_q_heads (32 for Llama-3-8B) where n_kv_heads belongs gives 512 KiB, not the printed 128 KiB.
     case = [c for c in TB.GOLDEN["per_token"] if c["model"] == "Llama-3-8B"][0]
     assert KB.kv_bytes_per_token(case["n_layers"], 32, case["head_dim"], case["bytes_per_elem"]) != case["bytes"]
+
+
+# ------------------------------------------------------------ 8-bit KV cache
+from oracle import kv_quant as KQ  # noqa: E402
+
+from . import test_oracle_kv_quant as TQ  # noqa: E402
+
+
+def test_quant_zero_point_sign_is_caught(monkeypatch):
+    monkeypatch.setattr(KQ, "dequantize_vector",
+                        lambda u, s, z: np.float64(s) * (np.asarray(u, dtype=np.float64) + np.float64(z)))
+    assert _fails(TQ.test_hand_worked_vector_with_exact_scale)
+    assert _fails(TQ.test_grid_points_round_trip_exactly)
+
+
+def test_quant_floor_instead_of_rint_is_caught(monkeypatch):
+    orig_rint = np.rint
+
+    class _NP:
+        def __getattr__(self, name):
+            return np.floor if name == "rint" else getattr(np, name)
+    monkeypatch.setattr(KQ, "np", _NP())
+    assert _fails(TQ.test_hand_worked_vector_with_exact_scale)
+    assert orig_rint is np.rint
+
+
+def test_quant_meta_slot_off_by_one_is_caught(monkeypatch):
+    orig = KQ.dequantize_vector
+
+    def tiles_shifted(k_codes, v_codes, meta, page, head):
+        ku = k_codes[page, head].transpose(1, 0, 2).reshape(k_codes.shape[3], -1)
+        vu = v_codes[page, head].T
+        m = np.roll(meta[page, head], 1, axis=1)          # planted: scale of the previous slot
+        return orig(ku, m[0][:, None], m[1][:, None]), orig(vu, m[2][:, None], m[3][:, None])
+    monkeypatch.setattr(KQ, "dequantized_tiles", tiles_shifted)
+    assert any(_fails(TQ.test_decode_equals_decode_of_dequantized_pools, *c)
+               for c in [(8, 2, 64, [40, 5, 17]), (4, 4, 32, [33])])
+    assert _fails(TQ.test_decode_brute_force_tiny)
+
+
+def test_quant_key_chunk_order_is_caught(monkeypatch):
+    orig = KQ.dequantize_vector
+
+    def tiles_swapped(k_codes, v_codes, meta, page, head):
+        ku = k_codes[page, head].transpose(1, 2, 0).reshape(k_codes.shape[3], -1)   # planted: x-major
+        vu = v_codes[page, head].T
+        m = meta[page, head]
+        return orig(ku, m[0][:, None], m[1][:, None]), orig(vu, m[2][:, None], m[3][:, None])
+    monkeypatch.setattr(KQ, "dequantized_tiles", tiles_swapped)
+    # needs more than one 16-feature chunk: the D = 64 and D = 32 pins
+    assert any(_fails(TQ.test_decode_equals_decode_of_dequantized_pools, *c)
+               for c in [(8, 2, 64, [40, 5, 17]), (4, 4, 32, [33])])
