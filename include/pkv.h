@@ -72,7 +72,9 @@ enum {
   PKV_ERR_EXISTS = -7        /* sequence id already in use                   */
 };
 
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+/* Element types.  PKV_U8 names the 8-bit KV cache below (its q and out are
+ * bf16); the dense calls take PKV_F32 or PKV_BF16. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_U8 = 2 };
 
 /* Description of a status code (static string). */
 const char* pkv_status_string(int status);
@@ -289,6 +291,63 @@ int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
                     int32_t block_size, int32_t max_blocks_per_seq, int32_t n_items,
                     int32_t min_chunk_pages, int32_t* chunk_pages, int32_t* first_chunk,
                     int32_t* last_chunk);
+
+/* ------------------------------------------------------------------------ *
+ * 8-bit KV cache (device).  Cache quantization changes the bytes per cached
+ * element (evaltude docs "Transformer inference mechanics", section "What the
+ * KV cache stores per layer"); uniform integer quantization uses a scale and a
+ * zero point, with per-group scales (byteknotlabs "Efficient inference",
+ * section "Quantization: fewer bytes per weight").  Here each token's K vector
+ * and V vector of each KV head is one group, stored as uint8 codes u with
+ * x = s * (u - z):
+ *   lo = min(min(x), 0), hi = max(max(x), 0), s = (hi - lo) / 255 (1 when
+ *   hi == lo), z = rint(-lo / s), u = clamp(rint(x / s) + z, 0, 255),
+ * decided in float32 with IEEE division and round-half-to-even.
+ * Pools, per page and KV head (caller-owned device memory, 16-byte aligned):
+ *   k_codes uint8 [num_pages][n_kv_heads][head_dim / 16][16][16]
+ *           (token t, feature 16 c + x at [c][t][x])
+ *   v_codes uint8 [num_pages][n_kv_heads][head_dim][16]  (feature d, token t at [d][t])
+ *   meta    float [num_pages][n_kv_heads][4][16]  (k scale, k zero, v scale, v zero per slot)
+ * 2 * head_dim + 16 bytes per token and KV head (272 at head_dim 128, against
+ * 512 in bf16).  Unused slots may hold anything, NaN scales included.
+ *
+ * kv_append_q8: quantizes k_new / v_new ([batch][n_kv_heads][head_dim],
+ * dtype PKV_BF16 or PKV_F32) into slot positions[b] % 16 of page
+ * block_table[b][positions[b] / 16]; invalid positions or page ids skip the
+ * sequence, as pkv_kv_append.
+ * ------------------------------------------------------------------------ */
+int pkv_kv_append_q8(const void* k_new, const void* v_new, void* k_codes, void* v_codes, void* meta,
+                     const int32_t* block_table, const int32_t* positions, int32_t batch, int32_t n_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_pages,
+                     int32_t dtype, void* stream);
+
+/* Decode over the 8-bit cache: the attention of pkv_paged_decode_attn with
+ * K and V the dequantized cache, q and out bf16 [batch][n_q_heads][head_dim].
+ * Same semantics, work split, workspace (sized with pkv_decode_resolve and
+ * dtype PKV_U8) and options.  The codes enter fp16 matrix products exactly;
+ * scores and weights are fp32 with the per-token scales applied to them, so
+ * no element is dequantized one by one. */
+int pkv_paged_decode_attn_q8(const void* q, const void* k_codes, const void* v_codes, const void* meta,
+                             const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                             void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                             void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
+
+/* The split half alone (partials in the workspace as for pkv_paged_decode_split;
+ * merge with pkv_lse_combine, dtype PKV_BF16 or PKV_U8). */
+int pkv_paged_decode_split_q8(const void* q, const void* k_codes, const void* v_codes, const void* meta,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                              int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                              void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                              void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
+
+/* Decode step over the 8-bit cache: pkv_kv_append_q8 of k_new / v_new (bf16)
+ * at seq_lens - 1, then pkv_paged_decode_attn_q8 (two launches on stream). */
+int pkv_decode_step_q8(const void* q, const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                       void* meta, const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                       void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                       void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
 
 /* ------------------------------------------------------------------------ *
  * copy_blocks (device): copy-on-write of shared blocks (prefix sharing with

@@ -18,6 +18,7 @@ PKV_ERR_NOT_FOUND = -6
 PKV_ERR_EXISTS = -7
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_U8 = 2
 
 
 class PkvError(RuntimeError):
@@ -87,6 +88,17 @@ SIGNATURES = {
                                           ctypes.POINTER(DecodeOpts), ctypes.POINTER(ctypes.c_int64)]),
     "pkv_decode_plan": (ctypes.c_int, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_kv_append_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _vp]),
+    "pkv_paged_decode_attn_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                                _vp, _vp, _i32, _i32, _i32, _vp, _sz,
+                                                ctypes.POINTER(DecodeOpts)]),
+    "pkv_paged_decode_split_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                                 _vp, _vp, _i32, _i32, _i32, _vp, _sz,
+                                                 ctypes.POINTER(DecodeOpts)]),
+    "pkv_decode_step_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                          _f32, _vp, _vp, _i32, _i32, _i32, _vp, _sz,
+                                          ctypes.POINTER(DecodeOpts)]),
     "pkv_hbm_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "pkv_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
 }

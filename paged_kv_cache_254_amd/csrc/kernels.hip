@@ -200,6 +200,7 @@ struct DecodeArgs {
   void* v_pages;
   const void* k_new;       // non-null: fused append of each sequence's last token
   const void* v_new;
+  const void* meta;        // 8-bit cache only: per (page, KV head) scales and zero points
   const int32_t* block_table;
   const int32_t* seq_lens;
   void* out;
@@ -390,6 +391,48 @@ struct PendingMerges {
   }
 };
 
+// Writes one segment's normalised result o (lane (c, n): features
+// 16 nb + 4c .. +3 of head gb*16 + n) and its natural-log lse: the output rows
+// when the pair lies in a single chunk, otherwise this chunk's partial, which
+// the last of the pair's chunks to finish then merges (if counters are on).
+template <bool kOutBf16, int D>
+__device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pages, int seg_start, int chunk,
+                             int C, const f32x4 (&o)[D / 16], float lse, int lane, PendingMerges& pending) {
+  using O = Ops<kOutBf16, D>;
+  const int c = lane >> 4;
+  const uint32_t n = lane & 15;
+  const int g = gb * 16 + static_cast<int>(n);
+  const int first_chunk = seg_start / C;
+  const int last_chunk = (seg_start + n_pages - 1) / C;
+  if (first_chunk == last_chunk) {
+    if (g >= a.group) return;
+    const size_t row = (static_cast<size_t>(b) * a.n_q + h * a.group + g) * D;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, o[nb]);
+    return;
+  }
+  // Device-scope stores: written through to the point where every XCD sees
+  // them, so the chunk that merges (possibly on another XCD) reads them
+  // without any cache-wide write-back or invalidation.  The row resource's
+  // range ends at the group's last head, which masks the lanes of heads past it.
+  const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
+  const int rows = min(16, a.group - gb * 16);
+  const size_t row0 = slot * a.group + gb * 16;
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, rows * D * 4, PKV_RSRC_WORD3);
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb)
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[nb]), ro, 4 * (n * D + 16 * nb + 4 * c), 0,
+                                           kDeviceScope);
+  if (c == 0) {
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_lse + row0, 0, rows * 4, PKV_RSRC_WORD3);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), rl, 4 * n, 0, kDeviceScope);
+  }
+  const int nparts = last_chunk - first_chunk + 1;
+  if (a.counters != nullptr && nparts <= a.fuse_max_parts) pending.add(b, h, first_chunk, nparts);
+}
+
 // One segment: the pages of one (sequence b, KV head h) pair that one chunk
 // covers, for the 16 query heads gblk*16 .. gblk*16+15 (lane column n = head
 // gblk*16 + n).  Holds the query operand, the online-softmax state and, when
@@ -497,47 +540,17 @@ struct Segment {
                            lane >> 4, m, l, acc);
   }
 
-  // Normalises and writes the result: the output row when the pair lies in a
-  // single chunk, otherwise this chunk's partial (o, natural-log lse), which
-  // the last of the pair's chunks to finish then merges (if counters are on).
+  // Normalises the segment's result in place and writes it (see
+  // emit_segment); the segment is closed afterwards.
   __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
-                         PendingMerges& pending) const {
-    const int c = lane >> 4;
+                         PendingMerges& pending) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = bad ? NAN : 1.0f / lt;
-    const int first_chunk = seg_start / C;
-    const int last_chunk = (seg_start + n_pages - 1) / C;
-    if (first_chunk == last_chunk) {
-      if (!g_ok) return;
-      const size_t row = (static_cast<size_t>(b) * a.n_q + hq) * D;
 #pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, acc[nb] * inv);
-      return;
-    }
-    // Device-scope stores: written through to the point where every XCD
-    // sees them, so the chunk that merges (possibly on another XCD) reads
-    // them without any cache-wide write-back or invalidation.  The row
-    // resource's range ends at the group's last head, which masks the lanes
-    // of heads past it.
-    const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
-    const int rows = min(16, a.group - gb * 16);
-    const size_t row0 = slot * a.group + gb * 16;
-    const __amdgpu_buffer_rsrc_t ro =
-        __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, rows * D * 4, PKV_RSRC_WORD3);
-    const uint32_t n = lane & 15;
-#pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[nb] * inv), ro,
-                                             4 * (n * D + 16 * nb + 4 * c), 0, kDeviceScope);
-    if (c == 0) {
-      const __amdgpu_buffer_rsrc_t rl =
-          __builtin_amdgcn_make_buffer_rsrc(a.part_lse + row0, 0, rows * 4, PKV_RSRC_WORD3);
-      const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse), rl, 4 * n, 0, kDeviceScope);
-    }
-    const int nparts = last_chunk - first_chunk + 1;
-    if (a.counters != nullptr && nparts <= a.fuse_max_parts) pending.add(b, h, first_chunk, nparts);
+    for (int nb = 0; nb < O::NV; ++nb) acc[nb] *= inv;
+    const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
+    emit_segment<kBf16, D>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
   }
 };
 
@@ -656,6 +669,162 @@ __device__ void write_empty_rows(const DecodeArgs& a, const int32_t* s_prefix, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit KV cache: uint8 codes u with a scale s and a zero point z per (token,
+// KV head), x = s (u - z).  Tile layouts per (page, KV head):
+//   K codes [D/16][16 tokens][16]    (lane l of load j reads bytes 1024 j + 16 l)
+//   V codes [D][16 tokens]
+//   meta    float [4][16 tokens]     (k scale, k zero, v scale, v zero)
+// The codes enter fp16 MFMAs as 1024 + u: one byte permute builds two such
+// fp16 values (0x64 is the high byte of 1024, whose unit in the last place is
+// 1), and the 1024 is folded into the zero point.  Scores are
+//   s_t (sum_f (1024 + u_tf) q_f - (1024 + z_t) sum_f q_f),
+// and the value sum is sum_t w_t (1024 + u_t) - sum_t w_t (1024 + z_t) with
+// w_t = p_t s_t, so no element is dequantized one by one.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+constexpr float kCodeBias = 1024.0f;
+
+// Codes 2e and 2e + 1 of the word as the fp16 pair (1024 + u, 1024 + u').
+template <int E>
+__device__ inline uint32_t code_pair_f16(uint32_t w) {
+  return __builtin_amdgcn_perm(0x64646464u, w, E == 0 ? 0x04010400u : 0x04030402u);
+}
+
+template <int D>
+struct PageRegsQ8 {
+  static constexpr int NK = D / 64;   // 16-byte K loads per lane
+  static constexpr int NV = D / 16;   // 4-byte V loads per lane (4 tokens of one feature)
+  u32x4 k[NK];
+  uint32_t v[NV];
+  f32x4 ks, kz, vs, vz;               // tokens 4c .. 4c+3
+};
+
+// One segment of the 8-bit cache (same role and lane layout as Segment).
+template <int D>
+struct SegmentQ8 {
+  static constexpr int NQ = D / 32;   // fp16 query registers, one per 32-feature MFMA
+  static constexpr int NV = D / 16;
+  int b, h, gb, g, hq, len, n_pages;
+  bool g_ok, append;
+  u32x4 qh[NQ];
+  float qsum, m, l, corr;
+  f32x4 acc[NV];
+
+  // Query operand: MFMA 2j + e takes, in lane (c, n), features
+  // 16 (4j + c) + 8e .. +7 of head n: the features the K codes of load j
+  // bring to lanes of group c.  qsum = sum of the fp16 query features of the
+  // lane's head (the same fp16 values the MFMAs multiply).
+  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, bool, int gblk, int lane) {
+    const int c = lane >> 4, n = lane & 15;
+    b = b_;
+    h = h_;
+    n_pages = n_pages_;
+    gb = gblk;
+    g = gblk * 16 + n;
+    g_ok = g < a.group;
+    hq = h * a.group + g;
+    len = a.seq_lens[b];
+    append = false;
+    const char* qb = static_cast<const char*>(a.q) + (static_cast<size_t>(b) * a.n_q + (g_ok ? hq : 0)) * D * 2;
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int j = i / 2, e = i % 2;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(qb + 128 * j + 32 * c + 16 * e);
+      f16x8 hv;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float lo = __builtin_bit_cast(float, t[w] << 16);
+        const float hi = __builtin_bit_cast(float, t[w] & 0xffff0000u);
+        hv[2 * w] = static_cast<_Float16>(lo);
+        hv[2 * w + 1] = static_cast<_Float16>(hi);
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) part += static_cast<float>(hv[w]);
+      qh[i] = g_ok ? __builtin_bit_cast(u32x4, hv) : u32x4{0u, 0u, 0u, 0u};
+    }
+    part = g_ok ? part : 0.f;
+    qsum = part + __shfl_xor(part, 16);
+    qsum += __shfl_xor(qsum, 32);
+    m = -INFINITY;
+    l = 0.f;
+    corr = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  __device__ void page(PageRegsQ8<D>& r, int j, float scale_log2, int lane) {
+    const int c = lane >> 4;
+    const int valid = j == n_pages - 1 ? len - kBlock * j : kBlock;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PageRegsQ8<D>::NK; ++i) {
+      const u32x4 kk = r.k[i];
+      const u32x4 a0 = {code_pair_f16<0>(kk.x), code_pair_f16<1>(kk.x), code_pair_f16<0>(kk.y),
+                        code_pair_f16<1>(kk.y)};
+      const u32x4 a1 = {code_pair_f16<0>(kk.z), code_pair_f16<1>(kk.z), code_pair_f16<0>(kk.w),
+                        code_pair_f16<1>(kk.w)};
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
+                                                 __builtin_bit_cast(f16x8, qh[2 * i]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
+                                                 __builtin_bit_cast(f16x8, qh[2 * i + 1]), s1, 0, 0, 0);
+    }
+    const f32x4 raw = s0 + s1;   // lane (c, n): tokens 4c + i, head n
+    float x[4];
+    bool in[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      in[i] = 4 * c + i < valid;
+      const float sc = r.ks[i] * (raw[i] - (kCodeBias + r.kz[i]) * qsum) * scale_log2;
+      x[i] = in[i] ? sc : -INFINITY;
+    }
+    const float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__builtin_amdgcn_ballot_w64(pm > m + kLazyRescale) != 0) {
+      float cm = fmaxf(pm, __shfl_xor(pm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float mn = fmaxf(m, cm);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+      corr *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb) acc[nb] *= alpha;
+      m = mn;
+    }
+    // Weights w = p s in fp16 (round to nearest); slots past the length weigh
+    // nothing, whatever their codes and scales hold.
+    f16x4 wh;
+    float wz = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(x[i] - m);
+      l += p;
+      wh[i] = static_cast<_Float16>(in[i] ? p * r.vs[i] : 0.f);
+      wz += in[i] ? static_cast<float>(wh[i]) * (kCodeBias + r.vz[i]) : 0.f;
+    }
+    corr += wz;
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb) {
+      const u32x2 va = {code_pair_f16<0>(r.v[nb]), code_pair_f16<1>(r.v[nb])};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va), wh, acc[nb], 0, 0, 0);
+    }
+  }
+
+  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
+                         PendingMerges& pending) {
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    float ct = corr + __shfl_xor(corr, 16);
+    ct += __shfl_xor(ct, 32);
+    const float inv = bad ? NAN : 1.0f / lt;
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb) acc[nb] = (acc[nb] - ct) * inv;
+    const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
+    emit_segment<true, D>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
+  }
+};
+
 // Position in the flattened (sequence, KV head, page) order of all pages:
 // flat index f, sequence b (with pb = pages before b and n = pages of b),
 // KV head h, page j of the pair.
@@ -702,9 +871,62 @@ constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
 #ifndef PKV_GROUPED_WAVES_PER_EU
 #define PKV_GROUPED_WAVES_PER_EU 2
 #endif
-template <bool kBf16, int D, int kNG>
-constexpr int kKernelWavesPerEu = kNG == 1 ? kSplitWavesPerEu<kBf16, D>
-                                           : ((kBf16 || D == 64) ? PKV_GROUPED_WAVES_PER_EU : 1);
+// Cache policies of the split kernel: what one (page, KV head) holds, how a
+// wavefront loads it, and the segment type that consumes it.
+template <bool kBf16, int D>
+struct DenseKV {                       // bf16 or fp32 K/V, the q and out dtype
+  static constexpr int kHeadDim = D;
+  static constexpr bool kOutBf16 = kBf16;
+  static constexpr bool kFusedAppend = true;
+  static constexpr int kTileK = kBlock * D * Ops<kBf16, D>::ES;
+  static constexpr int kWavesPerEu = kSplitWavesPerEu<kBf16, D>;
+  static constexpr int kWavesPerEuGrouped = (kBf16 || D == 64) ? PKV_GROUPED_WAVES_PER_EU : 1;
+  using Regs = PageRegs<kBf16, D>;
+  using Seg = Segment<kBf16, D>;
+  template <int kAux>
+  __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
+    const int c = lane >> 4, n = lane & 15;
+    const size_t off = tile * kTileK;
+    load_page<kBf16, D, kAux>(r, static_cast<const char*>(a.k_pages) + off, static_cast<const char*>(a.v_pages) + off,
+                              16u * lane, Ops<kBf16, D>::ES * (n * kBlock + 4 * c), on ? kTileK : 0);
+  }
+};
+
+template <int D>
+struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
+  static constexpr int kHeadDim = D;
+  static constexpr bool kOutBf16 = true;
+  static constexpr bool kFusedAppend = false;
+  static constexpr int kTileK = kBlock * D;        // bytes of one K (or V) code tile
+  static constexpr int kMetaBytes = 4 * kBlock * 4;
+  static constexpr int kWavesPerEu = 2;
+  static constexpr int kWavesPerEuGrouped = PKV_GROUPED_WAVES_PER_EU;
+  using Regs = PageRegsQ8<D>;
+  using Seg = SegmentQ8<D>;
+  template <int kAux>
+  __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
+    const int c = lane >> 4, n = lane & 15;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(a.k_pages) + tile * kTileK, 0, on ? kTileK : 0, PKV_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(a.v_pages) + tile * kTileK, 0, on ? kTileK : 0, PKV_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(a.meta)) + tile * kMetaBytes, 0, on ? kMetaBytes : 0,
+        PKV_RSRC_WORD3);
+#pragma unroll
+    for (int j = 0; j < Regs::NK; ++j) r.k[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, 1024 * j + 16 * lane, 0, kAux);
+#pragma unroll
+    for (int nb = 0; nb < Regs::NV; ++nb)
+      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b32(vr, 16 * (16 * nb + n) + 4 * c, 0, kAux);
+    r.ks = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 16 * c, 0, kAux));
+    r.kz = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 64 + 16 * c, 0, kAux));
+    r.vs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 128 + 16 * c, 0, kAux));
+    r.vz = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 192 + 16 * c, 0, kAux));
+  }
+};
+
+template <class KV, int kNG>
+constexpr int kKernelWavesPerEu = kNG == 1 ? KV::kWavesPerEu : KV::kWavesPerEuGrouped;
 
 // Split-KV decode: one chunk of the flattened (sequence, KV head, page) order
 // per kNG wavefronts, each wavefront taking one 16-query-head block of the
@@ -716,13 +938,14 @@ constexpr int kKernelWavesPerEu = kNG == 1 ? kSplitWavesPerEu<kBf16, D>
 // compute cursor closes a segment (writes its output rows or partial) and
 // opens the next one when the pair changes.  No barrier after the prefix:
 // wavefronts without work return early.
-template <bool kBf16, int D, int kDepth, int kNG>
+template <class KV, int kDepth, int kNG>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(kKernelWavesPerEu<kBf16, D, kNG>)))
+__attribute__((amdgpu_waves_per_eu(kKernelWavesPerEu<KV, kNG>)))
 split_kernel(DecodeArgs a) {
-  using O = Ops<kBf16, D>;
-  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int D = KV::kHeadDim;
+  constexpr int kTile = KV::kTileK;
   constexpr int kBufs = kDepth + 1;
+  using Regs = typename KV::Regs;
   constexpr int kAux = kNG == 1 ? PKV_KV_LOAD_AUX : PKV_KV_LOAD_AUX_GROUPED;
   static_assert(kWavesPerGroup % kNG == 0, "head blocks per chunk divide the workgroup");
   extern __shared__ int32_t smem[];
@@ -732,7 +955,7 @@ split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uni(threadIdx.x / kWave);
-  if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, kBf16, lane);
+  if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, KV::kOutBf16, lane);
   const int chunk = blockIdx.x * (kWavesPerGroup / kNG) + wave / kNG;
   const int gblk = wave % kNG;
   if (chunk >= a.n_items || gblk * 16 >= a.group) return;
@@ -745,9 +968,6 @@ split_kernel(DecodeArgs a) {
   const size_t page_stride = static_cast<size_t>(kTile) * a.n_kv;
   char* kp0 = static_cast<char*>(a.k_pages);
   char* vp0 = static_cast<char*>(a.v_pages);
-  const int c = lane >> 4, n = lane & 15;
-  const uint32_t koff = 16u * lane;
-  const uint32_t voff = O::ES * (n * kBlock + 4 * c);
   auto bt_row = [&](int b) {
     return (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
   };
@@ -758,14 +978,13 @@ split_kernel(DecodeArgs a) {
   FlatCursor ld;
   ld.seek(s_prefix, a.batch, a.n_kv, f0);
   int issued = 0;
-  PageRegs<kBf16, D> buf[kBufs];
+  Regs buf[kBufs];
   int page_of[kBufs];   // page id of each buffer (scalar), for the compute side
-  auto issue = [&](PageRegs<kBf16, D>& r, int& pg_out) {
+  auto issue = [&](Regs& r, int& pg_out) {
     const bool in = issued < cnt;
     const int pg = bt_row(ld.b)[ld.j];
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-    const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
-    load_page<kBf16, D, kAux>(r, kp0 + off, vp0 + off, koff, voff, in && ok ? kTile : 0);
+    KV::template load<kAux>(r, a, static_cast<size_t>(ok ? pg : 0) * a.n_kv + ld.h, in && ok, lane);
     pg_out = pg;
     if (in) {
       ++issued;
@@ -776,11 +995,11 @@ split_kernel(DecodeArgs a) {
   // ---- compute.
   FlatCursor cp;
   cp.seek(s_prefix, a.batch, a.n_kv, f0);
-  Segment<kBf16, D> seg;
+  typename KV::Seg seg;
   PendingMerges pending;
   bool open = false, bad = false;
   int seg_start = 0;
-  auto compute = [&](PageRegs<kBf16, D>& r, int pg, int p) {
+  auto compute = [&](Regs& r, int pg, int p) {
     if (open && (cp.b != seg.b || cp.h != seg.h)) {
       seg.finish(a, seg_start, chunk, C, bad, lane, pending);
       open = false;
@@ -795,11 +1014,13 @@ split_kernel(DecodeArgs a) {
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     bad |= !ok;
     // Every head block patches its registers; the first stores the token.
-    if (seg.append && cp.j == cp.n - 1) {
-      seg.patch(r, lane);
-      if (ok && gblk == 0) {
-        const size_t head_off = static_cast<size_t>(cp.h) * kTile;
-        seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+    if constexpr (KV::kFusedAppend) {
+      if (seg.append && cp.j == cp.n - 1) {
+        seg.patch(r, lane);
+        if (ok && gblk == 0) {
+          const size_t head_off = static_cast<size_t>(cp.h) * kTile;
+          seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+        }
       }
     }
     seg.page(r, cp.j, a.scale_log2, lane);
@@ -830,8 +1051,10 @@ split_kernel(DecodeArgs a) {
   if (open) seg.finish(a, seg_start, chunk, C, bad, lane, pending);
   if (pending.n > 0) {
     const int last = arrive(a, pending, gblk, lane);
-    if (last & 1) merge_pair<kBf16, D>(a, pending.b0, pending.h0, gblk, pending.first0, pending.nparts0, lane);
-    if (last & 2) merge_pair<kBf16, D>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
+    if (last & 1)
+      merge_pair<KV::kOutBf16, D>(a, pending.b0, pending.h0, gblk, pending.first0, pending.nparts0, lane);
+    if (last & 2)
+      merge_pair<KV::kOutBf16, D>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
   }
 }
 
@@ -981,6 +1204,73 @@ append_kernel(const void* k_new, const void* v_new, void* k_pages, void* v_pages
 // tile of page src[i] to page dst[i] (copy-on-write of a shared block), 16
 // bytes per lane per instruction.  Pairs with an id outside the pool, or
 // src == dst, are skipped.
+// Quantizing append (8-bit cache): one wavefront per (sequence, KV head)
+// quantizes the new token's K and V vectors (each with its own scale and
+// zero point) and writes the codes into slot pos % 16 of page
+// block_table[b][pos / 16], and the scales and zero points into that slot's
+// meta.  pos = positions[b] - from_lens (from_lens = 1 when given lengths).
+// The quantizer is decided in float32 exactly as the oracle's: the range
+// includes 0, s = (hi - lo) / 255 (1 if hi == lo), z = rint(-lo / s),
+// u = clamp(rint(x / s) + z, 0, 255), with IEEE division and
+// round-half-to-even.
+template <bool kInBf16>
+__global__ void __launch_bounds__(256)
+append_q8_kernel(const void* k_new, const void* v_new, uint8_t* k_codes, uint8_t* v_codes, float* meta,
+                 const int32_t* block_table, const int32_t* positions, int from_lens, int batch, int n_kv,
+                 int D, int max_blocks, int num_pages) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
+  if (item >= batch * n_kv) return;
+  const int b = item / n_kv;
+  const int h = item - b * n_kv;
+  const int pos = positions[b] - from_lens;
+  if (pos < 0 || pos >= max_blocks * kBlock) return;
+  const int pg = block_table[static_cast<size_t>(b) * max_blocks + pos / kBlock];
+  if (pg < 0 || pg >= num_pages) return;
+  const int slot = pos % kBlock;
+  const size_t row = (static_cast<size_t>(b) * n_kv + h) * D;
+  const size_t tile = static_cast<size_t>(pg) * n_kv + h;
+  auto read = [&](const void* src, int d) -> float {
+    if (kInBf16) {
+      const uint32_t bits = static_cast<const uint16_t*>(src)[row + d];
+      return __builtin_bit_cast(float, bits << 16);
+    }
+    return static_cast<const float*>(src)[row + d];
+  };
+  const bool two = D > kWave;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which == 0 ? k_new : v_new;
+    const float x0 = read(src, lane);
+    const float x1 = two ? read(src, lane + kWave) : 0.f;
+    float lo = fminf(fminf(x0, x1), 0.f);
+    float hi = fmaxf(fmaxf(x0, x1), 0.f);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off));
+      hi = fmaxf(hi, __shfl_xor(hi, off));
+    }
+    float sc = (hi - lo) / 255.0f;
+    if (sc == 0.f) sc = 1.0f;
+    const float z = __builtin_rintf(-lo / sc);
+    auto code = [&](float x) {
+      return static_cast<uint8_t>(fminf(fmaxf(__builtin_rintf(x / sc) + z, 0.f), 255.f));
+    };
+    for (int e = 0; e < (two ? 2 : 1); ++e) {
+      const int d = lane + e * kWave;
+      const uint8_t u = code(e == 0 ? x0 : x1);
+      if (which == 0)
+        k_codes[tile * kBlock * D + static_cast<size_t>(d / 16) * 256 + slot * 16 + d % 16] = u;
+      else
+        v_codes[tile * kBlock * D + static_cast<size_t>(d) * kBlock + slot] = u;
+    }
+    if (lane == 0) {
+      meta[tile * 64 + (2 * which) * kBlock + slot] = sc;
+      meta[tile * 64 + (2 * which + 1) * kBlock + slot] = z;
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256)
 copy_blocks_kernel(char* k_pages, char* v_pages, const int32_t* src, const int32_t* dst,
                    int n_pairs, int n_kv, int tile_bytes, int num_pages) {
@@ -1049,19 +1339,29 @@ size_t split_lds_bytes(int batch) {
 // as large, so fp32 keeps one page ahead.
 constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
 
+// 8-bit pages are half the bytes of bf16 ones: one more page ahead keeps
+// about as many bytes in flight.
+#ifndef PKV_Q8_PREFETCH_PAGES
+#define PKV_Q8_PREFETCH_PAGES 3
+#endif
+
 template <int kNG>
-SplitFn split_fn_ng(int dtype, int head_dim) {
+SplitFn split_fn_ng(int dtype, int head_dim, bool q8) {
   constexpr int kDepth = kNG == 1 ? kPrefetchPages : PKV_GROUPED_DEPTH;
+  if (q8)
+    return head_dim == 128 ? split_kernel<Q8KV<128>, PKV_Q8_PREFETCH_PAGES, kNG>
+                           : split_kernel<Q8KV<64>, PKV_Q8_PREFETCH_PAGES, kNG>;
   if (dtype == PKV_BF16)
-    return head_dim == 128 ? split_kernel<true, 128, kDepth, kNG> : split_kernel<true, 64, kDepth, kNG>;
-  return head_dim == 128 ? split_kernel<false, 128, 1, kNG> : split_kernel<false, 64, 1, kNG>;
+    return head_dim == 128 ? split_kernel<DenseKV<true, 128>, kDepth, kNG>
+                           : split_kernel<DenseKV<true, 64>, kDepth, kNG>;
+  return head_dim == 128 ? split_kernel<DenseKV<false, 128>, 1, kNG> : split_kernel<DenseKV<false, 64>, 1, kNG>;
 }
 
-SplitFn split_fn(int dtype, int head_dim, int group) {
+SplitFn split_fn(int dtype, int head_dim, int group, bool q8) {
   switch (waves_per_chunk(group)) {
-    case 1: return split_fn_ng<1>(dtype, head_dim);
-    case 2: return split_fn_ng<2>(dtype, head_dim);
-    default: return split_fn_ng<4>(dtype, head_dim);
+    case 1: return split_fn_ng<1>(dtype, head_dim, q8);
+    case 2: return split_fn_ng<2>(dtype, head_dim, q8);
+    default: return split_fn_ng<4>(dtype, head_dim, q8);
   }
 }
 
@@ -1075,7 +1375,7 @@ int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
       &per_cu,
-      reinterpret_cast<const void*>(split_fn(dtype, head_dim, group)),
+      reinterpret_cast<const void*>(split_fn(dtype, head_dim, group, dtype == PKV_U8)),
       kWave * kWavesPerGroup, lds);
   if (e != hipSuccess) return hip_fail("hipOccupancyMaxActiveBlocksPerMultiprocessor", e);
   if (per_cu < 1) per_cu = 1;
@@ -1087,7 +1387,7 @@ int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, i
                         int32_t block_size, int32_t batch, int32_t max_blocks_per_seq,
                         int32_t num_pages, int32_t dtype) {
   std::string f(fn);
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, f + ": dtype");
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_U8) return fail(PKV_ERR_UNSUPPORTED, f + ": dtype");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
   if (block_size != kBlock) return fail(PKV_ERR_UNSUPPORTED, f + ": block_size must be 16");
@@ -1131,7 +1431,7 @@ int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, 
 
 int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                   const void* k_new, const void* v_new,
-                  const void* k_pages, const void* v_pages, const int32_t* block_table,
+                  const void* k_pages, const void* v_pages, const void* meta, const int32_t* block_table,
                   const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                   int32_t block_size, float scale, void* out, void* stream, int32_t batch,
                   int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
@@ -1148,6 +1448,13 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                    !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(block_table, 4)))
     return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned q/k_pages/v_pages/block_table");
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, f + ": scale is not finite");
+  // PKV_U8: 8-bit cache (codes + per-token scales and zero points), bf16 q and out.
+  const bool q8 = dtype == PKV_U8;
+  if (do_split && q8 != (meta != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, f + (q8 ? ": the 8-bit cache needs its meta array (16-byte aligned)"
+                                             : ": this entry point takes the 8-bit cache only with dtype PKV_U8"));
+  if (do_split && q8 && (!aligned(meta, 16) || k_new != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, f + ": meta must be 16-byte aligned; no fused append on the 8-bit cache");
   if ((k_new != nullptr) != (v_new != nullptr) ||
       (k_new && (!aligned(k_new, 16) || !aligned(v_new, 4))))
     return fail(PKV_ERR_INVALID_ARG, f + ": k_new/v_new must both be given, 16/4-byte aligned");
@@ -1171,6 +1478,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.v_pages = const_cast<void*>(v_pages);
   a.k_new = k_new;
   a.v_new = v_new;
+  a.meta = meta;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = out;
@@ -1202,18 +1510,47 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   if (do_split) {
     const int chunks_per_group = kWavesPerGroup / r.wpc;
     const int grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
-    hipLaunchKernelGGL(split_fn(dtype, head_dim, group), dim3(grid),
+    hipLaunchKernelGGL(split_fn(dtype, head_dim, group, q8), dim3(grid),
                        dim3(kWave * kWavesPerGroup), r.lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
   }
   if (run_combine) {
-    auto fn_c = dtype == PKV_BF16 ? combine_kernel<true> : combine_kernel<false>;
+    auto fn_c = dtype == PKV_F32 ? combine_kernel<false> : combine_kernel<true>;
     const size_t prefix_lds = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
     hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), prefix_lds, s, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
+  return ok();
+}
+
+int append_q8_common(const char* fn, const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                     void* meta, const int32_t* block_table, const int32_t* positions, bool from_lens,
+                     int32_t batch, int32_t n_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* stream) {
+  std::string f(fn);
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, f + ": dtype of k_new/v_new");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (block_size != kBlock) return fail(PKV_ERR_UNSUPPORTED, f + ": block_size must be 16");
+  if (batch < 0 || n_kv_heads < 1 || max_blocks_per_seq < 1 || num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARG, f + ": bad batch/n_kv_heads/max_blocks/num_pages");
+  if (static_cast<int64_t>(batch) * n_kv_heads >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(batch) * max_blocks_per_seq >= (int64_t{1} << 31))
+    return fail(PKV_ERR_UNSUPPORTED, f + ": batch too large");
+  if (batch == 0) return ok();
+  if (!k_new || !v_new || !k_codes || !v_codes || !meta || !block_table || !positions || !aligned(k_new, 4) ||
+      !aligned(v_new, 4) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(meta, 16) ||
+      !aligned(block_table, 4) || !aligned(positions, 4))
+    return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned pointer");
+  const int grid = (batch * n_kv_heads + kWavesPerGroup - 1) / kWavesPerGroup;
+  auto kern = dtype == PKV_BF16 ? append_q8_kernel<true> : append_q8_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, static_cast<hipStream_t>(stream), k_new,
+                     v_new, static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes),
+                     static_cast<float*>(meta), block_table, positions, from_lens ? 1 : 0, batch, n_kv_heads,
+                     head_dim, max_blocks_per_seq, num_pages);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail((f + " launch").c_str(), e);
   return ok();
 }
 
@@ -1266,7 +1603,7 @@ int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_page
                           int32_t num_pages, int32_t dtype, void* workspace,
                           size_t workspace_bytes, const pkv_decode_opts* opts) {
   return pkv::decode_common(true, true, "pkv_paged_decode_attn", q, nullptr, nullptr, k_pages, v_pages,
-                            block_table,
+                            nullptr, block_table,
                             seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out,
                             stream, batch, max_blocks_per_seq, num_pages, dtype, workspace,
                             workspace_bytes, opts);
@@ -1279,7 +1616,7 @@ int pkv_paged_decode_split(const void* q, const void* k_pages, const void* v_pag
                            int32_t num_pages, int32_t dtype, void* workspace,
                            size_t workspace_bytes, const pkv_decode_opts* opts) {
   return pkv::decode_common(true, false, "pkv_paged_decode_split", q, nullptr, nullptr, k_pages,
-                            v_pages, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
+                            v_pages, nullptr, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
                             scale, out, stream, batch, max_blocks_per_seq, num_pages, dtype,
                             workspace, workspace_bytes, opts);
 }
@@ -1293,7 +1630,7 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k
   if (batch > 0 && (!k_new || !v_new))
     return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step: k_new and v_new are required");
   return pkv::decode_common(true, true, "pkv_decode_step", q, k_new, v_new, k_pages, v_pages,
-                            block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
+                            nullptr, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size,
                             scale, out, stream, batch, max_blocks_per_seq, num_pages, dtype,
                             workspace, workspace_bytes, opts);
 }
@@ -1307,7 +1644,7 @@ int pkv_decode_step_split(const void* q, const void* k_new, const void* v_new, v
   if (batch > 0 && (!k_new || !v_new))
     return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_split: k_new and v_new are required");
   return pkv::decode_common(true, false, "pkv_decode_step_split", q, k_new, v_new, k_pages,
-                            v_pages, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim,
+                            v_pages, nullptr, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim,
                             block_size, scale, out, stream, batch, max_blocks_per_seq, num_pages,
                             dtype, workspace, workspace_bytes, opts);
 }
@@ -1317,10 +1654,60 @@ int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t
                     int32_t block_size, int32_t max_blocks_per_seq, void* out, int32_t dtype,
                     const pkv_decode_opts* opts, void* stream) {
   return pkv::decode_common(false, true, "pkv_lse_combine", nullptr, nullptr, nullptr, nullptr, nullptr,
-                            nullptr,
+                            nullptr, nullptr,
                             seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, 1.0f, out,
                             stream, batch, max_blocks_per_seq, 1, dtype,
                             const_cast<void*>(workspace), workspace_bytes, opts);
+}
+
+int pkv_paged_decode_attn_q8(const void* q, const void* k_codes, const void* v_codes, const void* meta,
+                             const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                             int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                             void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                             void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts) {
+  return pkv::decode_common(true, true, "pkv_paged_decode_attn_q8", q, nullptr, nullptr, k_codes, v_codes,
+                            meta, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale,
+                            out, stream, batch, max_blocks_per_seq, num_pages, PKV_U8, workspace,
+                            workspace_bytes, opts);
+}
+
+int pkv_paged_decode_split_q8(const void* q, const void* k_codes, const void* v_codes, const void* meta,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                              int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                              void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                              void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts) {
+  return pkv::decode_common(true, false, "pkv_paged_decode_split_q8", q, nullptr, nullptr, k_codes, v_codes,
+                            meta, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale,
+                            out, stream, batch, max_blocks_per_seq, num_pages, PKV_U8, workspace,
+                            workspace_bytes, opts);
+}
+
+int pkv_decode_step_q8(const void* q, const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                       void* meta, const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                       void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                       void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts) {
+  if (batch > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_q8: k_new and v_new are required");
+  if (batch > 0 && !seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_q8: seq_lens is required");
+  const int st = pkv::append_q8_common("pkv_decode_step_q8", k_new, v_new, k_codes, v_codes, meta, block_table,
+                                       seq_lens, true, batch, n_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, num_pages, PKV_BF16, stream);
+  if (st != PKV_OK) return st;
+  return pkv::decode_common(true, true, "pkv_decode_step_q8", q, nullptr, nullptr, k_codes, v_codes, meta,
+                            block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out,
+                            stream, batch, max_blocks_per_seq, num_pages, PKV_U8, workspace, workspace_bytes,
+                            opts);
+}
+
+int pkv_kv_append_q8(const void* k_new, const void* v_new, void* k_codes, void* v_codes, void* meta,
+                     const int32_t* block_table, const int32_t* positions, int32_t batch, int32_t n_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_pages,
+                     int32_t dtype, void* stream) {
+  return pkv::append_q8_common("pkv_kv_append_q8", k_new, v_new, k_codes, v_codes, meta, block_table, positions,
+                               false, batch, n_kv_heads, head_dim, block_size, max_blocks_per_seq, num_pages,
+                               dtype, stream);
 }
 
 int pkv_decode_resolve(int32_t dtype, int32_t head_dim, int32_t n_q_heads, int32_t n_kv_heads,

@@ -8,7 +8,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib
-from ._lib import PKV_BF16, PKV_F32, DecodeOpts, check, lib
+from ._lib import PKV_BF16, PKV_F32, PKV_U8, DecodeOpts, check, lib
 
 BLOCK_SIZE = 16
 
@@ -19,6 +19,8 @@ def _dtype_code(t) -> int:
         return PKV_BF16
     if t.dtype == torch.float32:
         return PKV_F32
+    if t.dtype == torch.uint8:
+        return PKV_U8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -129,6 +131,8 @@ def decode_plan(seq_lens: Sequence[int], n_kv_heads: int, max_blocks: int, n_ite
 
 # --------------------------------------------------------------- device side
 def kv_append(k_new, v_new, k_pages, v_pages, block_table, positions, stream=None) -> None:
+    if not (k_new.dtype == v_new.dtype == k_pages.dtype == v_pages.dtype):
+        raise TypeError("kv_append: k_new, v_new and the pools must share dtype")
     B, n_kv, D = k_new.shape
     check(lib.pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                             _ptr(positions), B, n_kv, D, BLOCK_SIZE, block_table.shape[1], k_pages.shape[0],
@@ -146,6 +150,23 @@ def copy_blocks(k_pages, v_pages, src_pages, dst_pages, stream=None) -> None:
                               _dtype_code(k_pages), _stream(stream)), "pkv_copy_blocks")
 
 
+def q8_pool_shapes(num_pages: int, n_kv_heads: int, head_dim: int):
+    """Shapes of the 8-bit cache's (k_codes uint8, v_codes uint8, meta float32)."""
+    return ((num_pages, n_kv_heads, head_dim // 16, BLOCK_SIZE, 16), (num_pages, n_kv_heads, head_dim, BLOCK_SIZE),
+            (num_pages, n_kv_heads, 4, BLOCK_SIZE))
+
+
+def kv_append_q8(k_new, v_new, k_codes, v_codes, meta, block_table, positions, stream=None) -> None:
+    """Quantize each sequence's new K/V token into the 8-bit cache at positions[b]."""
+    import torch
+    if k_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8 or meta.dtype != torch.float32:
+        raise TypeError("kv_append_q8: k_codes and v_codes uint8, meta float32")
+    B, n_kv, D = k_new.shape
+    check(lib.pkv_kv_append_q8(_ptr(k_new), _ptr(v_new), _ptr(k_codes), _ptr(v_codes), _ptr(meta),
+                               _ptr(block_table), _ptr(positions), B, n_kv, D, BLOCK_SIZE, block_table.shape[1],
+                               k_codes.shape[0], _dtype_code(k_new), _stream(stream)), "pkv_kv_append_q8")
+
+
 class Decoder:
     """Holds the resolved work split and a workspace for one decode shape
     (batch, heads, head_dim, dtype and the block-table width max_blocks).
@@ -155,7 +176,7 @@ class Decoder:
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype, max_blocks: int,
                  n_items: int = 0, min_chunk_pages: int = 0, device="cuda", combine_mode: int = 0):
         import torch
-        code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+        code = {torch.bfloat16: PKV_BF16, torch.float32: PKV_F32, torch.uint8: PKV_U8}[dtype]
         self.n_items, self.min_chunk_pages, self.ws_bytes = decode_resolve(
             code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks, n_items, min_chunk_pages, combine_mode)
         self.combine_mode = combine_mode
@@ -164,6 +185,8 @@ class Decoder:
         self.max_blocks = max_blocks
 
     def _args(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream):
+        if not (q.dtype == k_pages.dtype == v_pages.dtype == out.dtype) or _dtype_code(q) == PKV_U8:
+            raise TypeError("dense decode: q, k_pages, v_pages and out must share dtype bf16 or float32")
         B, Hq, D = q.shape
         return (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hq,
                 k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B,
@@ -176,6 +199,9 @@ class Decoder:
         return out
 
     def _step_args(self, q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, out, stream):
+        if not (q.dtype == k_new.dtype == v_new.dtype == k_pages.dtype == v_pages.dtype == out.dtype) or \
+                _dtype_code(q) == PKV_U8:
+            raise TypeError("dense decode step: all tensors must share dtype bf16 or float32")
         B, Hq, D = q.shape
         return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                 _ptr(seq_lens), Hq, k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream),
@@ -203,6 +229,33 @@ class Decoder:
                                   BLOCK_SIZE, max_blocks, _ptr(out), _dtype_code(out),
                                   _opts(self.n_items, self.min_chunk_pages, self.combine_mode), _stream(stream)),
               "pkv_lse_combine")
+
+    def _q8_args(self, q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream):
+        import torch
+        if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or k_codes.dtype != torch.uint8 or \
+                v_codes.dtype != torch.uint8 or meta.dtype != torch.float32:
+            raise TypeError("8-bit decode: q and out bf16, k_codes and v_codes uint8, meta float32")
+        B, Hq, D = q.shape
+        return (_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(meta), _ptr(block_table), _ptr(seq_lens), Hq,
+                k_codes.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B, block_table.shape[1],
+                k_codes.shape[0], _ptr(self.workspace), self.workspace.numel(),
+                _opts(self.n_items, self.min_chunk_pages, self.combine_mode))
+
+    def attn_q8(self, q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream=None):
+        """Decode over the 8-bit cache (Decoder built with dtype=torch.uint8; q and out bf16)."""
+        check(lib.pkv_paged_decode_attn_q8(*self._q8_args(q, k_codes, v_codes, meta, block_table, seq_lens, scale,
+                                                          out, stream)), "pkv_paged_decode_attn_q8")
+        return out
+
+    def split_q8(self, q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream=None):
+        check(lib.pkv_paged_decode_split_q8(*self._q8_args(q, k_codes, v_codes, meta, block_table, seq_lens, scale,
+                                                           out, stream)), "pkv_paged_decode_split_q8")
+
+    def step_q8(self, q, k_new, v_new, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream=None):
+        """Quantizing append at seq_lens - 1, then decode over the 8-bit cache."""
+        a = self._q8_args(q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream)
+        check(lib.pkv_decode_step_q8(a[0], _ptr(k_new), _ptr(v_new), *a[1:]), "pkv_decode_step_q8")
+        return out
 
     def partials(self):
         """Views (partial_o [slots][G][D], partial_lse [slots][G]) into the workspace."""

@@ -195,3 +195,25 @@ def make_pools(w: Workload, layer: int = 0, device="cpu"):
     k = torch.randn(k_pool_shape(w), generator=g, device=device, dtype=dt)
     v = torch.randn(v_pool_shape(w), generator=g, device=device, dtype=dt)
     return k, v
+
+
+def q8_pool_shapes(w: Workload, num_pages: Optional[int] = None):
+    """(k_codes, v_codes, meta) shapes of the 8-bit cache for this workload."""
+    P = pool_pages(w) if num_pages is None else num_pages
+    D = w.head_dim
+    return ((P, w.n_kv_heads, D // 16, 16, 16), (P, w.n_kv_heads, D, 16), (P, w.n_kv_heads, 4, 16))
+
+
+def make_q8_pools(w: Workload, layer: int = 0, device="cpu"):
+    """8-bit cache pools as random inputs: codes uniform in [0, 255]; per slot
+    scales uniform in [0.02, 0.03] (about the scale of an N(0,1) vector over
+    255 steps) and integer zero points uniform in [118, 138]."""
+    import torch
+    g = _gen(device, w.seed * 1000 + 10 * layer + 5)
+    ks, vs, ms = q8_pool_shapes(w)
+    k = torch.randint(0, 256, ks, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    v = torch.randint(0, 256, vs, generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    meta = torch.empty(ms, device=device, dtype=torch.float32)
+    meta[:, :, 0::2] = torch.rand(ms[:2] + (2, ms[3]), generator=g, device=device) * 0.01 + 0.02
+    meta[:, :, 1::2] = torch.randint(118, 139, ms[:2] + (2, ms[3]), generator=g, device=device).float()
+    return k, v, meta
