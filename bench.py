@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--kv", choices=["dense", "u8"], default="dense",
+                    help="cache format: the workload's dtype, or the 8-bit cache (bf16 q/out)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (one graph per pool-rotation position)")
     ap.add_argument("--separate-combine", action="store_true",
@@ -67,7 +69,7 @@ class Layer:
     pass
 
 
-def setup(w, device):
+def setup(w, device, kv="dense"):
     import torch
     import paged_kv_cache_254_amd as pkv
     import workloads as W
@@ -85,7 +87,10 @@ def setup(w, device):
         positions=torch.from_numpy(cached.astype(np.int32)).to(device),
         seq_lens=torch.from_numpy(att.astype(np.int32)).to(device),
     )
-    kv_bytes_layer = int(att.sum()) * w.n_kv_heads * w.head_dim * 2 * w.elem_bytes
+    # bytes of cache the step reads per layer: K and V of every attended token
+    # (8-bit cache: the codes plus the slot's 16 bytes of scales and zero points)
+    per_token_head = 2 * w.head_dim + 16 if kv == "u8" else w.head_dim * 2 * w.elem_bytes
+    kv_bytes_layer = int(att.sum()) * w.n_kv_heads * per_token_head
     # Rotate pool copies so that between two reads of one copy at least twice
     # the last-level cache's size of other KV streams through it, and small
     # caches stream at least 4x that cache per step: no launch can be served
@@ -96,7 +101,10 @@ def setup(w, device):
     layers = []
     for i in range(n_copies):
         L = Layer()
-        L.k_pages, L.v_pages = W.make_pools(w, i % max(1, w.n_layers), device)
+        if kv == "u8":
+            L.k_pages, L.v_pages, L.meta = W.make_q8_pools(w, i % max(1, w.n_layers), device)
+        else:
+            L.k_pages, L.v_pages = W.make_pools(w, i % max(1, w.n_layers), device)
         L.q = W.make_q(w, i, device)
         L.k_new, L.v_new = W.make_new_kv(w, i, device)
         L.out = torch.empty_like(L.q)
@@ -105,12 +113,13 @@ def setup(w, device):
                 kv_bytes_layer=kv_bytes_layer, grown=grown, n_copies=n_copies)
 
 
-def cpu_baseline(w, S, budget_s):
+def cpu_baseline(w, S, budget_s, kv="dense"):
     """The oracle, as it stands, on a bounded sample: whole sequences of layer 0
     (append + decode for every query head), until the time budget is used."""
     import torch
     import workloads as W
     from oracle import attention as OA
+    from oracle import kv_quant as KQ
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -123,18 +132,28 @@ def cpu_baseline(w, S, budget_s):
     for b in pick:
         nblk = (int(S["att"][b]) + 15) // 16
         pages = torch.from_numpy(S["bt_np"][b, :nblk].astype(np.int64)).to(L.k_pages.device)
-        kp = L.k_pages.index_select(0, pages).double().cpu().numpy()
-        vp = L.v_pages.index_select(0, pages).double().cpu().numpy()
-        kn = L.k_new[b:b + 1].double().cpu().numpy()
-        vn = L.v_new[b:b + 1].double().cpu().numpy()
         qb = L.q[b:b + 1].double().cpu().numpy()
         bt = np.arange(nblk, dtype=np.int32)[None, :]
-        t0 = time.perf_counter()
-        k2, v2 = OA.append(kp, vp, bt, [int(S["cached"][b])], kn, vn, 16)
-        OA.decode(qb, k2, v2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
+        if kv == "u8":
+            kp = L.k_pages.index_select(0, pages).cpu().numpy()
+            vp = L.v_pages.index_select(0, pages).cpu().numpy()
+            mp = L.meta.index_select(0, pages).cpu().numpy()
+            kn = L.k_new[b:b + 1].float().cpu().numpy()
+            vn = L.v_new[b:b + 1].float().cpu().numpy()
+            t0 = time.perf_counter()
+            k2, v2, m2 = KQ.append(kp, vp, mp, bt, [int(S["cached"][b])], kn, vn, 16)
+            KQ.decode(qb, k2, v2, m2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
+        else:
+            kp = L.k_pages.index_select(0, pages).double().cpu().numpy()
+            vp = L.v_pages.index_select(0, pages).double().cpu().numpy()
+            kn = L.k_new[b:b + 1].double().cpu().numpy()
+            vn = L.v_new[b:b + 1].double().cpu().numpy()
+            t0 = time.perf_counter()
+            k2, v2 = OA.append(kp, vp, bt, [int(S["cached"][b])], kn, vn, 16)
+            OA.decode(qb, k2, v2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
         secs += time.perf_counter() - t0
         done += 1
-        kv_bytes += int(S["att"][b]) * w.n_kv_heads * w.head_dim * 2 * w.elem_bytes
+        kv_bytes += int(S["att"][b]) * S["kv_bytes_layer"] // int(S["att"].sum())
         toks += 1
         if secs >= budget_s:
             break
@@ -169,10 +188,10 @@ def hbm_probe(device):
     return best
 
 
-def traffic_for(workload):
+def traffic_for(workload, kv="dense"):
     """HBM bytes per split-kernel launch from committed rocprofv3 counters, if
     they were taken on the current kernel source; otherwise None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}{'_u8' if kv == 'u8' else ''}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -203,13 +222,22 @@ def main():
         return
     w = W.get(args.workload)
     log(f"setup {w.name}")
-    S = setup(w, device)
-    dt = W.torch_dtype(w)
+    u8 = args.kv == "u8"
+    if u8 and w.dtype != "bf16":
+        print("--kv u8 takes a bf16 workload (its q and out stay bf16)", file=sys.stderr)
+        sys.exit(2)
+    if u8 and args.unfused:
+        print("--kv u8 always appends with its own (quantizing) kernel; --unfused does not apply", file=sys.stderr)
+        sys.exit(2)
+    S = setup(w, device, args.kv)
+    dt = torch.uint8 if u8 else W.torch_dtype(w)
     dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, S["mb"], args.n_items, args.min_chunk,
                       device=device, combine_mode=1 if args.separate_combine else 0)
     # One kernel per layer when every pair can be merged inside the decode
     # kernel (a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks).
-    one_kernel = not args.separate_combine and -(-S["mb"] // dec.min_chunk_pages) + 1 <= 64
+    # (the library's rule: a pair spans at most ceil(max_blocks / min_chunk) + 1
+    # chunks, and pairs of at most 96 are merged inside the decode kernel)
+    one_kernel = not args.separate_combine and -(-S["mb"] // dec.min_chunk_pages) + 1 <= 96
     layers = S["layers"]
     n_layers = w.n_layers
     kv_step = S["kv_bytes_layer"] * n_layers
@@ -226,6 +254,24 @@ def main():
         for li in range(n_layers):
             L = layers[rot[0] % len(layers)]
             rot[0] += 1
+            if u8:
+                if ev is None:
+                    dec.step_q8(L.q, L.k_new, L.v_new, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"],
+                                w.scale, L.out, stream)
+                    continue
+                # timed halves: the quantizing append, then the decode kernel (and combine)
+                pkv.kv_append_q8(L.k_new, L.v_new, L.k_pages, L.v_pages, L.meta, S["bt"], S["positions"], stream)
+                ev[3 * li].record(stream)
+                if one_kernel:
+                    dec.attn_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+                    ev[3 * li + 1].record(stream)
+                else:
+                    dec.split_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out,
+                                 stream)
+                    ev[3 * li + 1].record(stream)
+                    dec.combine(S["seq_lens"], L.out, S["mb"], stream)
+                ev[3 * li + 2].record(stream)
+                continue
             if args.unfused:
                 pkv.kv_append(L.k_new, L.v_new, L.k_pages, L.v_pages, S["bt"], S["positions"], stream)
             if ev is not None:
@@ -299,13 +345,13 @@ def main():
     split_avg = float(np.mean(split_ms))
     achieved = S["kv_bytes_layer"] / (split_avg / 1e3) / 1e9
     value = kv_step / (ms_per_step / 1e3) / 1e9
-    traffic = traffic_for(w.name)
+    traffic = traffic_for(w.name, args.kv)
 
     probe = None if args.no_probe else hbm_probe(device)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(w, S, args.cpu_seconds)
+        cpu = cpu_baseline(w, S, args.cpu_seconds, args.kv)
         cpu.pop("seconds", None)
 
     rec = {
@@ -319,7 +365,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("u8 cache, bf16 q/out" if u8 else "bf16") if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
@@ -327,8 +373,9 @@ def main():
             "attended_tokens": int(S["att"].sum()), "kv_bytes_per_step": kv_step,
             "accumulate": "fp32", "n_items": dec.n_items, "min_chunk_pages": dec.min_chunk_pages,
             "pool_copies": len(layers),
-            "append": "separate kernel" if args.unfused else "fused into the decode kernel",
+            "append": "quantizing kernel" if u8 else ("separate kernel" if args.unfused else "fused into the decode kernel"),
             "merge": "combine kernel" if not one_kernel else "inside the decode kernel",
+            "kv_cache": "8-bit codes + per-token scale/zero (2D+16 B per token and head)" if u8 else w.dtype,
             "launch": "hip graph replay" if graphs else "eager",
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

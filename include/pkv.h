@@ -180,21 +180,23 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  * exponentials) and the partials are merged.  By default the chunk that
  * finishes a pair last merges them in the same launch (arrival counted by
  * one atomic per chunk; merge order is fixed, so results are run-to-run
- * identical); pairs that may span more than 64 chunks (ceil(max_blocks_per_seq
- * / min_chunk_pages) + 1 > 64) are merged by a second kernel, which is then
+ * identical); pairs that may span more than 96 chunks (ceil(max_blocks_per_seq
+ * / min_chunk_pages) + 1 > 96) are merged by a second kernel, which is then
  * launched on the same stream.
  *
  * workspace: device, 256-byte aligned, at least
  * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
- * bytes (n_items after defaults are applied).  Its partials are overwritten
- * by every call; its arrival counters (the last 16 * batch * n_kv_heads
- * bytes) must be zero before the first pkv_paged_decode_attn or
- * pkv_decode_step call that uses it (e.g. a zero-filled allocation), and
- * every call leaves them zero.  Calls that overlap in time must not share a
- * workspace.
+ * bytes (n_items after defaults are applied).  Layout: the partials, then
+ * (256-byte aligned) 16 * batch * n_kv_heads bytes of arrival counters, then
+ * 4 * (batch + 1) bytes where the split kernel stores the per-sequence page
+ * prefix for the combine kernel.  Partials and prefix are overwritten by
+ * every call; the counters must be zero before the first full call that uses
+ * the workspace (e.g. a zero-filled allocation), and every call leaves them
+ * zero.  Calls that overlap in time must not share a workspace.
  * opts (nullable): n_items <= 0 means as many chunks as the device holds at
  * once (resident wavefronts divided by the wavefronts per chunk);
- * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups);
+ * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups,
+ * and the 8-bit cache, dtype PKV_U8, at every group size);
  * combine_mode 0 merges in the decode kernel where the bound above allows,
  * 1 always merges with the separate combine kernel (counters untouched).
  * ------------------------------------------------------------------------ */

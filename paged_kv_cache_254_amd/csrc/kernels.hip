@@ -213,6 +213,9 @@ struct DecodeArgs {
   // chunks last merges its partials (one counter per pair and head block).
   int32_t* counters;
   int32_t fuse_max_parts;
+  // Per-sequence page prefix [batch + 1] in the workspace: written by the
+  // split kernel's first workgroup, read by the combine kernel.
+  int32_t* prefix;
 };
 
 // Pages per sequence, exclusive prefix over the batch, into LDS (whole
@@ -955,6 +958,8 @@ split_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uni(threadIdx.x / kWave);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.prefix[i] = s_prefix[i];
   if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, KV::kOutBf16, lane);
   const int chunk = blockIdx.x * (kWavesPerGroup / kNG) + wave / kNG;
   const int gblk = wave % kNG;
@@ -1065,15 +1070,13 @@ split_kernel(DecodeArgs a) {
 // threads; thread (slice, t) accumulates features 8t .. 8t+7 (two 16-byte
 // loads) of every n_slices-th partial, and the slices are summed through
 // LDS.  Rows of empty sequences become zeros, rows of invalid lengths NaN.
+// The page prefix comes from the workspace, where the split kernel stored it.
 template <bool kBf16>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
-  extern __shared__ int32_t smem[];
-  int32_t* s_prefix = smem;
-  int32_t* s_wsum = smem + a.batch + 1;
   __shared__ float s_red[256];
   __shared__ f32x4 s_acc[2 * 256];
   __shared__ float s_den[256];
-  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
+  const int32_t* s_prefix = a.prefix;   // stored by the split kernel
   const int G = a.group;
   const int row = blockIdx.x;                 // b * n_q + hq
   const int b = row / a.n_q;
@@ -1339,10 +1342,10 @@ size_t split_lds_bytes(int batch) {
 // as large, so fp32 keeps one page ahead.
 constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
 
-// 8-bit pages are half the bytes of bf16 ones: one more page ahead keeps
-// about as many bytes in flight.
+// Pages ahead in the 8-bit kernel's ring: 3 measured no faster than 2, and
+// 4 no longer fits the registers of two wavefronts per SIMD (spills).
 #ifndef PKV_Q8_PREFETCH_PAGES
-#define PKV_Q8_PREFETCH_PAGES 3
+#define PKV_Q8_PREFETCH_PAGES 2
 #endif
 
 template <int kNG>
@@ -1412,7 +1415,7 @@ int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, 
     return fail(PKV_ERR_INVALID_ARG, "decode: combine_mode must be 0 or 1");
   r->lds = split_lds_bytes(batch);
   r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages
-                                                     : default_min_chunk(group);
+                                                     : default_min_chunk(group, dtype == PKV_U8);
   if (opts && opts->n_items > 0) {
     if (opts->n_items > kMaxItems)
       return fail(PKV_ERR_INVALID_ARG, "decode: n_items above 2^22");
@@ -1505,6 +1508,8 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                                                                         r.n_items))
                     : nullptr;
   a.fuse_max_parts = kFuseMaxParts;
+  a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                        decode_prefix_offset(batch, group, n_kv_heads, head_dim, r.n_items));
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
@@ -1517,8 +1522,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   }
   if (run_combine) {
     auto fn_c = dtype == PKV_F32 ? combine_kernel<false> : combine_kernel<true>;
-    const size_t prefix_lds = static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
-    hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), prefix_lds, s, a, head_dim);
+    hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), 0, s, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }

@@ -25,8 +25,12 @@ constexpr int kMaxGroup = 64;       // query heads per KV head
 // them short, and each chunk pays a start-up latency and one partial per
 // query head.  Measured on MI355X: 64 pages for groups <= 16 (131072-token
 // GQA layer: 1024 chunks of 64 pages beat 2048 of 32 by 10%), 32 for larger
-// groups (131072-token MQA: one chunk per CU is best).
-__host__ __device__ inline int default_min_chunk(int group) { return group > 16 ? 32 : 64; }
+// groups (131072-token MQA: one chunk per CU is best).  The 8-bit cache's
+// pages are half the bytes, and 32 pages is best there at every group size
+// (131072-token GQA layer: 2048 chunks of 32 pages beat 1024 of 64 by 27%).
+__host__ __device__ inline int default_min_chunk(int group, bool q8 = false) {
+  return (q8 || group > 16) ? 32 : 64;
+}
 constexpr int kMaxItems = 1 << 22;  // work items per decode launch
 constexpr size_t kMaxLdsBytes = 64 * 1024;  // LDS one decode workgroup may use
 
@@ -53,12 +57,13 @@ __host__ __device__ inline int64_t decode_slots(int64_t batch, int64_t n_kv, int
 // Pairs whose pages span at most this many chunks are merged by the chunk
 // that finishes last, inside the decode kernel; longer ones by the combine
 // kernel (one wavefront would read all their partials).
-constexpr int kFuseMaxParts = 64;
+constexpr int kFuseMaxParts = 96;
 constexpr int kMaxWavesPerChunk = 4;
 
 // Workspace layout: partial outputs [slots][group][head_dim] f32, partial
 // lse [slots][group] f32, then (256-byte aligned) one arrival counter per
-// (sequence, KV head, head block), int32.
+// (sequence, KV head, head block), int32, then the per-sequence page prefix
+// [batch + 1] int32 that the split kernel stores for the combine kernel.
 __host__ __device__ inline int64_t decode_counters_offset(int64_t batch, int64_t group, int64_t n_kv,
                                                           int64_t head_dim, int64_t n_items) {
   const int64_t parts = decode_slots(batch, n_kv, n_items) * group * (head_dim + 1) * 4;
@@ -66,6 +71,10 @@ __host__ __device__ inline int64_t decode_counters_offset(int64_t batch, int64_t
 }
 __host__ __device__ inline int64_t decode_counters_count(int64_t batch, int64_t n_kv) {
   return batch * n_kv * kMaxWavesPerChunk;
+}
+__host__ __device__ inline int64_t decode_prefix_offset(int64_t batch, int64_t group, int64_t n_kv,
+                                                        int64_t head_dim, int64_t n_items) {
+  return decode_counters_offset(batch, group, n_kv, head_dim, n_items) + decode_counters_count(batch, n_kv) * 4;
 }
 
 }  // namespace pkv

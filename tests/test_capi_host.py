@@ -176,12 +176,13 @@ def test_plan_matches_flattened_chunking(lens, n_kv, n_items, min_chunk):
 
 def test_workspace_bytes():
     # partials (slots x group x (head_dim + 1) floats), padded to 256 bytes,
-    # then 4 int32 arrival counters per (sequence, KV head)
+    # then 4 int32 arrival counters per (sequence, KV head), then the
+    # per-sequence page prefix (batch + 1 int32)
     def layout(batch, hq, hkv, d, n_items):
         parts = (n_items + batch * hkv) * (hq // hkv) * (d + 1) * 4
-        return -(-parts // 256) * 256 + batch * hkv * 4 * 4
-    assert pkv.decode_workspace_bytes(16, 32, 32, 128, 2048) == (2048 + 16 * 32) * 1 * 129 * 4 + 16 * 32 * 16
-    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4) == 4352 + 64
+        return -(-parts // 256) * 256 + batch * hkv * 4 * 4 + (batch + 1) * 4
+    assert pkv.decode_workspace_bytes(16, 32, 32, 128, 2048) == (2048 + 16 * 32) * 1 * 129 * 4 + 16 * 32 * 16 + 68
+    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4) == 4352 + 64 + 12
     for args in ((16, 32, 32, 128, 2048), (2, 4, 2, 64, 4), (3, 64, 1, 128, 7), (256, 32, 8, 128, 2048)):
         assert pkv.decode_workspace_bytes(*args) == layout(*args)
     with pytest.raises(pkv.PkvError):

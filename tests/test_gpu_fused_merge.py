@@ -2,7 +2,7 @@
 merges the pair's partials): parity with the oracle, run-to-run identity on
 one workspace (the arrival counters reset themselves), agreement with the
 separate combine kernel, large groups (one counter per 16-head block), and
-the mixed launch where pairs that may span more than 64 chunks still go to
+the mixed launch where pairs that may span more than 96 chunks still go to
 the combine kernel while the others are merged in the decode kernel."""
 import numpy as np
 import pytest
@@ -44,9 +44,12 @@ def _decode(pkv, w, c, n_items, min_chunk, combine_mode=0, dec=None):
 
 
 def _counters_zero(dec):
+    # layout tail: counters (16 bytes per sequence and KV head), then the
+    # page prefix (4 bytes per sequence, plus one)
     B, Hq, Hkv, D = dec.shape
-    tail = dec.workspace[dec.ws_bytes - 16 * B * Hkv: dec.ws_bytes]
-    return int(tail.count_nonzero().item()) == 0
+    end = dec.ws_bytes - 4 * (B + 1)
+    ctr = dec.workspace[end - 16 * B * Hkv: end]
+    return int(ctr.count_nonzero().item()) == 0
 
 
 def test_repeated_calls_on_one_workspace(pkv):
@@ -68,17 +71,17 @@ def test_repeated_calls_on_one_workspace(pkv):
 
 
 def test_long_pairs_use_the_combine_kernel_beside_fused_ones(pkv):
-    # chunks of one page: pair (0, h) spans 69 chunks (> 64, combine kernel),
+    # chunks of one page: pair (0, h) spans 101 chunks (> 96, combine kernel),
     # pair (1, h) spans 3 (merged in the decode kernel), sequence 2 is empty
-    w, c, ref = _case(pkv, "fm_mixed", 3, 8, 2, 128, "bf16", [1099, 39, 5], 72)
+    w, c, ref = _case(pkv, "fm_mixed", 3, 8, 2, 128, "bf16", [1615, 39, 5], 72)
     c.seq_lens[2] = 0
-    H.log("fused merge: mixed long/short pairs, 150 chunks of 1 page")
+    H.log("fused merge: mixed long/short pairs, 250 chunks of 1 page")
     for mode in (0, 1):
-        out, dec = _decode(pkv, w, c, 150, 1, combine_mode=mode)
+        out, dec = _decode(pkv, w, c, 250, 1, combine_mode=mode)
         o = H.f64(out)
         H.assert_close(o[:2], ref[:2], "bf16", f"mixed mode {mode}")
         assert (o[2] == 0).all()
-        again, _ = _decode(pkv, w, c, 150, 1, dec=dec)
+        again, _ = _decode(pkv, w, c, 250, 1, dec=dec)
         assert torch.equal(again, out)
         assert _counters_zero(dec)
 
