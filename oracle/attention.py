@@ -31,6 +31,11 @@ What is computed, and where the pages define it:
   the combine reweights partials by exp(lse - max lse).
 * Appending: each decode step writes the new token's K and V into each layer's
   cache (docs section "What the KV cache stores per layer").
+* Several query tokens at once (``decode_multi``): the last q_len cached
+  tokens each attend causally, optionally within a sliding window (see
+  ``query_range``); the speculative-decoding passages of "Inference Engines"
+  and the CS336 notes ("Exploit checking is faster than generating") run the
+  target model once over all drafted tokens.
 
 Physical layout read here (a caller/library contract; the pages fix only the
 block size): K pages ``[P][Hkv][D/X][bs][X]``, V pages ``[P][Hkv][D][bs]``.
@@ -143,6 +148,51 @@ def decode(q, k_pages, v_pages, block_table, seq_lens, n_q_heads: int, n_kv_head
         for hq in range(n_q_heads):
             h = hq // group
             out[b, hq] = attend(q[b, hq], K[:, h, :], V[:, h, :], scale)
+    return out
+
+
+def query_range(seq_len: int, q_len: int, i: int, window: int) -> Tuple[int, int]:
+    """Keys [lo, hi) that query token i of the last q_len cached tokens attends.
+
+    Query i sits at position seq_len - q_len + i and, causally, sees keys up
+    to and including its own position (evaltude docs, "What Q, K, and V do in
+    causal attention").  With a sliding window of W > 0 it sees only the last
+    W of those (CS336 lecture 10 notes, "Local attention & sparse variants":
+    each token attends to the last K)."""
+    hi = seq_len - q_len + i + 1
+    lo = max(0, hi - window) if window > 0 else 0
+    return lo, hi
+
+
+def decode_multi(q, k_pages, v_pages, block_table, seq_lens, q_len: int, n_q_heads: int,
+                 n_kv_heads: int, block_size: int, scale: float, window: int = 0) -> np.ndarray:
+    """Attention of the last q_len cached tokens of each sequence (a drafted
+    run being verified in one pass, or a prefill chunk), each over the keys
+    query_range gives: out[b, i, hq] = attend(q[b, i, hq], K_b[lo:hi, h],
+    V_b[lo:hi, h]) with h = hq // G.  q and out are [B][q_len][Hq][D];
+    seq_lens count every cached token, the q_len new ones included (the
+    drafted tokens' K/V are appended first; "Inference Engines", the
+    speculative-decoding paragraph: the target model runs once over the whole
+    drafted sequence).  q_len = 1, window = 0 is decode()."""
+    if n_q_heads % n_kv_heads != 0:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    group = n_q_heads // n_kv_heads
+    q = _as_f64(q)
+    B, T, _, d = q.shape
+    assert T == q_len
+    out = np.zeros((B, T, n_q_heads, d), dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        K, V = gather(k_pages, v_pages, block_table[b], n, block_size)
+        for i in range(T):
+            lo, hi = query_range(n, T, i, window)
+            if hi <= 0:
+                continue
+            for hq in range(n_q_heads):
+                h = hq // group
+                out[b, i, hq] = attend(q[b, i, hq], K[lo:hi, h, :], V[lo:hi, h, :], scale)
     return out
 
 

@@ -185,3 +185,32 @@ def test_quant_key_chunk_order_is_caught(monkeypatch):
     # needs more than one 16-feature chunk: the D = 64 and D = 32 pins
     assert any(_fails(TQ.test_decode_equals_decode_of_dequantized_pools, *c)
                for c in [(8, 2, 64, [40, 5, 17]), (4, 4, 32, [33])])
+
+
+# ------------------------------------------------------- multi-token queries
+from . import test_oracle_multi as TM  # noqa: E402
+
+_SELF = [(4, 2, 32, 37, 0), (4, 2, 32, 45, 7)]
+
+
+def test_multi_causal_bound_excluding_self_is_caught(monkeypatch):
+    def range_no_self(seq_len, q_len, i, window):
+        hi = seq_len - q_len + i               # planted: the query's own key left out
+        return (max(0, hi - window) if window > 0 else 0), hi
+    monkeypatch.setattr(A, "query_range", range_no_self)
+    assert any(_fails(TM.test_all_tokens_as_queries_is_causal_self_attention, *c) for c in _SELF)
+    assert _fails(TM.test_brute_force_tiny_window)
+
+
+def test_multi_window_off_by_one_is_caught(monkeypatch):
+    orig = A.query_range
+    monkeypatch.setattr(A, "query_range",
+                        lambda n, T, i, w: (orig(n, T, i, w)[0] + (1 if w > 0 else 0), orig(n, T, i, w)[1]))
+    assert _fails(TM.test_all_tokens_as_queries_is_causal_self_attention, 4, 2, 32, 45, 7)
+    assert _fails(TM.test_keys_outside_the_range_do_not_matter)
+
+
+def test_multi_query_order_reversed_is_caught(monkeypatch):
+    orig = A.query_range
+    monkeypatch.setattr(A, "query_range", lambda n, T, i, w: orig(n, T, T - 1 - i, w))   # planted
+    assert any(_fails(TM.test_all_tokens_as_queries_is_causal_self_attention, *c) for c in _SELF)
