@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--kv", choices=["dense", "u8"], default="dense",
                     help="cache format: the workload's dtype, or the 8-bit cache (bf16 q/out)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence: the last q-len cached tokens attend causally (no append)")
+    ap.add_argument("--window", type=int, default=0, help="sliding window (with --q-len; 0: none)")
     ap.add_argument("--graph", action="store_true",
                     help="replay each step from a captured HIP graph (one graph per pool-rotation position)")
     ap.add_argument("--separate-combine", action="store_true",
@@ -69,7 +72,16 @@ class Layer:
     pass
 
 
-def setup(w, device, kv="dense"):
+def multi_kv_tokens(att, q_len, window):
+    """Tokens whose K/V the multi-token decode must read per sequence and KV
+    head: the union of the query tokens' key ranges, from the first query's
+    window start (0 without a window) to the end."""
+    if window <= 0:
+        return att.copy()
+    return np.minimum(att, window + q_len - 1)
+
+
+def setup(w, device, kv="dense", q_len=1, window=0):
     import torch
     import paged_kv_cache_254_amd as pkv
     import workloads as W
@@ -90,7 +102,8 @@ def setup(w, device, kv="dense"):
     # bytes of cache the step reads per layer: K and V of every attended token
     # (8-bit cache: the codes plus the slot's 16 bytes of scales and zero points)
     per_token_head = 2 * w.head_dim + 16 if kv == "u8" else w.head_dim * 2 * w.elem_bytes
-    kv_bytes_layer = int(att.sum()) * w.n_kv_heads * per_token_head
+    read_tokens = multi_kv_tokens(att, q_len, window) if q_len > 1 or window > 0 else att
+    kv_bytes_layer = int(read_tokens.sum()) * w.n_kv_heads * per_token_head
     # Rotate pool copies so that between two reads of one copy at least twice
     # the last-level cache's size of other KV streams through it, and small
     # caches stream at least 4x that cache per step: no launch can be served
@@ -105,7 +118,11 @@ def setup(w, device, kv="dense"):
             L.k_pages, L.v_pages, L.meta = W.make_q8_pools(w, i % max(1, w.n_layers), device)
         else:
             L.k_pages, L.v_pages = W.make_pools(w, i % max(1, w.n_layers), device)
-        L.q = W.make_q(w, i, device)
+        if q_len > 1 or window > 0:
+            # [B][q_len][Hq][D]: the query vectors of the last q_len cached tokens
+            L.q = torch.stack([W.make_q(w, i * q_len + t, device) for t in range(q_len)], dim=1).contiguous()
+        else:
+            L.q = W.make_q(w, i, device)
         L.k_new, L.v_new = W.make_new_kv(w, i, device)
         L.out = torch.empty_like(L.q)
         layers.append(L)
@@ -113,9 +130,10 @@ def setup(w, device, kv="dense"):
                 kv_bytes_layer=kv_bytes_layer, grown=grown, n_copies=n_copies)
 
 
-def cpu_baseline(w, S, budget_s, kv="dense"):
+def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0):
     """The oracle, as it stands, on a bounded sample: whole sequences of layer 0
-    (append + decode for every query head), until the time budget is used."""
+    (append + decode for every query head; with q_len > 1 or a window, the
+    multi-token decode), until the time budget is used."""
     import torch
     import workloads as W
     from oracle import attention as OA
@@ -134,7 +152,14 @@ def cpu_baseline(w, S, budget_s, kv="dense"):
         pages = torch.from_numpy(S["bt_np"][b, :nblk].astype(np.int64)).to(L.k_pages.device)
         qb = L.q[b:b + 1].double().cpu().numpy()
         bt = np.arange(nblk, dtype=np.int32)[None, :]
-        if kv == "u8":
+        multi = q_len > 1 or window > 0
+        if multi:
+            kp = L.k_pages.index_select(0, pages).double().cpu().numpy()
+            vp = L.v_pages.index_select(0, pages).double().cpu().numpy()
+            t0 = time.perf_counter()
+            OA.decode_multi(qb, kp, vp, bt, [int(S["att"][b])], q_len, w.n_q_heads, w.n_kv_heads, 16, w.scale,
+                            window)
+        elif kv == "u8":
             kp = L.k_pages.index_select(0, pages).cpu().numpy()
             vp = L.v_pages.index_select(0, pages).cpu().numpy()
             mp = L.meta.index_select(0, pages).cpu().numpy()
@@ -153,13 +178,15 @@ def cpu_baseline(w, S, budget_s, kv="dense"):
             OA.decode(qb, k2, v2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
         secs += time.perf_counter() - t0
         done += 1
-        kv_bytes += int(S["att"][b]) * S["kv_bytes_layer"] // int(S["att"].sum())
-        toks += 1
+        read = multi_kv_tokens(S["att"], q_len, window) if multi else S["att"]
+        kv_bytes += int(read[b]) * S["kv_bytes_layer"] // int(read.sum())
+        toks += q_len
         if secs >= budget_s:
             break
     return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.batch} sequences of one layer (append + decode, all {w.n_q_heads} query "
-                      f"heads), {kv_bytes / 2**20:.0f} MiB of KV, {secs:.1f} s",
+            "sample": f"{done} of {w.batch} sequences of one layer "
+                      f"({f'{q_len}-token decode' if q_len > 1 or window > 0 else 'append + decode'}, "
+                      f"all {w.n_q_heads} query heads), {kv_bytes / 2**20:.0f} MiB of KV, {secs:.1f} s",
             "seconds": secs}
 
 
@@ -229,10 +256,16 @@ def main():
     if u8 and args.unfused:
         print("--kv u8 always appends with its own (quantizing) kernel; --unfused does not apply", file=sys.stderr)
         sys.exit(2)
-    S = setup(w, device, args.kv)
+    T, window = args.q_len, args.window
+    multi = T > 1 or window > 0
+    if multi and (u8 or args.unfused or args.separate_combine or T < 1 or window < 0):
+        print("--q-len/--window take the dense cache, with the library's own merge", file=sys.stderr)
+        sys.exit(2)
+    S = setup(w, device, args.kv, T, window)
     dt = torch.uint8 if u8 else W.torch_dtype(w)
-    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, dt, S["mb"], args.n_items, args.min_chunk,
-                      device=device, combine_mode=1 if args.separate_combine else 0)
+    # the multi-token decode runs q_len x Hq query columns: the Decoder is built for them
+    dec = pkv.Decoder(w.batch, w.n_q_heads * T, w.n_kv_heads, w.head_dim, dt, S["mb"], args.n_items,
+                      args.min_chunk, device=device, combine_mode=1 if args.separate_combine else 0)
     # One kernel per layer when every pair can be merged inside the decode
     # kernel (a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks).
     # (the library's rule: a pair spans at most ceil(max_blocks / min_chunk) + 1
@@ -254,6 +287,16 @@ def main():
         for li in range(n_layers):
             L = layers[rot[0] % len(layers)]
             rot[0] += 1
+            if multi:
+                # one library call (decode kernel, merge inside it or in the combine kernel)
+                if ev is not None:
+                    ev[3 * li].record(stream)
+                dec.attn_multi(L.q, L.k_pages, L.v_pages, S["bt"], S["seq_lens"], T, w.scale, L.out, window,
+                               stream)
+                if ev is not None:
+                    ev[3 * li + 1].record(stream)
+                    ev[3 * li + 2].record(stream)
+                continue
             if u8:
                 if ev is None:
                     dec.step_q8(L.q, L.k_new, L.v_new, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"],
@@ -345,13 +388,13 @@ def main():
     split_avg = float(np.mean(split_ms))
     achieved = S["kv_bytes_layer"] / (split_avg / 1e3) / 1e9
     value = kv_step / (ms_per_step / 1e3) / 1e9
-    traffic = traffic_for(w.name, args.kv)
+    traffic = None if multi else traffic_for(w.name, args.kv)   # counters are taken on the one-token decode
 
     probe = None if args.no_probe else hbm_probe(device)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(w, S, args.cpu_seconds, args.kv)
+        cpu = cpu_baseline(w, S, args.cpu_seconds, args.kv, T, window)
         cpu.pop("seconds", None)
 
     rec = {
@@ -377,9 +420,11 @@ def main():
             "merge": "combine kernel" if not one_kernel else "inside the decode kernel",
             "kv_cache": "8-bit codes + per-token scale/zero (2D+16 B per token and head)" if u8 else w.dtype,
             "launch": "hip graph replay" if graphs else "eager",
+            **({"q_len": T, "window": window, "append": "none (tokens cached before the step)",
+                "merge": "library call (split + merge; timed together)"} if multi else {}),
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(w.batch / (ms_per_step / 1e3), 1),
+        "tokens_per_s": round(w.batch * T / (ms_per_step / 1e3), 1),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -387,7 +432,7 @@ def main():
             "algorithmic_bytes_per_launch": S["kv_bytes_layer"],
         },
         "split_median_ms": round(float(np.median(split_ms)), 5),
-        "combine_avg_ms": None if one_kernel else round(float(np.mean(comb_ms)), 5),
+        "combine_avg_ms": None if one_kernel or multi else round(float(np.mean(comb_ms)), 5),
         "hbm_read_probe_gbs": None if probe is None else round(probe, 1),
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),

@@ -295,6 +295,30 @@ int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
                     int32_t* last_chunk);
 
 /* ------------------------------------------------------------------------ *
+ * paged_decode_multi (device): several query tokens per sequence, for
+ * verifying a drafted run in one pass (speculative decoding: "Inference
+ * Engines" and the CS336 notes run the target once over all drafted tokens)
+ * or a chunk of prefill, optionally with a sliding window (CS336 notes,
+ * "Local attention & sparse variants": each token attends to the last W).
+ * The last q_len cached tokens of sequence b are the queries: query i sits at
+ * position seq_lens[b] - q_len + i and attends keys [lo, hi) with
+ * hi = seq_lens[b] - q_len + i + 1 and lo = window > 0 ? max(0, hi - window)
+ * : 0.  Their K/V must already be appended (pkv_kv_append per token).
+ * q, out: [batch][q_len][n_q_heads][head_dim], dtype as pkv_paged_decode_attn.
+ * Requires q_len >= 1, window >= 0, q_len * (n_q_heads / n_kv_heads) <= 64;
+ * a length of 0 gives zero rows, a length below q_len NaN rows.  Pages wholly
+ * before every query's window are not read.  The workspace and options are
+ * those of pkv_paged_decode_attn for n_q_heads * q_len query heads (size it
+ * with pkv_decode_resolve / pkv_decode_workspace_bytes given n_q_heads *
+ * q_len).  q_len = 1, window = 0 is pkv_paged_decode_attn.
+ * ------------------------------------------------------------------------ */
+int pkv_paged_decode_multi(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t q_len, int32_t window, float scale, void* out,
+                           void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                           int32_t dtype, void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
+
+/* ------------------------------------------------------------------------ *
  * 8-bit KV cache (device).  Cache quantization changes the bytes per cached
  * element (evaltude docs "Transformer inference mechanics", section "What the
  * KV cache stores per layer"); uniform integer quantization uses a scale and a

@@ -6,7 +6,8 @@ library has not been built, and there is no CPU or PyTorch fallback.
 """
 from ._lib import LIB_PATH, PKV_BF16, PKV_F32, PKV_U8, PkvError, lib  # noqa: F401
 from .ops import (BLOCK_SIZE, Decoder, PagePool, copy_blocks, copy_probe, decode_resolve,  # noqa: F401
-                  decode_plan, decode_workspace_bytes, hbm_read_probe, kv_append, kv_append_q8, q8_pool_shapes,
+                  decode_plan, decode_workspace_bytes, hbm_read_probe, kv_append, kv_append_q8, kv_append_tokens,
+                  q8_pool_shapes,
                   kv_bytes_per_token, kv_cache_bytes, paged_decode_attn)
 
 __version__ = lib.pkv_version().decode()

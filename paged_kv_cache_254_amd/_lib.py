@@ -88,6 +88,9 @@ SIGNATURES = {
                                           ctypes.POINTER(DecodeOpts), ctypes.POINTER(ctypes.c_int64)]),
     "pkv_decode_plan": (ctypes.c_int, [_pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32, _pi32]),
     "pkv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_decode_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                              _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz,
+                                              ctypes.POINTER(DecodeOpts)]),
     "pkv_kv_append_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _vp]),
     "pkv_paged_decode_attn_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,

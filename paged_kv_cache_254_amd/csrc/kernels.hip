@@ -207,6 +207,10 @@ struct DecodeArgs {
   float* part_o;
   float* part_lse;
   int32_t batch, n_q, n_kv, group, max_blocks, num_pages;
+  // Query tokens per sequence (the last q_len cached tokens, causal) and the
+  // sliding window (0: none); cols = q_len * group columns per KV head, in
+  // (query token, query head) order.
+  int32_t q_len, window, cols;
   int32_t n_items, min_chunk, waves_per_chunk;
   float scale_log2;
   // Non-null: the chunk that finishes a pair of at most fuse_max_parts
@@ -218,18 +222,19 @@ struct DecodeArgs {
   int32_t* prefix;
 };
 
-// Pages per sequence, exclusive prefix over the batch, into LDS (whole
+// Pages per sequence (those from its first attended block, see
+// pages_of_range), exclusive prefix over the batch, into LDS (whole
 // workgroup).  s_prefix[b] = pages of sequences before b; s_prefix[batch] =
-// total.  A length outside [0, 16 * max_blocks] counts as zero pages.
-__device__ void build_prefix(const int32_t* __restrict__ seq_lens, int batch, int max_blocks,
-                             int32_t* s_prefix, int32_t* s_wsum) {
+// total.  A length outside [q_len, 16 * max_blocks] counts as zero pages.
+__device__ void build_prefix(const int32_t* __restrict__ seq_lens, int batch, int max_blocks, int q_len,
+                             int window, int32_t* s_prefix, int32_t* s_wsum) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int per = (batch + nthr - 1) / nthr;
   const int b0 = min(batch, tid * per);
   const int b1 = min(batch, b0 + per);
   int local = 0;
-  for (int b = b0; b < b1; ++b) local += pages_of_len(seq_lens[b], max_blocks);
+  for (int b = b0; b < b1; ++b) local += pages_of_range(seq_lens[b], max_blocks, q_len, window);
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
   int x = local;
@@ -245,7 +250,7 @@ __device__ void build_prefix(const int32_t* __restrict__ seq_lens, int batch, in
   int run = base + x - local;
   for (int b = b0; b < b1; ++b) {
     s_prefix[b] = run;
-    run += pages_of_len(seq_lens[b], max_blocks);
+    run += pages_of_range(seq_lens[b], max_blocks, q_len, window);
   }
   if (tid == nthr - 1) s_prefix[batch] = base + x;
   __syncthreads();
@@ -336,6 +341,12 @@ __device__ inline void load_page(PageRegs<kBf16, D>& r, const char* kbase, const
 // accepted without rescaling: exponentials stay <= 2^8, far from overflow in
 // fp32 accumulation and exactly representable in range for bf16.
 constexpr float kLazyRescale = 8.0f;
+// Running maximum of a column before it has seen any key.  Finite, so that a
+// column whose keys are all masked so far (a later query token whose window
+// starts past the page, or a chunk wholly past a query token's position)
+// weighs its scores exp2(-inf - kNoKeysMax) = 0 and rescales by exp2(0) = 1,
+// where -inf would give exp2(-inf - -inf) = NaN.  Scores are far above it.
+constexpr float kNoKeysMax = -1.0e30f;
 
 // One page of the online softmax for the 16 query heads of this wavefront.
 // The running maximum m of a query head is shared by the four lanes of its
@@ -343,19 +354,30 @@ constexpr float kLazyRescale = 8.0f;
 // score of the page exceeds it by more than kLazyRescale, which one wave-wide
 // vote detects.  Between raises, m is an upper bound minus at most 8, so
 // exp2(x - m) <= 2^8, and the final division by the sum is unchanged.
-template <bool kBf16, int D>
-__device__ inline void compute_page(PageRegs<kBf16, D>& r, int valid,
+//
+// Masks: when `cut` (scalar: some column's key range [lo, hi) ends or starts
+// inside this page), the lane keeps token tok0 + 4c + i only inside its own
+// column's range; V elements of slots past the sequence (valid < 16, last
+// page only) are zeroed, since 0 * NaN would poison the sums.
+template <bool kBf16, int D, bool kMulti>
+__device__ inline void compute_page(PageRegs<kBf16, D>& r, int valid, bool cut, int tok0, int hi, int lo,
                                     const u32x4 (&qreg)[Ops<kBf16, D>::NK], float scale_log2,
                                     int c, float& m, float& l,
                                     f32x4 (&acc)[Ops<kBf16, D>::NV]) {
   using O = Ops<kBf16, D>;
-  f32x4 s = O::qk(r.k, qreg);   // lane (c, n): tokens 4c + i, query head n
+  f32x4 s = O::qk(r.k, qreg);   // lane (c, n): tokens 4c + i, column n
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = s[i] * scale_log2;
-  if (valid < kBlock) {
+  if (cut) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * c + i < valid) ? x[i] : -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      const int t = tok0 + 4 * c + i;
+      const bool in = kMulti ? (t < hi && t >= lo) : 4 * c + i < valid;
+      x[i] = in ? x[i] : -INFINITY;
+    }
+  }
+  if (valid < kBlock) {
 #pragma unroll
     for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::mask_v(r.v[nb], c, valid);
   }
@@ -394,22 +416,33 @@ struct PendingMerges {
   }
 };
 
+// Output row of column g = (query token qi, query head gq) of KV head h of
+// sequence b, in out [batch][q_len][n_q][D].
+// One query token (kMulti false): column g is query head g of the group.
+template <bool kMulti>
+__device__ inline size_t out_row(const DecodeArgs& a, int b, int h, int g) {
+  if constexpr (!kMulti) return static_cast<size_t>(b) * a.n_q + h * a.group + g;
+  const int qi = g / a.group;
+  const int gq = g - qi * a.group;
+  return (static_cast<size_t>(b) * a.q_len + qi) * a.n_q + h * a.group + gq;
+}
+
 // Writes one segment's normalised result o (lane (c, n): features
 // 16 nb + 4c .. +3 of head gb*16 + n) and its natural-log lse: the output rows
 // when the pair lies in a single chunk, otherwise this chunk's partial, which
 // the last of the pair's chunks to finish then merges (if counters are on).
-template <bool kOutBf16, int D>
+template <bool kOutBf16, int D, bool kMulti>
 __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pages, int seg_start, int chunk,
                              int C, const f32x4 (&o)[D / 16], float lse, int lane, PendingMerges& pending) {
   using O = Ops<kOutBf16, D>;
   const int c = lane >> 4;
   const uint32_t n = lane & 15;
-  const int g = gb * 16 + static_cast<int>(n);
+  const int g = gb * 16 + static_cast<int>(n);      // column (query token, query head)
   const int first_chunk = seg_start / C;
   const int last_chunk = (seg_start + n_pages - 1) / C;
   if (first_chunk == last_chunk) {
-    if (g >= a.group) return;
-    const size_t row = (static_cast<size_t>(b) * a.n_q + h * a.group + g) * D;
+    if (g >= a.cols) return;
+    const size_t row = out_row<kMulti>(a, b, h, g) * D;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, o[nb]);
     return;
@@ -419,8 +452,8 @@ __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pa
   // without any cache-wide write-back or invalidation.  The row resource's
   // range ends at the group's last head, which masks the lanes of heads past it.
   const size_t slot = static_cast<size_t>(chunk) + static_cast<size_t>(b) * a.n_kv + h;
-  const int rows = min(16, a.group - gb * 16);
-  const size_t row0 = slot * a.group + gb * 16;
+  const int rows = min(16, a.cols - gb * 16);
+  const size_t row0 = slot * a.cols + gb * 16;
   const __amdgpu_buffer_rsrc_t ro =
       __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, rows * D * 4, PKV_RSRC_WORD3);
 #pragma unroll
@@ -441,11 +474,11 @@ __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pa
 // gblk*16 + n).  Holds the query operand, the online-softmax state and, when
 // the segment ends with the pair's last page and the step appends, the new
 // token's K/V in the lanes that hold its slot.
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kMulti>
 struct Segment {
   using O = Ops<kBf16, D>;
   static constexpr int kTileBytes = kBlock * D * O::ES;
-  int b, h, gb, g, hq, len, n_pages, s_new;
+  int b, h, gb, g, hq, len, n_pages, s_new, fb, q_len, window, hi, lo;
   bool g_ok, append;
   u32x4 qreg[O::NK];
   u32x4 knew[O::NK];
@@ -453,26 +486,35 @@ struct Segment {
   float m, l;
   f32x4 acc[O::NV];
 
-  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, bool ends_pair, int gblk,
+  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, int fb_, bool ends_pair, int gblk,
                         int lane) {
     const int c = lane >> 4, n = lane & 15;
     b = b_;
     h = h_;
     n_pages = n_pages_;
+    fb = fb_;
     gb = gblk;
+    // Column g = (query token qi, query head gq) of this KV head.
     g = gblk * 16 + n;
-    g_ok = g < a.group;
-    hq = h * a.group + g;
+    g_ok = g < a.cols;
+    const int qi = kMulti ? g / a.group : 0;
+    const int gq = g - qi * a.group;
+    hq = h * a.group + gq;
     len = a.seq_lens[b];
-    // Query operand: lane (c, n) holds q[hq][(4i + c) * X .. +X) for each i.
-    const char* qb = static_cast<const char*>(a.q) +
-                     (static_cast<size_t>(b) * a.n_q + (g_ok ? hq : 0)) * D * O::ES;
+    q_len = kMulti ? a.q_len : 1;
+    window = kMulti ? a.window : 0;
+    hi = len - q_len + qi + 1;
+    lo = window > 0 ? max(0, hi - window) : 0;
+    // Query operand: lane (c, n) holds q[b][qi][hq][(4i + c) * X .. +X) for each i
+    // (columns past the group read row 0 and hold zeros).
+    const size_t qrow = g_ok ? (static_cast<size_t>(b) * q_len + qi) * a.n_q + hq : 0;
+    const char* qb = static_cast<const char*>(a.q) + qrow * D * O::ES;
 #pragma unroll
     for (int i = 0; i < O::NK; ++i) {
-      u32x4 t = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * i + c));
+      const u32x4 t = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * i + c));
       qreg[i] = g_ok ? t : u32x4{0u, 0u, 0u, 0u};
     }
-    m = -INFINITY;
+    m = kNoKeysMax;
     l = 0.f;
 #pragma unroll
     for (int nb = 0; nb < O::NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -538,9 +580,19 @@ struct Segment {
     }
   }
 
+  // Page j of the segment holds sequence tokens 16 (fb + j) .. +15.  Columns
+  // see keys [lo, hi): the smallest hi is len - q_len + 1, the largest lo is
+  // len - window.  One query token (kMulti false): every column sees [0, len)
+  // and only the last page is cut.
   __device__ void page(PageRegs<kBf16, D>& r, int j, float scale_log2, int lane) {
-    compute_page<kBf16, D>(r, j == n_pages - 1 ? len - kBlock * j : kBlock, qreg, scale_log2,
-                           lane >> 4, m, l, acc);
+    if constexpr (kMulti) {
+      const int tok0 = kBlock * (fb + j);
+      const bool cut = tok0 + kBlock > len - q_len + 1 || (window > 0 && tok0 < len - window);
+      compute_page<kBf16, D, true>(r, len - tok0, cut, tok0, hi, lo, qreg, scale_log2, lane >> 4, m, l, acc);
+    } else {
+      const int valid = len - kBlock * j;
+      compute_page<kBf16, D, false>(r, valid, valid < kBlock, 0, 0, 0, qreg, scale_log2, lane >> 4, m, l, acc);
+    }
   }
 
   // Normalises the segment's result in place and writes it (see
@@ -549,11 +601,11 @@ struct Segment {
                          PendingMerges& pending) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
-    const float inv = bad ? NAN : 1.0f / lt;
+    const float inv = bad ? NAN : (!kMulti || lt > 0.f ? 1.0f / lt : 0.f);   // no key seen: zero row, lse -inf
 #pragma unroll
     for (int nb = 0; nb < O::NV; ++nb) acc[nb] *= inv;
     const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
-    emit_segment<kBf16, D>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
+    emit_segment<kBf16, D, kMulti>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
   }
 };
 
@@ -588,14 +640,14 @@ __device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int g
   return (pm.n > 0 && o0 == pm.nparts0 - 1 ? 1 : 0) | (pm.n > 1 && o1 == pm.nparts1 - 1 ? 2 : 0);
 }
 
-template <bool kBf16, int D>
+template <bool kBf16, int D, bool kMulti>
 __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_chunk, int nparts, int lane) {
   using O = Ops<kBf16, D>;
   int32_t* ctr = merge_counter(a, b, h, gb);
   const uint32_t c = lane >> 4, n = lane & 15;
-  const int g = gb * 16 + static_cast<int>(n);
-  const bool g_ok = g < a.group;
-  const uint32_t G = a.group;
+  const int g = gb * 16 + static_cast<int>(n);   // column
+  const bool g_ok = g < a.cols;
+  const uint32_t G = a.cols;                      // partial rows per slot
   const size_t row0 = (static_cast<size_t>(first_chunk) + static_cast<size_t>(b) * a.n_kv + h) * G + gb * 16;
   // One resource per array over the nparts slots' rows of this head block;
   // part i is at scalar offset i * G rows.  Lanes past the group read
@@ -609,7 +661,7 @@ __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_
   // identity as the page loop).  Parts past nparts read zeros (outside the
   // range) and weigh nothing.  32 f32x4 registers of loads per group.
   constexpr int kMergeGroup = 32 / O::NV;
-  float mx = -INFINITY, den = 0.f;
+  float mx = kNoKeysMax, den = 0.f;   // parts that saw no key have lse -inf and weigh 0
   f32x4 o[O::NV];
 #pragma unroll
   for (int nb = 0; nb < O::NV; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -643,7 +695,7 @@ __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_
   }
   if (g_ok) {
     const float inv = 1.0f / den;
-    const size_t row = (static_cast<size_t>(b) * a.n_q + h * a.group + g) * D;
+    const size_t row = out_row<kMulti>(a, b, h, g) * D;
 #pragma unroll
     for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, o[nb] * inv);
   }
@@ -654,7 +706,7 @@ __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_
 // partials (no combine kernel runs for them): zeros for length 0, NaN for an
 // invalid length.  One wavefront; the empty sequences are found 64 at a time.
 __device__ void write_empty_rows(const DecodeArgs& a, const int32_t* s_prefix, int D, bool bf16, int lane) {
-  const size_t row_elems = static_cast<size_t>(a.n_q) * D;
+  const size_t row_elems = static_cast<size_t>(a.q_len) * a.n_q * D;   // all rows of one sequence
   for (int b0 = 0; b0 < a.batch; b0 += kWave) {
     const int bl = b0 + lane;
     const bool empty = bl < a.batch && s_prefix[bl + 1] == s_prefix[bl];
@@ -705,11 +757,11 @@ struct PageRegsQ8 {
 };
 
 // One segment of the 8-bit cache (same role and lane layout as Segment).
-template <int D>
+template <int D, bool kMulti>
 struct SegmentQ8 {
   static constexpr int NQ = D / 32;   // fp16 query registers, one per 32-feature MFMA
   static constexpr int NV = D / 16;
-  int b, h, gb, g, hq, len, n_pages;
+  int b, h, gb, g, hq, len, n_pages, fb, q_len, window, hi, lo;
   bool g_ok, append;
   u32x4 qh[NQ];
   float qsum, m, l, corr;
@@ -719,18 +771,26 @@ struct SegmentQ8 {
   // 16 (4j + c) + 8e .. +7 of head n: the features the K codes of load j
   // bring to lanes of group c.  qsum = sum of the fp16 query features of the
   // lane's head (the same fp16 values the MFMAs multiply).
-  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, bool, int gblk, int lane) {
+  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, int fb_, bool, int gblk, int lane) {
     const int c = lane >> 4, n = lane & 15;
     b = b_;
     h = h_;
     n_pages = n_pages_;
+    fb = fb_;
     gb = gblk;
-    g = gblk * 16 + n;
-    g_ok = g < a.group;
-    hq = h * a.group + g;
+    g = gblk * 16 + n;                 // column (query token qi, query head gq)
+    g_ok = g < a.cols;
+    const int qi = kMulti ? g / a.group : 0;
+    const int gq = g - qi * a.group;
+    hq = h * a.group + gq;
     len = a.seq_lens[b];
+    q_len = kMulti ? a.q_len : 1;
+    window = kMulti ? a.window : 0;
+    hi = len - q_len + qi + 1;
+    lo = window > 0 ? max(0, hi - window) : 0;
     append = false;
-    const char* qb = static_cast<const char*>(a.q) + (static_cast<size_t>(b) * a.n_q + (g_ok ? hq : 0)) * D * 2;
+    const size_t qrow = g_ok ? (static_cast<size_t>(b) * q_len + qi) * a.n_q + hq : 0;
+    const char* qb = static_cast<const char*>(a.q) + qrow * D * 2;
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
@@ -751,7 +811,7 @@ struct SegmentQ8 {
     part = g_ok ? part : 0.f;
     qsum = part + __shfl_xor(part, 16);
     qsum += __shfl_xor(qsum, 32);
-    m = -INFINITY;
+    m = kNoKeysMax;
     l = 0.f;
     corr = 0.f;
 #pragma unroll
@@ -760,7 +820,9 @@ struct SegmentQ8 {
 
   __device__ void page(PageRegsQ8<D>& r, int j, float scale_log2, int lane) {
     const int c = lane >> 4;
-    const int valid = j == n_pages - 1 ? len - kBlock * j : kBlock;
+    const int tok0 = kBlock * ((kMulti ? fb : 0) + j);
+    const bool cut = kMulti ? tok0 + kBlock > len - q_len + 1 || (window > 0 && tok0 < len - window)
+                            : tok0 + kBlock > len;
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < PageRegsQ8<D>::NK; ++i) {
@@ -779,7 +841,8 @@ struct SegmentQ8 {
     bool in[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      in[i] = 4 * c + i < valid;
+      const int t = tok0 + 4 * c + i;
+      in[i] = !cut || (kMulti ? (t < hi && t >= lo) : t < len);   // hi <= len: slots past the sequence are out too
       const float sc = r.ks[i] * (raw[i] - (kCodeBias + r.kz[i]) * qsum) * scale_log2;
       x[i] = in[i] ? sc : -INFINITY;
     }
@@ -820,40 +883,47 @@ struct SegmentQ8 {
     lt += __shfl_xor(lt, 32);
     float ct = corr + __shfl_xor(corr, 16);
     ct += __shfl_xor(ct, 32);
-    const float inv = bad ? NAN : 1.0f / lt;
+    const float inv = bad ? NAN : (!kMulti || lt > 0.f ? 1.0f / lt : 0.f);   // no key seen: zero row, lse -inf
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb) acc[nb] = (acc[nb] - ct) * inv;
     const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
-    emit_segment<true, D>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
+    emit_segment<true, D, kMulti>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
   }
 };
 
 // Position in the flattened (sequence, KV head, page) order of all pages:
 // flat index f, sequence b (with pb = pages before b and n = pages of b),
 // KV head h, page j of the pair.
+template <bool kMulti>
 struct FlatCursor {
-  int f, b, h, j, n, pb;
-  __device__ void seek(const int32_t* s_prefix, int batch, int n_kv, int f0) {
+  int f, b, h, j, n, pb, fb;   // fb: block of the pair's first page (window start; 0 for one query token)
+  __device__ static int first_block_of(const DecodeArgs& a, int b) {
+    if constexpr (!kMulti) return 0;
+    return a.window > 0 ? uni(first_block(a.seq_lens[b], a.q_len, a.window)) : 0;
+  }
+  __device__ void seek(const DecodeArgs& a, const int32_t* s_prefix, int f0) {
     f = f0;
-    b = uni(find_seq(s_prefix, batch, n_kv, f0));
+    b = uni(find_seq(s_prefix, a.batch, a.n_kv, f0));
     pb = uni(s_prefix[b]);
     n = uni(s_prefix[b + 1]) - pb;
-    const int off = f0 - n_kv * pb;
+    fb = first_block_of(a, b);
+    const int off = f0 - a.n_kv * pb;
     h = off / n;
     j = off - h * n;
   }
   // Next page; must not be called on the last page of all.
-  __device__ void next(const int32_t* s_prefix, int n_kv) {
+  __device__ void next(const DecodeArgs& a, const int32_t* s_prefix) {
     ++f;
     if (++j == n) {
       j = 0;
-      if (++h == n_kv) {
+      if (++h == a.n_kv) {
         h = 0;
         do {
           ++b;
           pb = uni(s_prefix[b]);
           n = uni(s_prefix[b + 1]) - pb;
         } while (n == 0);
+        fb = first_block_of(a, b);
       }
     }
   }
@@ -876,16 +946,17 @@ constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
 #endif
 // Cache policies of the split kernel: what one (page, KV head) holds, how a
 // wavefront loads it, and the segment type that consumes it.
-template <bool kBf16, int D>
-struct DenseKV {                       // bf16 or fp32 K/V, the q and out dtype
+template <bool kBf16, int D, bool kMulti_>
+struct DenseKV {                       // bf16 or fp32 K/V, the q and out dtype; kMulti: q_len > 1 or a window
   static constexpr int kHeadDim = D;
   static constexpr bool kOutBf16 = kBf16;
   static constexpr bool kFusedAppend = true;
+  static constexpr bool kMulti = kMulti_;
   static constexpr int kTileK = kBlock * D * Ops<kBf16, D>::ES;
   static constexpr int kWavesPerEu = kSplitWavesPerEu<kBf16, D>;
   static constexpr int kWavesPerEuGrouped = (kBf16 || D == 64) ? PKV_GROUPED_WAVES_PER_EU : 1;
   using Regs = PageRegs<kBf16, D>;
-  using Seg = Segment<kBf16, D>;
+  using Seg = Segment<kBf16, D, kMulti_>;
   template <int kAux>
   __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -900,12 +971,13 @@ struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
   static constexpr int kHeadDim = D;
   static constexpr bool kOutBf16 = true;
   static constexpr bool kFusedAppend = false;
+  static constexpr bool kMulti = false;
   static constexpr int kTileK = kBlock * D;        // bytes of one K (or V) code tile
   static constexpr int kMetaBytes = 4 * kBlock * 4;
   static constexpr int kWavesPerEu = 2;
   static constexpr int kWavesPerEuGrouped = PKV_GROUPED_WAVES_PER_EU;
   using Regs = PageRegsQ8<D>;
-  using Seg = SegmentQ8<D>;
+  using Seg = SegmentQ8<D, false>;   // one query token, no window
   template <int kAux>
   __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -954,7 +1026,7 @@ split_kernel(DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
   int32_t* s_wsum = smem + a.batch + 1;
-  build_prefix(a.seq_lens, a.batch, a.max_blocks, s_prefix, s_wsum);
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, a.q_len, a.window, s_prefix, s_wsum);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uni(threadIdx.x / kWave);
@@ -963,7 +1035,7 @@ split_kernel(DecodeArgs a) {
   if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, KV::kOutBf16, lane);
   const int chunk = blockIdx.x * (kWavesPerGroup / kNG) + wave / kNG;
   const int gblk = wave % kNG;
-  if (chunk >= a.n_items || gblk * 16 >= a.group) return;
+  if (chunk >= a.n_items || gblk * 16 >= a.cols) return;
   const int total = uni(a.n_kv * s_prefix[a.batch]);
   const int C = chunk_pages(total, a.n_items, a.min_chunk);
   const int64_t f64 = static_cast<int64_t>(chunk) * C;
@@ -980,26 +1052,26 @@ split_kernel(DecodeArgs a) {
   // ---- loader.  Past the chunk's end the loads are issued with an empty
   // range, so every ring step issues the same instructions but nothing is
   // read; a page id outside the pool is never dereferenced either.
-  FlatCursor ld;
-  ld.seek(s_prefix, a.batch, a.n_kv, f0);
+  FlatCursor<KV::kMulti> ld;
+  ld.seek(a, s_prefix, f0);
   int issued = 0;
   Regs buf[kBufs];
   int page_of[kBufs];   // page id of each buffer (scalar), for the compute side
   auto issue = [&](Regs& r, int& pg_out) {
     const bool in = issued < cnt;
-    const int pg = bt_row(ld.b)[ld.j];
+    const int pg = bt_row(ld.b)[ld.fb + ld.j];
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     KV::template load<kAux>(r, a, static_cast<size_t>(ok ? pg : 0) * a.n_kv + ld.h, in && ok, lane);
     pg_out = pg;
     if (in) {
       ++issued;
-      if (issued < cnt) ld.next(s_prefix, a.n_kv);
+      if (issued < cnt) ld.next(a, s_prefix);
     }
   };
 
   // ---- compute.
-  FlatCursor cp;
-  cp.seek(s_prefix, a.batch, a.n_kv, f0);
+  FlatCursor<KV::kMulti> cp;
+  cp.seek(a, s_prefix, f0);
   typename KV::Seg seg;
   PendingMerges pending;
   bool open = false, bad = false;
@@ -1011,7 +1083,7 @@ split_kernel(DecodeArgs a) {
     }
     if (!open) {
       const bool ends_pair = cp.j + (cnt - p) >= cp.n;
-      seg.begin(a, cp.b, cp.h, cp.n, ends_pair, gblk, lane);
+      seg.begin(a, cp.b, cp.h, cp.n, cp.fb, ends_pair, gblk, lane);
       seg_start = a.n_kv * cp.pb + cp.h * cp.n;
       bad = false;
       open = true;
@@ -1048,7 +1120,7 @@ split_kernel(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (p < cnt) {
         compute(buf[s], page_of[s], p);
-        if (p + 1 < cnt) cp.next(s_prefix, a.n_kv);
+        if (p + 1 < cnt) cp.next(a, s_prefix);
       }
       ++p;
     }
@@ -1057,9 +1129,9 @@ split_kernel(DecodeArgs a) {
   if (pending.n > 0) {
     const int last = arrive(a, pending, gblk, lane);
     if (last & 1)
-      merge_pair<KV::kOutBf16, D>(a, pending.b0, pending.h0, gblk, pending.first0, pending.nparts0, lane);
+      merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b0, pending.h0, gblk, pending.first0, pending.nparts0, lane);
     if (last & 2)
-      merge_pair<KV::kOutBf16, D>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
+      merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
   }
 }
 
@@ -1077,12 +1149,14 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   __shared__ f32x4 s_acc[2 * 256];
   __shared__ float s_den[256];
   const int32_t* s_prefix = a.prefix;   // stored by the split kernel
-  const int G = a.group;
-  const int row = blockIdx.x;                 // b * n_q + hq
-  const int b = row / a.n_q;
-  const int hq = row - b * a.n_q;
-  const int h = hq / G;
-  const int g = hq - h * G;
+  const int G = a.cols;                       // partial rows per slot
+  const int row = blockIdx.x;                 // (b * q_len + qi) * n_q + hq
+  const int b = row / (a.q_len * a.n_q);
+  const int bq = row - b * a.q_len * a.n_q;
+  const int qi = bq / a.n_q;
+  const int hq = bq - qi * a.n_q;
+  const int h = hq / a.group;
+  const int g = qi * a.group + (hq - h * a.group);   // column
   const int pair = b * a.n_kv + h;
   const int n = s_prefix[b + 1] - s_prefix[b];
   const size_t row0 = static_cast<size_t>(row) * D;
@@ -1348,23 +1422,26 @@ constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
 #define PKV_Q8_PREFETCH_PAGES 2
 #endif
 
-template <int kNG>
+template <int kNG, bool kMulti>
 SplitFn split_fn_ng(int dtype, int head_dim, bool q8) {
   constexpr int kDepth = kNG == 1 ? kPrefetchPages : PKV_GROUPED_DEPTH;
   if (q8)
     return head_dim == 128 ? split_kernel<Q8KV<128>, PKV_Q8_PREFETCH_PAGES, kNG>
                            : split_kernel<Q8KV<64>, PKV_Q8_PREFETCH_PAGES, kNG>;
   if (dtype == PKV_BF16)
-    return head_dim == 128 ? split_kernel<DenseKV<true, 128>, kDepth, kNG>
-                           : split_kernel<DenseKV<true, 64>, kDepth, kNG>;
-  return head_dim == 128 ? split_kernel<DenseKV<false, 128>, 1, kNG> : split_kernel<DenseKV<false, 64>, 1, kNG>;
+    return head_dim == 128 ? split_kernel<DenseKV<true, 128, kMulti>, kDepth, kNG>
+                           : split_kernel<DenseKV<true, 64, kMulti>, kDepth, kNG>;
+  return head_dim == 128 ? split_kernel<DenseKV<false, 128, kMulti>, 1, kNG>
+                         : split_kernel<DenseKV<false, 64, kMulti>, 1, kNG>;
 }
 
-SplitFn split_fn(int dtype, int head_dim, int group, bool q8) {
-  switch (waves_per_chunk(group)) {
-    case 1: return split_fn_ng<1>(dtype, head_dim, q8);
-    case 2: return split_fn_ng<2>(dtype, head_dim, q8);
-    default: return split_fn_ng<4>(dtype, head_dim, q8);
+// cols: MFMA columns per KV head (query tokens x query heads); multi: more
+// than one query token or a sliding window (dense caches only).
+SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
+  switch (waves_per_chunk(cols)) {
+    case 1: return multi ? split_fn_ng<1, true>(dtype, head_dim, q8) : split_fn_ng<1, false>(dtype, head_dim, q8);
+    case 2: return multi ? split_fn_ng<2, true>(dtype, head_dim, q8) : split_fn_ng<2, false>(dtype, head_dim, q8);
+    default: return multi ? split_fn_ng<4, true>(dtype, head_dim, q8) : split_fn_ng<4, false>(dtype, head_dim, q8);
   }
 }
 
@@ -1378,7 +1455,7 @@ int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
       &per_cu,
-      reinterpret_cast<const void*>(split_fn(dtype, head_dim, group, dtype == PKV_U8)),
+      reinterpret_cast<const void*>(split_fn(dtype, head_dim, group, dtype == PKV_U8, false)),
       kWave * kWavesPerGroup, lds);
   if (e != hipSuccess) return hip_fail("hipOccupancyMaxActiveBlocksPerMultiprocessor", e);
   if (per_cu < 1) per_cu = 1;
@@ -1438,11 +1515,18 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                   const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                   int32_t block_size, float scale, void* out, void* stream, int32_t batch,
                   int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
-                  size_t workspace_bytes, const pkv_decode_opts* opts) {
+                  size_t workspace_bytes, const pkv_decode_opts* opts, int32_t q_len = 1,
+                  int32_t window = 0) {
   int st = check_decode_shapes(fn, n_q_heads, n_kv_heads, head_dim, block_size, batch,
                                max_blocks_per_seq, num_pages, dtype);
   if (st != PKV_OK) return st;
   std::string f(fn);
+  if (q_len < 1 || window < 0)
+    return fail(PKV_ERR_INVALID_ARG, f + ": q_len must be >= 1 and window >= 0");
+  if (static_cast<int64_t>(q_len) * (n_q_heads / n_kv_heads) > kMaxGroup)
+    return fail(PKV_ERR_UNSUPPORTED, f + ": q_len * (n_q_heads / n_kv_heads) above 64");
+  if (q_len > 1 && k_new != nullptr)
+    return fail(PKV_ERR_INVALID_ARG, f + ": the fused append takes one token per sequence");
   if (batch == 0) return ok();
   if (!seq_lens || !out || !workspace || !aligned(seq_lens, 4) || !aligned(out, 16) ||
       !aligned(workspace, 256))
@@ -1462,13 +1546,14 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
       (k_new && (!aligned(k_new, 16) || !aligned(v_new, 4))))
     return fail(PKV_ERR_INVALID_ARG, f + ": k_new/v_new must both be given, 16/4-byte aligned");
   const int group = n_q_heads / n_kv_heads;
+  const int cols = q_len * group;   // MFMA columns per KV head: (query token, query head)
   Resolved r;
-  st = resolve_opts(dtype, head_dim, group, batch, max_blocks_per_seq, n_kv_heads, opts, &r);
+  st = resolve_opts(dtype, head_dim, cols, batch, max_blocks_per_seq, n_kv_heads, opts, &r);
   if (st != PKV_OK) return st;
   if (do_split && r.lds > kMaxLdsBytes)
     return fail(PKV_ERR_UNSUPPORTED, f + ": batch too large for this group size (LDS " +
                                          std::to_string(r.lds) + " bytes)");
-  const int64_t need = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
+  const int64_t need = pkv_decode_workspace_bytes(batch, n_q_heads * q_len, n_kv_heads, head_dim, r.n_items);
   if (need < 0) return static_cast<int>(need);
   if (workspace_bytes < static_cast<size_t>(need))
     return fail(PKV_ERR_WORKSPACE, f + ": workspace needs " + std::to_string(need) + " bytes");
@@ -1486,11 +1571,14 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.seq_lens = seq_lens;
   a.out = out;
   a.part_o = static_cast<float*>(workspace);
-  a.part_lse = static_cast<float*>(workspace) + slots * group * head_dim;
+  a.part_lse = static_cast<float*>(workspace) + slots * cols * head_dim;
   a.batch = batch;
   a.n_q = n_q_heads;
   a.n_kv = n_kv_heads;
   a.group = group;
+  a.q_len = q_len;
+  a.window = window;
+  a.cols = cols;
   a.max_blocks = max_blocks_per_seq;
   a.num_pages = num_pages;
   a.n_items = r.n_items;
@@ -1504,25 +1592,26 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   const bool fuse = do_split && do_combine && r.combine_mode == 0;
   const int64_t max_parts = (static_cast<int64_t>(max_blocks_per_seq) + r.min_chunk - 1) / r.min_chunk + 1;
   a.counters = fuse ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                                 decode_counters_offset(batch, group, n_kv_heads, head_dim,
+                                                 decode_counters_offset(batch, cols, n_kv_heads, head_dim,
                                                                         r.n_items))
                     : nullptr;
   a.fuse_max_parts = kFuseMaxParts;
   a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                        decode_prefix_offset(batch, group, n_kv_heads, head_dim, r.n_items));
+                                        decode_prefix_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
     const int chunks_per_group = kWavesPerGroup / r.wpc;
     const int grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
-    hipLaunchKernelGGL(split_fn(dtype, head_dim, group, q8), dim3(grid),
+    const bool multi = q_len > 1 || window > 0;
+    hipLaunchKernelGGL(split_fn(dtype, head_dim, cols, q8, multi), dim3(grid),
                        dim3(kWave * kWavesPerGroup), r.lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
   }
   if (run_combine) {
     auto fn_c = dtype == PKV_F32 ? combine_kernel<false> : combine_kernel<true>;
-    hipLaunchKernelGGL(fn_c, dim3(batch * n_q_heads), dim3(256), 0, s, a, head_dim);
+    hipLaunchKernelGGL(fn_c, dim3(batch * q_len * n_q_heads), dim3(256), 0, s, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
@@ -1662,6 +1751,17 @@ int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t
                             seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, 1.0f, out,
                             stream, batch, max_blocks_per_seq, 1, dtype,
                             const_cast<void*>(workspace), workspace_bytes, opts);
+}
+
+int pkv_paged_decode_multi(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                           const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t q_len, int32_t window, float scale, void* out,
+                           void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                           int32_t dtype, void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts) {
+  return pkv::decode_common(true, true, "pkv_paged_decode_multi", q, nullptr, nullptr, k_pages, v_pages, nullptr,
+                            block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out, stream,
+                            batch, max_blocks_per_seq, num_pages, dtype, workspace, workspace_bytes, opts, q_len,
+                            window);
 }
 
 int pkv_paged_decode_attn_q8(const void* q, const void* k_codes, const void* v_codes, const void* meta,

@@ -39,6 +39,21 @@ __host__ __device__ inline int pages_of_len(int64_t len, int64_t max_blocks) {
   return static_cast<int>((len + kBlock - 1) / kBlock);
 }
 
+// Several query tokens per sequence (the last q_len cached tokens, each
+// attending causally, optionally only to the last `window` keys): the first
+// block any of them attends, and the pages from there to the sequence's end.
+// A length below q_len is invalid (no pages; the rows become NaN).
+__host__ __device__ inline int first_block(int64_t len, int64_t q_len, int64_t window) {
+  if (window <= 0) return 0;
+  const int64_t lo = len - q_len + 1 - window;   // window start of the first query token
+  return lo <= 0 ? 0 : static_cast<int>(lo / kBlock);
+}
+__host__ __device__ inline int pages_of_range(int64_t len, int64_t max_blocks, int64_t q_len, int64_t window) {
+  if (len < q_len) return 0;
+  const int n = pages_of_len(len, max_blocks);
+  return n == 0 ? 0 : n - first_block(len, q_len, window);
+}
+
 // Wavefronts that share one chunk: one per 16 query heads, rounded up to a power of two.
 __host__ __device__ inline int waves_per_chunk(int group) {
   int gb = (group + 15) / 16;

@@ -150,6 +150,16 @@ def copy_blocks(k_pages, v_pages, src_pages, dst_pages, stream=None) -> None:
                               _dtype_code(k_pages), _stream(stream)), "pkv_copy_blocks")
 
 
+def kv_append_tokens(k_new, v_new, k_pages, v_pages, block_table, positions, stream=None) -> None:
+    """Append q_len tokens per sequence: k_new, v_new [B][q_len][Hkv][D] at
+    positions[b] + i (one kv_append launch per token)."""
+    import torch
+    T = k_new.shape[1]
+    for i in range(T):
+        kv_append(k_new[:, i].contiguous(), v_new[:, i].contiguous(), k_pages, v_pages, block_table,
+                  (positions + i).to(torch.int32), stream)
+
+
 def q8_pool_shapes(num_pages: int, n_kv_heads: int, head_dim: int):
     """Shapes of the 8-bit cache's (k_codes uint8, v_codes uint8, meta float32)."""
     return ((num_pages, n_kv_heads, head_dim // 16, BLOCK_SIZE, 16), (num_pages, n_kv_heads, head_dim, BLOCK_SIZE),
@@ -229,6 +239,25 @@ class Decoder:
                                   BLOCK_SIZE, max_blocks, _ptr(out), _dtype_code(out),
                                   _opts(self.n_items, self.min_chunk_pages, self.combine_mode), _stream(stream)),
               "pkv_lse_combine")
+
+    def attn_multi(self, q, k_pages, v_pages, block_table, seq_lens, q_len: int, scale, out, window: int = 0,
+                   stream=None):
+        """Attention of the last q_len cached tokens of each sequence (causal,
+        optional sliding window).  q, out: [B][q_len][Hq][D].  Build the
+        Decoder with n_q_heads * q_len query heads (the workspace is sized by
+        columns per KV head)."""
+        if not (q.dtype == k_pages.dtype == v_pages.dtype == out.dtype) or _dtype_code(q) == PKV_U8:
+            raise TypeError("decode_multi: q, k_pages, v_pages and out must share dtype bf16 or float32")
+        B, T, Hq, D = q.shape
+        if T != q_len or self.shape[1] != Hq * q_len:
+            raise ValueError("q must be [B][q_len][Hq][D] and the Decoder built for Hq * q_len heads")
+        check(lib.pkv_paged_decode_multi(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
+                                         Hq, k_pages.shape[1], D, BLOCK_SIZE, q_len, window, float(scale), _ptr(out),
+                                         _stream(stream), B, block_table.shape[1], k_pages.shape[0], _dtype_code(q),
+                                         _ptr(self.workspace), self.workspace.numel(),
+                                         _opts(self.n_items, self.min_chunk_pages, self.combine_mode)),
+              "pkv_paged_decode_multi")
+        return out
 
     def _q8_args(self, q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream):
         import torch
