@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="llama2_7b_mha")
     ap.add_argument("--n-items", type=int, default=0)
     ap.add_argument("--min-chunk", type=int, default=0)
+    ap.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
+                    help="work schedule: 0 the library's default, 1 static, 2 dynamic")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
@@ -265,7 +267,8 @@ def main():
     dt = torch.uint8 if u8 else W.torch_dtype(w)
     # the multi-token decode runs q_len x Hq query columns: the Decoder is built for them
     dec = pkv.Decoder(w.batch, w.n_q_heads * T, w.n_kv_heads, w.head_dim, dt, S["mb"], args.n_items,
-                      args.min_chunk, device=device, combine_mode=1 if args.separate_combine else 0)
+                      args.min_chunk, device=device, combine_mode=1 if args.separate_combine else 0,
+                      schedule=args.schedule)
     # One kernel per layer when every pair can be merged inside the decode
     # kernel (a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks).
     # (the library's rule: a pair spans at most ceil(max_blocks / min_chunk) + 1
@@ -415,6 +418,7 @@ def main():
             "head_dim": w.head_dim, "block_size": 16, "layers": n_layers,
             "attended_tokens": int(S["att"].sum()), "kv_bytes_per_step": kv_step,
             "accumulate": "fp32", "n_items": dec.n_items, "min_chunk_pages": dec.min_chunk_pages,
+            "schedule": {1: "static", 2: "dynamic"}.get(dec.schedule, dec.schedule),
             "pool_copies": len(layers),
             "append": "quantizing kernel" if u8 else ("separate kernel" if args.unfused else "fused into the decode kernel"),
             "merge": "combine kernel" if not one_kernel else "inside the decode kernel",

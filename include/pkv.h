@@ -189,21 +189,37 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  * bytes (n_items after defaults are applied).  Layout: the partials, then
  * (256-byte aligned) 16 * batch * n_kv_heads bytes of arrival counters, then
  * 4 * (batch + 1) bytes where the split kernel stores the per-sequence page
- * prefix for the combine kernel.  Partials and prefix are overwritten by
- * every call; the counters must be zero before the first full call that uses
- * the workspace (e.g. a zero-filled allocation), and every call leaves them
- * zero.  Calls that overlap in time must not share a workspace.
- * opts (nullable): n_items <= 0 means as many chunks as the device holds at
- * once (resident wavefronts divided by the wavefronts per chunk);
+ * prefix for the combine kernel, then one int32 chunk counter for the
+ * dynamic schedule.  Partials and prefix are overwritten by every call; the
+ * counters must be zero before the first call that uses the workspace (e.g.
+ * a zero-filled allocation), and every call leaves them zero.  Calls that
+ * overlap in time must not share a workspace.
+ * opts (nullable): n_items <= 0 means, for groups of at most 16 query heads
+ * (one wavefront per chunk), one chunk per wavefront of one workgroup per CU
+ * (4 x CUs), and for larger groups as many chunks as the device holds at
+ * once (resident wavefronts divided by the wavefronts per chunk); under the
+ * dynamic schedule, 8 chunks per wavefront of one workgroup per CU;
  * min_chunk_pages <= 0 means 64 pages (groups <= 16) or 32 (larger groups,
- * and the 8-bit cache, dtype PKV_U8, at every group size);
+ * and the 8-bit cache, dtype PKV_U8, at every group size), 16 under the
+ * dynamic schedule;
  * combine_mode 0 merges in the decode kernel where the bound above allows,
- * 1 always merges with the separate combine kernel (counters untouched).
+ * 1 always merges with the separate combine kernel (counters untouched);
+ * schedule (pkv_schedule) chooses how chunks are given to wavefronts.  The
+ * chunks, and so the results bit for bit, depend only on n_items and
+ * min_chunk_pages, not on the schedule.  The dynamic schedule takes at most
+ * 16 columns per KV head (query heads per KV head times query tokens).
  * ------------------------------------------------------------------------ */
+typedef enum {
+  PKV_SCHEDULE_AUTO = 0,     /* the library's choice (currently static) */
+  PKV_SCHEDULE_STATIC = 1,   /* chunk i to wavefront (group) i, fixed at launch */
+  PKV_SCHEDULE_DYNAMIC = 2   /* one workgroup per CU, chunks handed out as wavefronts free up */
+} pkv_schedule;
+
 typedef struct pkv_decode_opts {
   int32_t n_items;
   int32_t min_chunk_pages;
   int32_t combine_mode;
+  int32_t schedule;          /* pkv_schedule */
 } pkv_decode_opts;
 
 int pkv_paged_decode_attn(const void* q, const void* k_pages, const void* v_pages,

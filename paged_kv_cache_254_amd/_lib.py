@@ -19,6 +19,9 @@ PKV_ERR_EXISTS = -7
 PKV_F32 = 0
 PKV_BF16 = 1
 PKV_U8 = 2
+PKV_SCHEDULE_AUTO = 0
+PKV_SCHEDULE_STATIC = 1
+PKV_SCHEDULE_DYNAMIC = 2
 
 
 class PkvError(RuntimeError):
@@ -29,7 +32,7 @@ class PkvError(RuntimeError):
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("n_items", ctypes.c_int32), ("min_chunk_pages", ctypes.c_int32),
-                ("combine_mode", ctypes.c_int32)]
+                ("combine_mode", ctypes.c_int32), ("schedule", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):

@@ -227,7 +227,7 @@ int64_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_k
       n_q_heads % n_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_decode_workspace_bytes: bad argument");
   const int64_t group = n_q_heads / n_kv_heads;
-  return pkv::decode_prefix_offset(batch, group, n_kv_heads, head_dim, n_items) + (batch + 1) * 4;
+  return pkv::decode_workspace_end(batch, group, n_kv_heads, head_dim, n_items);
 }
 
 int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,

@@ -220,6 +220,8 @@ struct DecodeArgs {
   // Per-sequence page prefix [batch + 1] in the workspace: written by the
   // split kernel's first workgroup, read by the combine kernel.
   int32_t* prefix;
+  // Dynamic schedule: the counter chunks are taken from (zero between launches).
+  int32_t* work;
 };
 
 // Pages per sequence (those from its first attended block, see
@@ -416,6 +418,19 @@ struct PendingMerges {
   }
 };
 
+// The same for the dynamic schedule, where a wavefront takes any number of
+// chunks: the pairs are listed in this wavefront's slice of LDS (b, h, first
+// chunk, parts) until they are counted, at the end of its work or when the
+// list is full.
+struct PendingList {
+  int4* list;   // kMaxPending entries
+  int n = 0;
+  __device__ void add(int b, int h, int first, int nparts) {
+    if ((threadIdx.x & (kWave - 1)) == 0) list[n] = make_int4(b, h, first, nparts);
+    ++n;
+  }
+};
+
 // Output row of column g = (query token qi, query head gq) of KV head h of
 // sequence b, in out [batch][q_len][n_q][D].
 // One query token (kMulti false): column g is query head g of the group.
@@ -431,9 +446,9 @@ __device__ inline size_t out_row(const DecodeArgs& a, int b, int h, int g) {
 // 16 nb + 4c .. +3 of head gb*16 + n) and its natural-log lse: the output rows
 // when the pair lies in a single chunk, otherwise this chunk's partial, which
 // the last of the pair's chunks to finish then merges (if counters are on).
-template <bool kOutBf16, int D, bool kMulti>
+template <bool kOutBf16, int D, bool kMulti, class Pending>
 __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pages, int seg_start, int chunk,
-                             int C, const f32x4 (&o)[D / 16], float lse, int lane, PendingMerges& pending) {
+                             int C, const f32x4 (&o)[D / 16], float lse, int lane, Pending& pending) {
   using O = Ops<kOutBf16, D>;
   const int c = lane >> 4;
   const uint32_t n = lane & 15;
@@ -597,8 +612,9 @@ struct Segment {
 
   // Normalises the segment's result in place and writes it (see
   // emit_segment); the segment is closed afterwards.
+  template <class Pending>
   __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
-                         PendingMerges& pending) {
+                         Pending& pending) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = bad ? NAN : (!kMulti || lt > 0.f ? 1.0f / lt : 0.f);   // no key seen: zero row, lse -inf
@@ -640,7 +656,7 @@ __device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int g
   return (pm.n > 0 && o0 == pm.nparts0 - 1 ? 1 : 0) | (pm.n > 1 && o1 == pm.nparts1 - 1 ? 2 : 0);
 }
 
-template <bool kBf16, int D, bool kMulti>
+template <bool kBf16, int D, bool kMulti, int kGroupParts = 0>
 __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_chunk, int nparts, int lane) {
   using O = Ops<kBf16, D>;
   int32_t* ctr = merge_counter(a, b, h, gb);
@@ -659,8 +675,9 @@ __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_
   // One pass, kMergeGroup parts per round trip: all their loads are issued
   // before any is used, and the running maximum rescales the sums (the same
   // identity as the page loop).  Parts past nparts read zeros (outside the
-  // range) and weigh nothing.  32 f32x4 registers of loads per group.
-  constexpr int kMergeGroup = 32 / O::NV;
+  // range) and weigh nothing.  32 f32x4 registers of loads per group by
+  // default; fewer where the caller holds other live registers.
+  constexpr int kMergeGroup = kGroupParts > 0 ? kGroupParts : 32 / O::NV;
   float mx = kNoKeysMax, den = 0.f;   // parts that saw no key have lse -inf and weigh 0
   f32x4 o[O::NV];
 #pragma unroll
@@ -877,8 +894,9 @@ struct SegmentQ8 {
     }
   }
 
+  template <class Pending>
   __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
-                         PendingMerges& pending) {
+                         Pending& pending) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     float ct = corr + __shfl_xor(corr, 16);
@@ -1133,6 +1151,238 @@ split_kernel(DecodeArgs a) {
     if (last & 2)
       merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
   }
+}
+
+// Counts the arrivals of the listed pairs after this wavefront's partial
+// stores have completed (one lane per pair, up to 64 atomics in flight
+// together), merges the pairs for which it arrived last, and empties the
+// list.  kGroupParts: partials per round trip of the merge (0: the default).
+template <bool kOutBf16, int D, bool kMulti, int kGroupParts>
+__device__ void flush_pending(const DecodeArgs& a, PendingList& pl, int lane) {
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  for (int base = 0; base < pl.n; base += kWave) {
+    const int i = base + lane;
+    const bool in = i < pl.n;
+    const int4 e = in ? pl.list[i] : make_int4(0, 0, 0, 0);
+    int old = -1;
+    if (in)
+      old = __hip_atomic_fetch_add(merge_counter(a, e.x, e.y, 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t last = __builtin_amdgcn_ballot_w64(in && old == e.w - 1);
+    while (last != 0) {
+      const int k = __builtin_ctzll(last);
+      last &= last - 1;
+      const int4 m = pl.list[base + k];
+      merge_pair<kOutBf16, D, kMulti, kGroupParts>(a, uni(m.x), uni(m.y), 0, uni(m.z), uni(m.w), lane);
+    }
+  }
+  pl.n = 0;
+}
+
+// Split-KV decode with a dynamic schedule, for at most 16 columns per KV
+// head: one workgroup of four wavefronts per CU, one wavefront per chunk at a
+// time.  The chunks are those of split_kernel (fixed by n_items and
+// min_chunk), so every partial and every merge is the same whichever
+// wavefront computes it, and results stay run-to-run identical; only the
+// assignment is dynamic.  Wavefront w starts on chunk w and then takes
+// chunks W, W + 1, ... (W wavefronts in the grid) from a counter in the
+// workspace, requesting the next one as it starts loading the current one.
+// Wavefronts that run faster (CUs differ, and so do XCDs) take more chunks,
+// so all of them end at about the same time.  The loader moves from one
+// chunk to the next without draining its ring; the compute side follows the
+// chunk id each ring buffer carries.  Arrivals of split pairs are counted
+// once the wavefront has no more work (or its pending list is full), so no
+// wait for its own partial stores stalls the stream of tile loads.
+// One wavefront per SIMD is all the grid asks for, so the kernel may use the
+// whole register file (512 per lane, accumulation registers included).
+template <class KV, int kDepth>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(1)))
+dyn_kernel(DecodeArgs a) {
+  constexpr int D = KV::kHeadDim;
+  constexpr int kTile = KV::kTileK;
+  constexpr int kBufs = kDepth + 1;
+  using Regs = typename KV::Regs;
+  constexpr int kAux = PKV_KV_LOAD_AUX;
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  int32_t* s_wsum = smem + a.batch + 1;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, a.q_len, a.window, s_prefix, s_wsum);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uni(threadIdx.x / kWave);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.prefix[i] = s_prefix[i];
+  if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, KV::kOutBf16, lane);
+  PendingList pl;
+  pl.list = reinterpret_cast<int4*>(smem + dyn_pending_offset(a.batch)) + wave * kMaxPending;
+
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int n_chunks = (total + C - 1) / C;
+  const int W = static_cast<int>(gridDim.x) * kWavesPerGroup;
+  // Every wavefront takes from the counter until it is refused once, so a
+  // launch makes max(0, n_chunks - W) + W takes; the wavefront refused by
+  // the last of them resets the counter to zero for the next launch.
+  const int last_take = max(0, n_chunks - W) + W - 1;
+  // A take is one buffer atomic over a 4-byte range: only lane 0's offset
+  // is in range, the other lanes' operations are dropped.  No branch on the
+  // lane: a lane-0 branch here makes the compiler treat the scalar state
+  // merged after it (took, nxt, the cursors) as divergent, keep it in
+  // vector registers, and wrap every tile load in a waterfall loop.
+  const __amdgpu_buffer_rsrc_t work_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.work, 0, 4, PKV_RSRC_WORD3);
+  auto take = [&]() { return __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, work_rsrc, 4u * lane, 0, 0); };
+  // nxt: the next chunk once known (kUnknown until then; >= n_chunks once
+  // refused).  A take is requested at the first step of a ring turn, just
+  // before that step's tile loads, and read at step kDepth of the same turn,
+  // after the compute side has waited for those loads: vector memory
+  // operations complete in order, so the read never waits, and the take's
+  // register never lives across the loop (where copies of it would each
+  // wait for every load in flight).
+  constexpr int kUnknown = -1;
+  int nxt = kUnknown;
+  int refused = -1;                     // this wavefront's refused take (-1: still taking)
+  bool took = false;
+  int tk = 0;                           // lane 0: the take in flight (assigned only at a turn's first step)
+  auto resolve_v = [&](int v) {         // a take's value -> nxt
+    nxt = W + v;
+    if (nxt >= n_chunks) refused = v;
+  };
+  auto resolve = [&]() {                // the take in flight -> nxt
+    resolve_v(uni(tk));
+    took = false;
+  };
+  int lchunk = static_cast<int>(blockIdx.x) * kWavesPerGroup + wave;
+  bool lmore = lchunk < n_chunks;
+  if (!lmore) {                         // no chunk of its own: one (refused) take
+    const int t = take();
+    resolve_v(uni(t));
+  }
+
+  const size_t page_stride = static_cast<size_t>(kTile) * a.n_kv;
+  char* kp0 = static_cast<char*>(a.k_pages);
+  char* vp0 = static_cast<char*>(a.v_pages);
+  auto bt_row = [&](int b) {
+    return (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
+  };
+
+  // ---- loader.  Once it has no chunk left, the loads are issued with an
+  // empty range (nothing is read) and the buffers carry chunk -1.
+  FlatCursor<KV::kMulti> ld;
+  int lcnt = 0, lissued = 0;
+  if (lmore) {
+    ld.seek(a, s_prefix, lchunk * C);
+    lcnt = min(C, total - lchunk * C);
+  }
+  Regs buf[kBufs];
+  int page_of[kBufs];
+  int chunk_of[kBufs];
+  auto issue = [&](Regs& r, int& pg_out, int& chunk_out) {
+    int pg = -1, hh = 0;
+    if (lmore) {
+      pg = bt_row(ld.b)[ld.fb + ld.j];
+      hh = ld.h;
+    }
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    KV::template load<kAux>(r, a, static_cast<size_t>(ok ? pg : 0) * a.n_kv + hh, ok, lane);
+    pg_out = pg;
+    chunk_out = lmore ? lchunk : -1;
+    if (lmore) {
+      if (++lissued < lcnt) {
+        ld.next(a, s_prefix);
+      } else {
+        // Chunk done.  The next one is normally known by now (chunks are
+        // longer than a ring turn); otherwise its take is read here, which
+        // waits for the loads in flight.
+        if (nxt == kUnknown) {
+          if (took) {
+            resolve();
+          } else {
+            const int t = take();
+            resolve_v(uni(t));
+          }
+        }
+        if (nxt < n_chunks) {
+          lchunk = nxt;
+          nxt = kUnknown;
+          lissued = 0;
+          ld.seek(a, s_prefix, lchunk * C);
+          lcnt = min(C, total - lchunk * C);
+        } else {
+          lmore = false;
+        }
+      }
+    }
+  };
+
+  // ---- compute.
+  FlatCursor<KV::kMulti> cp;
+  int cchunk = -1, ccnt = 0, cpos = 0;
+  typename KV::Seg seg;
+  bool open = false, bad = false;
+  int seg_start = 0;
+  auto close = [&]() {
+    seg.finish(a, seg_start, cchunk, C, bad, lane, pl);
+    open = false;
+    // A full list is counted and merged here, with one partial per round
+    // trip: few registers beside the ring's.
+    if (pl.n == kMaxPending) flush_pending<KV::kOutBf16, D, KV::kMulti, 1>(a, pl, lane);
+  };
+  auto compute = [&](Regs& r, int pg, int ch) {
+    if (ch != cchunk) {
+      if (open) close();
+      cchunk = ch;
+      cpos = 0;
+      cp.seek(a, s_prefix, ch * C);
+      ccnt = min(C, total - ch * C);
+    } else if (open && (cp.b != seg.b || cp.h != seg.h)) {
+      close();
+    }
+    if (!open) {
+      const bool ends_pair = cp.j + (ccnt - cpos) >= cp.n;
+      seg.begin(a, cp.b, cp.h, cp.n, cp.fb, ends_pair, 0, lane);
+      seg_start = a.n_kv * cp.pb + cp.h * cp.n;
+      bad = false;
+      open = true;
+    }
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    bad |= !ok;
+    if constexpr (KV::kFusedAppend) {
+      if (seg.append && cp.j == cp.n - 1) {
+        seg.patch(r, lane);
+        if (ok) {
+          const size_t head_off = static_cast<size_t>(cp.h) * kTile;
+          seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+        }
+      }
+    }
+    seg.page(r, cp.j, a.scale_log2, lane);
+    if (++cpos < ccnt) cp.next(a, s_prefix);
+  };
+
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s], chunk_of[s]);
+  // Whole turns of the ring with uniform guards, as in split_kernel.
+  bool more = true;
+  while (more) {
+#pragma unroll
+    for (int s = 0; s < kBufs; ++s) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (s == 0 && refused < 0 && nxt == kUnknown && !took) {
+        tk = take();
+        took = true;
+      }
+      issue(buf[(s + kDepth) % kBufs], page_of[(s + kDepth) % kBufs], chunk_of[(s + kDepth) % kBufs]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (chunk_of[s] >= 0) compute(buf[s], page_of[s], chunk_of[s]);
+      else more = false;
+      if (s == kDepth && took) resolve();
+    }
+  }
+  if (took) resolve();   // (not reached: a take is resolved within its turn)
+  if (open) close();
+  if (pl.n > 0) flush_pending<KV::kOutBf16, D, KV::kMulti, 0>(a, pl, lane);
+  if (refused == last_take && lane == 0)
+    __hip_atomic_store(a.work, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
@@ -1400,6 +1650,7 @@ struct Resolved {
   int min_chunk;
   int combine_mode;
   int wpc;
+  int schedule;   // PKV_SCHEDULE_STATIC or PKV_SCHEDULE_DYNAMIC
   size_t lds;
 };
 
@@ -1409,6 +1660,12 @@ using SplitFn = void (*)(DecodeArgs);
 // used to build it.
 size_t split_lds_bytes(int batch) {
   return static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
+}
+
+// The dynamic kernel's LDS: the same, then each wavefront's pending list.
+size_t dyn_lds_bytes(int batch) {
+  return static_cast<size_t>(dyn_pending_offset(batch)) * sizeof(int32_t) +
+         static_cast<size_t>(kWavesPerGroup) * kMaxPending * 16;
 }
 
 // bf16 tiles are 4 KiB per (page, head) at head_dim 128: two pages ahead fit
@@ -1435,6 +1692,18 @@ SplitFn split_fn_ng(int dtype, int head_dim, bool q8) {
                          : split_kernel<DenseKV<false, 64, kMulti>, 1, kNG>;
 }
 
+template <bool kMulti>
+SplitFn dyn_fn(int dtype, int head_dim, bool q8) {
+  if (q8)
+    return head_dim == 128 ? dyn_kernel<Q8KV<128>, PKV_Q8_PREFETCH_PAGES>
+                           : dyn_kernel<Q8KV<64>, PKV_Q8_PREFETCH_PAGES>;
+  if (dtype == PKV_BF16)
+    return head_dim == 128 ? dyn_kernel<DenseKV<true, 128, kMulti>, kPrefetchPages>
+                           : dyn_kernel<DenseKV<true, 64, kMulti>, kPrefetchPages>;
+  return head_dim == 128 ? dyn_kernel<DenseKV<false, 128, kMulti>, 1>
+                         : dyn_kernel<DenseKV<false, 64, kMulti>, 1>;
+}
+
 // cols: MFMA columns per KV head (query tokens x query heads); multi: more
 // than one query token or a sliding window (dense caches only).
 SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
@@ -1445,14 +1714,32 @@ SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
   }
 }
 
-int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
+int device_cus(int* n_cu) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-  int n_cu = 0;
-  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
+  return ok();
+}
+
+// Default chunk count of the static schedule.  Kernels with one wavefront
+// per chunk: one chunk per wavefront of one workgroup per CU.  A second
+// resident workgroup on a CU does not add bandwidth: the CU's first
+// workgroup takes nearly all of its memory throughput and the second one
+// mostly waits, then finishes late (measured on MI355X: 1024 chunks of 128
+// pages beat 2048 of 64 by 5% on the 16 x 4096 MHA layer).  Larger groups
+// (several wavefronts per chunk): one chunk per resident group of them.
+int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
+  int n_cu = 0;
+  int st = device_cus(&n_cu);
+  if (st != PKV_OK) return st;
+  if (waves_per_chunk(group) == 1) {
+    *out = n_cu * kWavesPerGroup;
+    return ok();
+  }
   int per_cu = 0;
+  hipError_t e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
       &per_cu,
       reinterpret_cast<const void*>(split_fn(dtype, head_dim, group, dtype == PKV_U8, false)),
@@ -1490,16 +1777,33 @@ int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, 
   r->combine_mode = opts ? opts->combine_mode : 0;
   if (r->combine_mode != 0 && r->combine_mode != 1)
     return fail(PKV_ERR_INVALID_ARG, "decode: combine_mode must be 0 or 1");
-  r->lds = split_lds_bytes(batch);
+  const int sched = opts ? opts->schedule : PKV_SCHEDULE_AUTO;
+  if (sched != PKV_SCHEDULE_AUTO && sched != PKV_SCHEDULE_STATIC && sched != PKV_SCHEDULE_DYNAMIC)
+    return fail(PKV_ERR_INVALID_ARG, "decode: schedule must be 0 (auto), 1 (static) or 2 (dynamic)");
+  const bool dyn_ok = r->wpc == 1 && dyn_lds_bytes(batch) <= kMaxLdsBytes;
+  if (sched == PKV_SCHEDULE_DYNAMIC && !dyn_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: the dynamic schedule takes at most 16 columns per KV head "
+                                     "(query tokens x group) and a batch whose page prefix fits its LDS");
+  r->schedule = (sched == PKV_SCHEDULE_DYNAMIC) ? PKV_SCHEDULE_DYNAMIC : PKV_SCHEDULE_STATIC;
+  const bool dyn = r->schedule == PKV_SCHEDULE_DYNAMIC;
+  r->lds = dyn ? dyn_lds_bytes(batch) : split_lds_bytes(batch);
   r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages
-                                                     : default_min_chunk(group, dtype == PKV_U8);
+                 : dyn                                ? kDynMinChunk
+                                                      : default_min_chunk(group, dtype == PKV_U8);
   if (opts && opts->n_items > 0) {
     if (opts->n_items > kMaxItems)
       return fail(PKV_ERR_INVALID_ARG, "decode: n_items above 2^22");
     r->n_items = opts->n_items;
     return PKV_OK;
   }
-  int st = default_items(dtype, head_dim, group, r->lds, &r->n_items);
+  int st;
+  if (dyn) {
+    int n_cu = 0;
+    st = device_cus(&n_cu);
+    r->n_items = n_cu * kWavesPerGroup * kDynChunksPerWave;
+  } else {
+    st = default_items(dtype, head_dim, group, r->lds, &r->n_items);
+  }
   if (st != PKV_OK) return st;
   // No more chunks than the largest possible cache (every sequence at
   // max_blocks_per_seq pages) has chunks of min_chunk pages.
@@ -1598,14 +1902,27 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.fuse_max_parts = kFuseMaxParts;
   a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                         decode_prefix_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
+  a.work = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                      decode_work_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
-    const int chunks_per_group = kWavesPerGroup / r.wpc;
-    const int grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
     const bool multi = q_len > 1 || window > 0;
-    hipLaunchKernelGGL(split_fn(dtype, head_dim, cols, q8, multi), dim3(grid),
-                       dim3(kWave * kWavesPerGroup), r.lds, s, a);
+    SplitFn fn;
+    int grid;
+    if (r.schedule == PKV_SCHEDULE_DYNAMIC) {
+      // one workgroup per CU, never more than one chunk's worth of wavefronts each
+      int n_cu = 0;
+      st = device_cus(&n_cu);
+      if (st != PKV_OK) return st;
+      grid = std::max(1, std::min(n_cu, (r.n_items + kWavesPerGroup - 1) / kWavesPerGroup));
+      fn = multi ? dyn_fn<true>(dtype, head_dim, q8) : dyn_fn<false>(dtype, head_dim, q8);
+    } else {
+      const int chunks_per_group = kWavesPerGroup / r.wpc;
+      grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
+      fn = split_fn(dtype, head_dim, cols, q8, multi);
+    }
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * kWavesPerGroup), r.lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
   }
@@ -1829,6 +2146,7 @@ int pkv_decode_resolve(int32_t dtype, int32_t head_dim, int32_t n_q_heads, int32
   resolved->n_items = r.n_items;
   resolved->min_chunk_pages = r.min_chunk;
   resolved->combine_mode = r.combine_mode;
+  resolved->schedule = r.schedule;
   *workspace_bytes = pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, r.n_items);
   return *workspace_bytes < 0 ? static_cast<int>(*workspace_bytes) : ok();
 }

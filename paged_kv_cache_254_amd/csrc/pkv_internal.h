@@ -91,5 +91,28 @@ __host__ __device__ inline int64_t decode_prefix_offset(int64_t batch, int64_t g
                                                         int64_t head_dim, int64_t n_items) {
   return decode_counters_offset(batch, group, n_kv, head_dim, n_items) + decode_counters_count(batch, n_kv) * 4;
 }
+// After the prefix: the dynamic schedule's chunk counter (int32; zero
+// between launches, like the arrival counters).
+__host__ __device__ inline int64_t decode_work_offset(int64_t batch, int64_t group, int64_t n_kv,
+                                                      int64_t head_dim, int64_t n_items) {
+  return decode_prefix_offset(batch, group, n_kv, head_dim, n_items) + (batch + 1) * 4;
+}
+__host__ __device__ inline int64_t decode_workspace_end(int64_t batch, int64_t group, int64_t n_kv,
+                                                        int64_t head_dim, int64_t n_items) {
+  return decode_work_offset(batch, group, n_kv, head_dim, n_items) + 4;
+}
+
+// Dynamic schedule (pkv_decode_opts.schedule): one workgroup per CU; by
+// default kDynChunksPerWave chunks per wavefront of at least kDynMinChunk
+// pages, so that wavefronts that run faster can take more of them.
+constexpr int kDynChunksPerWave = 8;
+constexpr int kDynMinChunk = 16;
+// Pairs a wavefront of the dynamic kernel lists before counting their arrivals.
+constexpr int kMaxPending = 64;
+// LDS of the dynamic kernel: the prefix and per-wave sums (int32), then, 16-byte
+// aligned, each wavefront's list of pending pairs (kMaxPending int4 entries).
+__host__ __device__ inline int dyn_pending_offset(int batch) {   // in int32 units
+  return (batch + 1 + kWavesPerGroup + 3) & ~3;
+}
 
 }  // namespace pkv

@@ -35,8 +35,8 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
-def _opts(n_items: int = 0, min_chunk_pages: int = 0, combine_mode: int = 0):
-    return ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages), int(combine_mode)))
+def _opts(n_items: int = 0, min_chunk_pages: int = 0, combine_mode: int = 0, schedule: int = 0):
+    return ctypes.byref(DecodeOpts(int(n_items), int(min_chunk_pages), int(combine_mode), int(schedule)))
 
 
 # ----------------------------------------------------------------- host side
@@ -105,14 +105,15 @@ def decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim
 
 
 def decode_resolve(dtype_code: int, head_dim: int, n_q_heads: int, n_kv_heads: int, batch: int,
-                   max_blocks: int, n_items: int = 0, min_chunk_pages: int = 0, combine_mode: int = 0):
-    """(n_items, min_chunk_pages, workspace_bytes) the device calls use for these shapes."""
+                   max_blocks: int, n_items: int = 0, min_chunk_pages: int = 0, combine_mode: int = 0,
+                   schedule: int = 0):
+    """(n_items, min_chunk_pages, workspace_bytes, schedule) the device calls use for these shapes."""
     res = DecodeOpts()
     ws = ctypes.c_int64()
     check(lib.pkv_decode_resolve(dtype_code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks,
-                                 _opts(n_items, min_chunk_pages, combine_mode), ctypes.byref(res),
+                                 _opts(n_items, min_chunk_pages, combine_mode, schedule), ctypes.byref(res),
                                  ctypes.byref(ws)), "pkv_decode_resolve")
-    return res.n_items, res.min_chunk_pages, ws.value
+    return res.n_items, res.min_chunk_pages, ws.value, res.schedule
 
 
 def decode_plan(seq_lens: Sequence[int], n_kv_heads: int, max_blocks: int, n_items: int,
@@ -181,14 +182,18 @@ class Decoder:
     """Holds the resolved work split and a workspace for one decode shape
     (batch, heads, head_dim, dtype and the block-table width max_blocks).
     The workspace starts zero-filled, as the in-kernel merge's arrival
-    counters require; combine_mode 1 always merges with the combine kernel."""
+    counters and the dynamic schedule's chunk counter require; combine_mode 1
+    always merges with the combine kernel.  schedule: PKV_SCHEDULE_AUTO (0),
+    _STATIC (1) or _DYNAMIC (2); self.schedule holds the resolved one."""
 
     def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype, max_blocks: int,
-                 n_items: int = 0, min_chunk_pages: int = 0, device="cuda", combine_mode: int = 0):
+                 n_items: int = 0, min_chunk_pages: int = 0, device="cuda", combine_mode: int = 0,
+                 schedule: int = 0):
         import torch
         code = {torch.bfloat16: PKV_BF16, torch.float32: PKV_F32, torch.uint8: PKV_U8}[dtype]
-        self.n_items, self.min_chunk_pages, self.ws_bytes = decode_resolve(
-            code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks, n_items, min_chunk_pages, combine_mode)
+        self.n_items, self.min_chunk_pages, self.ws_bytes, self.schedule = decode_resolve(
+            code, head_dim, n_q_heads, n_kv_heads, batch, max_blocks, n_items, min_chunk_pages, combine_mode,
+            schedule)
         self.combine_mode = combine_mode
         self.workspace = torch.zeros(max(256, self.ws_bytes), dtype=torch.uint8, device=device)
         self.shape = (batch, n_q_heads, n_kv_heads, head_dim)
@@ -201,7 +206,7 @@ class Decoder:
         return (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hq,
                 k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B,
                 block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
-                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages, self.combine_mode))
+                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages, self.combine_mode, self.schedule))
 
     def __call__(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
         check(lib.pkv_paged_decode_attn(*self._args(q, k_pages, v_pages, block_table, seq_lens, scale, out,
@@ -216,7 +221,7 @@ class Decoder:
         return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                 _ptr(seq_lens), Hq, k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream),
                 B, block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
-                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages, self.combine_mode))
+                self.workspace.numel(), _opts(self.n_items, self.min_chunk_pages, self.combine_mode, self.schedule))
 
     def step(self, q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale, out, stream=None):
         """Append each sequence's new token at seq_lens - 1 and attend, in one pass."""
@@ -237,7 +242,7 @@ class Decoder:
         B, Hq, Hkv, D = self.shape
         check(lib.pkv_lse_combine(_ptr(self.workspace), self.workspace.numel(), _ptr(seq_lens), B, Hq, Hkv, D,
                                   BLOCK_SIZE, max_blocks, _ptr(out), _dtype_code(out),
-                                  _opts(self.n_items, self.min_chunk_pages, self.combine_mode), _stream(stream)),
+                                  _opts(self.n_items, self.min_chunk_pages, self.combine_mode, self.schedule), _stream(stream)),
               "pkv_lse_combine")
 
     def attn_multi(self, q, k_pages, v_pages, block_table, seq_lens, q_len: int, scale, out, window: int = 0,
@@ -255,7 +260,7 @@ class Decoder:
                                          Hq, k_pages.shape[1], D, BLOCK_SIZE, q_len, window, float(scale), _ptr(out),
                                          _stream(stream), B, block_table.shape[1], k_pages.shape[0], _dtype_code(q),
                                          _ptr(self.workspace), self.workspace.numel(),
-                                         _opts(self.n_items, self.min_chunk_pages, self.combine_mode)),
+                                         _opts(self.n_items, self.min_chunk_pages, self.combine_mode, self.schedule)),
               "pkv_paged_decode_multi")
         return out
 
@@ -268,7 +273,7 @@ class Decoder:
         return (_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(meta), _ptr(block_table), _ptr(seq_lens), Hq,
                 k_codes.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B, block_table.shape[1],
                 k_codes.shape[0], _ptr(self.workspace), self.workspace.numel(),
-                _opts(self.n_items, self.min_chunk_pages, self.combine_mode))
+                _opts(self.n_items, self.min_chunk_pages, self.combine_mode, self.schedule))
 
     def attn_q8(self, q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream=None):
         """Decode over the 8-bit cache (Decoder built with dtype=torch.uint8; q and out bf16)."""
@@ -285,6 +290,16 @@ class Decoder:
         a = self._q8_args(q, k_codes, v_codes, meta, block_table, seq_lens, scale, out, stream)
         check(lib.pkv_decode_step_q8(a[0], _ptr(k_new), _ptr(v_new), *a[1:]), "pkv_decode_step_q8")
         return out
+
+    def counters(self):
+        """(arrival counters [B][Hkv][4], chunk counter) int32 views into the workspace."""
+        import torch
+        B, Hq, Hkv, D = self.shape
+        slots = self.n_items + B * Hkv
+        parts = slots * (Hq // Hkv) * (D + 1) * 4
+        off = (parts + 255) // 256 * 256
+        i = self.workspace[: self.ws_bytes].view(torch.int32)
+        return i[off // 4: off // 4 + B * Hkv * 4].view(B, Hkv, 4), i[self.ws_bytes // 4 - 1]
 
     def partials(self):
         """Views (partial_o [slots][G][D], partial_lse [slots][G]) into the workspace."""

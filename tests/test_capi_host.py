@@ -177,12 +177,13 @@ def test_plan_matches_flattened_chunking(lens, n_kv, n_items, min_chunk):
 def test_workspace_bytes():
     # partials (slots x group x (head_dim + 1) floats), padded to 256 bytes,
     # then 4 int32 arrival counters per (sequence, KV head), then the
-    # per-sequence page prefix (batch + 1 int32)
+    # per-sequence page prefix (batch + 1 int32), then the dynamic
+    # schedule's chunk counter (one int32)
     def layout(batch, hq, hkv, d, n_items):
         parts = (n_items + batch * hkv) * (hq // hkv) * (d + 1) * 4
-        return -(-parts // 256) * 256 + batch * hkv * 4 * 4 + (batch + 1) * 4
-    assert pkv.decode_workspace_bytes(16, 32, 32, 128, 2048) == (2048 + 16 * 32) * 1 * 129 * 4 + 16 * 32 * 16 + 68
-    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4) == 4352 + 64 + 12
+        return -(-parts // 256) * 256 + batch * hkv * 4 * 4 + (batch + 1) * 4 + 4
+    assert pkv.decode_workspace_bytes(16, 32, 32, 128, 2048) == (2048 + 16 * 32) * 1 * 129 * 4 + 16 * 32 * 16 + 68 + 4
+    assert pkv.decode_workspace_bytes(2, 4, 2, 64, 4) == 4352 + 64 + 12 + 4
     for args in ((16, 32, 32, 128, 2048), (2, 4, 2, 64, 4), (3, 64, 1, 128, 7), (256, 32, 8, 128, 2048)):
         assert pkv.decode_workspace_bytes(*args) == layout(*args)
     with pytest.raises(pkv.PkvError):
@@ -197,7 +198,7 @@ def _decode(**kw):
              out=FAKE, stream=None, batch=2, mb=8, P=32, dtype=_lib.PKV_F32, ws=FAKE, wsb=1 << 30,
              n_items=4)
     a.update(kw)
-    opts = _lib.DecodeOpts(a["n_items"], 0, a.get("combine_mode", 0))
+    opts = _lib.DecodeOpts(a["n_items"], 0, a.get("combine_mode", 0), a.get("schedule", 0))
     return _lib.lib.pkv_paged_decode_attn(a["q"], a["k"], a["v"], a["bt"], a["sl"], a["hq"], a["hkv"], a["d"],
                                           a["bs"], a["scale"], a["out"], a["stream"], a["batch"], a["mb"],
                                           a["P"], a["dtype"], a["ws"], a["wsb"], ctypes.byref(opts))
@@ -219,6 +220,10 @@ def _decode(**kw):
     (dict(scale=float("nan")), _lib.PKV_ERR_INVALID_ARG),
     (dict(wsb=100), _lib.PKV_ERR_WORKSPACE),
     (dict(combine_mode=2), _lib.PKV_ERR_INVALID_ARG),
+    (dict(schedule=3), _lib.PKV_ERR_INVALID_ARG),
+    (dict(schedule=-1), _lib.PKV_ERR_INVALID_ARG),
+    # the dynamic schedule takes at most 16 MFMA columns per KV head
+    (dict(schedule=_lib.PKV_SCHEDULE_DYNAMIC, hq=64, hkv=2), _lib.PKV_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
     assert _decode(**kw) == status

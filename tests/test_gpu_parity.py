@@ -26,11 +26,11 @@ def pkv():
     return m
 
 
-def _run_step(pkv, c, n_items=0, min_chunk=0, out=None):
+def _run_step(pkv, c, n_items=0, min_chunk=0, out=None, schedule=0):
     w = c.w
     pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
     dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), c.max_blocks, n_items,
-                      min_chunk)
+                      min_chunk, schedule=schedule)
     out = torch.empty_like(c.q) if out is None else out
     dec(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out)
     torch.cuda.synchronize()
@@ -83,14 +83,17 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("schedule", [1, 2], ids=["static", "dynamic"])
 @pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached,n_items,min_chunk", SMALL, ids=[s[0] for s in SMALL])
-def test_small_parity(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, min_chunk):
+def test_small_parity(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, min_chunk, schedule):
     P = sum((n + 16) // 16 for n in cached) + 5
     w = W.custom(name, B, Hq, Hkv, D, dtype, cached, pool_pages=P, seed=zlib.crc32(name.encode()) % 1000)
     c = H.setup(w, device="cuda", gen_device="cpu")
-    H.log(f"small {name}")
+    H.log(f"small {name} schedule {schedule}")
     ref = H.oracle_full(c)
-    out, _ = _run_step(pkv, c, n_items, min_chunk)
+    if schedule == 2 and Hq // Hkv > 16:
+        pytest.skip("the dynamic schedule takes groups of at most 16 query heads")
+    out, _ = _run_step(pkv, c, n_items, min_chunk, schedule=schedule)
     H.assert_close(H.f64(out), ref, dtype, name)
 
 
