@@ -1031,9 +1031,19 @@ constexpr int kKernelWavesPerEu = kNG == 1 ? KV::kWavesPerEu : KV::kWavesPerEuGr
 // compute cursor closes a segment (writes its output rows or partial) and
 // opens the next one when the pair changes.  No barrier after the prefix:
 // wavefronts without work return early.
-template <class KV, int kDepth, int kNG>
+//
+// kNB = 2 (with kNG = 1, groups of 17 to 32 columns): each wavefront
+// computes both 16-column blocks, so a page is loaded once for the whole
+// group and its per-page work (page id, loads, masks, cursor) is shared.
+// The state of two blocks needs the whole register file: one wavefront per
+// SIMD.  Measured on MI355X against two one-block wavefronts per chunk: +8%
+// on the GQA layer with 8 query tokens (32 columns); above 32 columns two
+// such wavefronts per chunk lost to four one-block ones (the 131072-token
+// MQA layer: 1340 vs 1801 GB/s), which keep all four SIMDs of a CU busy on
+// one chunk.  Four blocks in one wavefront spill.
+template <class KV, int kDepth, int kNG, int kNB = 1>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
-__attribute__((amdgpu_waves_per_eu(kKernelWavesPerEu<KV, kNG>)))
+__attribute__((amdgpu_waves_per_eu(kNB > 1 ? 1 : kKernelWavesPerEu<KV, kNG>)))
 split_kernel(DecodeArgs a) {
   constexpr int D = KV::kHeadDim;
   constexpr int kTile = KV::kTileK;
@@ -1041,6 +1051,7 @@ split_kernel(DecodeArgs a) {
   using Regs = typename KV::Regs;
   constexpr int kAux = kNG == 1 ? PKV_KV_LOAD_AUX : PKV_KV_LOAD_AUX_GROUPED;
   static_assert(kWavesPerGroup % kNG == 0, "head blocks per chunk divide the workgroup");
+
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
   int32_t* s_wsum = smem + a.batch + 1;
@@ -1051,8 +1062,8 @@ split_kernel(DecodeArgs a) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.prefix[i] = s_prefix[i];
   if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, KV::kOutBf16, lane);
-  const int chunk = blockIdx.x * (kWavesPerGroup / kNG) + wave / kNG;
-  const int gblk = wave % kNG;
+  const int chunk = static_cast<int>(blockIdx.x) * (kWavesPerGroup / kNG) + wave / kNG;
+  const int gblk = (wave % kNG) * kNB;
   if (chunk >= a.n_items || gblk * 16 >= a.cols) return;
   const int total = uni(a.n_kv * s_prefix[a.batch]);
   const int C = chunk_pages(total, a.n_items, a.min_chunk);
@@ -1087,21 +1098,26 @@ split_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- compute.
+  // ---- compute.  seg[i] is head block gblk + i; block 0 carries the new
+  // token of a fused append and lists the pairs to merge.
   FlatCursor<KV::kMulti> cp;
   cp.seek(a, s_prefix, f0);
-  typename KV::Seg seg;
-  PendingMerges pending;
+  typename KV::Seg seg[kNB];
+  PendingMerges pending, unused;
   bool open = false, bad = false;
   int seg_start = 0;
   auto compute = [&](Regs& r, int pg, int p) {
-    if (open && (cp.b != seg.b || cp.h != seg.h)) {
-      seg.finish(a, seg_start, chunk, C, bad, lane, pending);
+    if (open && (cp.b != seg[0].b || cp.h != seg[0].h)) {
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].finish(a, seg_start, chunk, C, bad, lane, i == 0 ? pending : unused);
       open = false;
     }
     if (!open) {
       const bool ends_pair = cp.j + (cnt - p) >= cp.n;
-      seg.begin(a, cp.b, cp.h, cp.n, cp.fb, ends_pair, gblk, lane);
+#pragma unroll
+      for (int i = 0; i < kNB; ++i)
+        if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].begin(a, cp.b, cp.h, cp.n, cp.fb, i == 0 && ends_pair, gblk + i, lane);
       seg_start = a.n_kv * cp.pb + cp.h * cp.n;
       bad = false;
       open = true;
@@ -1110,15 +1126,17 @@ split_kernel(DecodeArgs a) {
     bad |= !ok;
     // Every head block patches its registers; the first stores the token.
     if constexpr (KV::kFusedAppend) {
-      if (seg.append && cp.j == cp.n - 1) {
-        seg.patch(r, lane);
+      if (seg[0].append && cp.j == cp.n - 1) {
+        seg[0].patch(r, lane);
         if (ok && gblk == 0) {
           const size_t head_off = static_cast<size_t>(cp.h) * kTile;
-          seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+          seg[0].store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
         }
       }
     }
-    seg.page(r, cp.j, a.scale_log2, lane);
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].page(r, cp.j, a.scale_log2, lane);
   };
 
 #pragma unroll
@@ -1143,13 +1161,23 @@ split_kernel(DecodeArgs a) {
       ++p;
     }
   }
-  if (open) seg.finish(a, seg_start, chunk, C, bad, lane, pending);
+  if (open) {
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].finish(a, seg_start, chunk, C, bad, lane, i == 0 ? pending : unused);
+  }
   if (pending.n > 0) {
-    const int last = arrive(a, pending, gblk, lane);
-    if (last & 1)
-      merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b0, pending.h0, gblk, pending.first0, pending.nparts0, lane);
-    if (last & 2)
-      merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b1, pending.h1, gblk, pending.first1, pending.nparts1, lane);
+#pragma unroll
+    for (int i = 0; i < kNB; ++i) {
+      if (i > 0 && (gblk + i) * 16 >= a.cols) continue;
+      const int last = arrive(a, pending, gblk + i, lane);
+      if (last & 1)
+        merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b0, pending.h0, gblk + i, pending.first0, pending.nparts0,
+                                                lane);
+      if (last & 2)
+        merge_pair<KV::kOutBf16, D, KV::kMulti>(a, pending.b1, pending.h1, gblk + i, pending.first1, pending.nparts1,
+                                                lane);
+    }
   }
 }
 
@@ -1679,6 +1707,20 @@ constexpr int kPrefetchPages = PKV_PREFETCH_PAGES;
 #define PKV_Q8_PREFETCH_PAGES 2
 #endif
 
+// Groups of 17 to 32 columns: one wavefront computes both head blocks of a
+// chunk, with a ring three pages deep (two for fp32 at head_dim 64, one at 128).
+constexpr int kWideDepth = 3;
+template <bool kMulti>
+SplitFn split_fn_wide(int dtype, int head_dim, bool q8) {
+  if (q8)
+    return head_dim == 128 ? split_kernel<Q8KV<128>, kWideDepth, 1, 2> : split_kernel<Q8KV<64>, kWideDepth, 1, 2>;
+  if (dtype == PKV_BF16)
+    return head_dim == 128 ? split_kernel<DenseKV<true, 128, kMulti>, kWideDepth, 1, 2>
+                           : split_kernel<DenseKV<true, 64, kMulti>, kWideDepth, 1, 2>;
+  return head_dim == 128 ? split_kernel<DenseKV<false, 128, kMulti>, 1, 1, 2>
+                         : split_kernel<DenseKV<false, 64, kMulti>, 2, 1, 2>;
+}
+
 template <int kNG, bool kMulti>
 SplitFn split_fn_ng(int dtype, int head_dim, bool q8) {
   constexpr int kDepth = kNG == 1 ? kPrefetchPages : PKV_GROUPED_DEPTH;
@@ -1707,6 +1749,7 @@ SplitFn dyn_fn(int dtype, int head_dim, bool q8) {
 // cols: MFMA columns per KV head (query tokens x query heads); multi: more
 // than one query token or a sliding window (dense caches only).
 SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
+  if (cols > 16 && cols <= 32) return multi ? split_fn_wide<true>(dtype, head_dim, q8) : split_fn_wide<false>(dtype, head_dim, q8);
   switch (waves_per_chunk(cols)) {
     case 1: return multi ? split_fn_ng<1, true>(dtype, head_dim, q8) : split_fn_ng<1, false>(dtype, head_dim, q8);
     case 2: return multi ? split_fn_ng<2, true>(dtype, head_dim, q8) : split_fn_ng<2, false>(dtype, head_dim, q8);
@@ -1730,11 +1773,14 @@ int device_cus(int* n_cu) {
 // mostly waits, then finishes late (measured on MI355X: 1024 chunks of 128
 // pages beat 2048 of 64 by 5% on the 16 x 4096 MHA layer).  Larger groups
 // (several wavefronts per chunk): one chunk per resident group of them.
+// Wavefronts per chunk of the kernel that serves cols columns per KV head.
+int chunk_waves(int cols) { return cols <= 32 ? 1 : waves_per_chunk(cols); }
+
 int default_items(int dtype, int head_dim, int group, size_t lds, int* out) {
   int n_cu = 0;
   int st = device_cus(&n_cu);
   if (st != PKV_OK) return st;
-  if (waves_per_chunk(group) == 1) {
+  if (chunk_waves(group) == 1) {
     *out = n_cu * kWavesPerGroup;
     return ok();
   }
@@ -1773,14 +1819,14 @@ int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, i
 
 int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, int32_t max_blocks,
                  int32_t n_kv, const pkv_decode_opts* opts, Resolved* r) {
-  r->wpc = waves_per_chunk(group);
+  r->wpc = chunk_waves(group);
   r->combine_mode = opts ? opts->combine_mode : 0;
   if (r->combine_mode != 0 && r->combine_mode != 1)
     return fail(PKV_ERR_INVALID_ARG, "decode: combine_mode must be 0 or 1");
   const int sched = opts ? opts->schedule : PKV_SCHEDULE_AUTO;
   if (sched != PKV_SCHEDULE_AUTO && sched != PKV_SCHEDULE_STATIC && sched != PKV_SCHEDULE_DYNAMIC)
     return fail(PKV_ERR_INVALID_ARG, "decode: schedule must be 0 (auto), 1 (static) or 2 (dynamic)");
-  const bool dyn_ok = r->wpc == 1 && dyn_lds_bytes(batch) <= kMaxLdsBytes;
+  const bool dyn_ok = group <= 16 && dyn_lds_bytes(batch) <= kMaxLdsBytes;
   if (sched == PKV_SCHEDULE_DYNAMIC && !dyn_ok)
     return fail(PKV_ERR_UNSUPPORTED, "decode: the dynamic schedule takes at most 16 columns per KV head "
                                      "(query tokens x group) and a batch whose page prefix fits its LDS");
