@@ -165,7 +165,7 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  *
  * Supported: head_dim 64 or 128; block_size 16; dtype PKV_F32 or PKV_BF16 (q,
  * pages and out share it; accumulation is fp32); n_q_heads a multiple of
- * n_kv_heads with group n_q_heads / n_kv_heads <= 64; 0 <= batch <= 16000.
+ * n_kv_heads with group n_q_heads / n_kv_heads <= 64; 0 <= batch <= 15000.
  * seq_lens[b] == 0 gives a zero row.  A length < 0 or > 16 * max_blocks_per_seq,
  * or a block-table entry outside [0, num_pages), gives a NaN row for that
  * sequence (nothing outside the pool is read).

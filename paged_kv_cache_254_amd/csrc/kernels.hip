@@ -484,6 +484,92 @@ __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pa
   if (a.counters != nullptr && nparts <= a.fuse_max_parts) pending.add(b, h, first_chunk, nparts);
 }
 
+// The new token of a fused append, held until the wavefront has no tile loads
+// in flight.  Vector memory operations retire in order, so a store issued in
+// the middle of the tile stream holds back the waits for every later tile;
+// measured on MI355X the token's stores cost 8 us of the 181-us GQA layer
+// when issued at the pair's last page (writing the whole 8-KiB tile back
+// instead, in full lines, cost as much).  The token waits in this
+// wavefront's slot of LDS (K row, then V row as 32-bit words), which costs
+// no registers; LDS accesses have their own counter.
+// kDefer false (kernels whose sibling wavefronts share a chunk): the token is
+// stored as soon as it is handed over.
+template <bool kBf16, int D, bool kDefer = true>
+struct HeldToken {
+  using O = Ops<kBf16, D>;
+  static constexpr int kSlotWords = D * O::ES / 4 + D;   // K row, then D words of V
+  bool on = false;
+  char* kbase;        // (page, KV head) tiles the token goes to
+  char* vbase;
+  int s_new;          // its slot
+  uint32_t* lds;      // this wavefront's kSlotWords words
+
+  // K: the 16-byte pieces of slot s_new (lanes with lane % 16 == s_new, as
+  // loaded); V: its element of every feature row (lanes with lane / 16 ==
+  // s_new / 4).
+  __device__ void store_regs(const u32x4 (&k)[O::NK], const uint32_t (&v)[O::NV], int lane) const {
+    const int c = lane >> 4, n = lane & 15;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc(kbase, 0, kBlock * D * O::ES, PKV_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc(vbase, 0, kBlock * D * O::ES, PKV_RSRC_WORD3);
+    if (n == s_new) {
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i) __builtin_amdgcn_raw_buffer_store_b128(k[i], kr, 16u * lane + 1024 * i, 0, 0);
+    }
+    if (c == (s_new >> 2)) {
+      const uint32_t vo = O::ES * (n * kBlock + s_new);
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) {
+        if constexpr (kBf16)
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v[nb]), vr, vo + O::ES * 16 * kBlock * nb, 0,
+                                                0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(v[nb], vr, vo + O::ES * 16 * kBlock * nb, 0, 0);
+      }
+    }
+  }
+
+  // Takes the token: k[i] in lanes (c, any n) is K piece 4i + c; v[nb] in
+  // lanes (any c, n) is V element 16 nb + n.  now: store it at once (the
+  // caller has no more tiles to stream).
+  __device__ void take(const u32x4 (&k)[O::NK], const uint32_t (&v)[O::NV], int lane, bool now) {
+    on = true;
+    if (!kDefer || now) {
+      store_regs(k, v, lane);
+      on = false;
+    } else {
+      const int c = lane >> 4, n = lane & 15;
+      u32x4* lk = reinterpret_cast<u32x4*>(lds);
+      if (n == 0) {
+#pragma unroll
+        for (int i = 0; i < O::NK; ++i) lk[4 * i + c] = k[i];
+      }
+      if (c == 0) {
+#pragma unroll
+        for (int nb = 0; nb < O::NV; ++nb) lds[D * O::ES / 4 + 16 * nb + n] = v[nb];
+      }
+    }
+  }
+
+  // Writes the held token to the pool, if any.
+  __device__ void store(int lane) {
+    if constexpr (kDefer) {
+      if (!on) return;
+      on = false;
+      const int c = lane >> 4, n = lane & 15;
+      const u32x4* lk = reinterpret_cast<const u32x4*>(lds);
+      u32x4 k[O::NK];
+      uint32_t v[O::NV];
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i) k[i] = lk[4 * i + c];
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) v[nb] = lds[D * O::ES / 4 + 16 * nb + n];
+      store_regs(k, v, lane);
+    }
+  }
+};
+
 // One segment: the pages of one (sequence b, KV head h) pair that one chunk
 // covers, for the 16 query heads gblk*16 .. gblk*16+15 (lane column n = head
 // gblk*16 + n).  Holds the query operand, the online-softmax state and, when
@@ -567,32 +653,17 @@ struct Segment {
     }
   }
 
-  // Writes the new token into page pg of the pool (the same bytes the patched
-  // lanes hold).  kpool/vpool point at head h of page 0.
-  __device__ void store_new_token(char* kpool, char* vpool, size_t page_stride, int pg,
-                                  int lane) const {
-    const int c = lane >> 4, n = lane & 15;
+  // Hands the new token (already in knew/vnew) to `held`, to be written to
+  // page pg of the pool (kpool/vpool point at head h of page 0) once the
+  // wavefront's tile stream has drained.
+  template <bool kDefer>
+  __device__ void hold(HeldToken<kBf16, D, kDefer>& t, char* kpool, char* vpool, size_t page_stride, int pg,
+                       int lane, bool now) const {
     const size_t off = static_cast<size_t>(pg) * page_stride;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc(kpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc(vpool + off, 0, kTileBytes, PKV_RSRC_WORD3);
-    if (n == s_new) {
-#pragma unroll
-      for (int i = 0; i < O::NK; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(knew[i], kr, 16u * lane + 1024 * i, 0, 0);
-    }
-    if (c == (s_new >> 2)) {
-      const uint32_t vo = O::ES * (n * kBlock + s_new);
-#pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) {
-        if constexpr (kBf16)
-          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(vnew[nb]), vr,
-                                                vo + O::ES * 16 * kBlock * nb, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(vnew[nb], vr, vo + O::ES * 16 * kBlock * nb, 0, 0);
-      }
-    }
+    t.kbase = kpool + off;
+    t.vbase = vpool + off;
+    t.s_new = s_new;
+    t.take(knew, vnew, lane, now);
   }
 
   // Page j of the segment holds sequence tokens 16 (fb + j) .. +15.  Columns
@@ -948,14 +1019,13 @@ struct FlatCursor {
 };
 
 // At least two wavefronts per SIMD: caps registers at 256 per lane, which the
-// bf16 kernel fits without spilling; fp32 at head_dim 128 needs more and runs
+// bf16 kernels fit without spilling; fp32 at head_dim 128 needs more and runs
 // one wavefront per SIMD.
 template <bool kBf16, int D>
 constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
 
-// Sibling wavefronts of a large group read the same pages, so a CU has only
-// one wavefront's ring of distinct pages in flight: the grouped kernels run
-// a deeper ring at one wavefront per SIMD.
+// Ring depth of the kernels whose sibling wavefronts (one per 16-head block
+// of a large group) read the same pages.
 #ifndef PKV_GROUPED_DEPTH
 #define PKV_GROUPED_DEPTH 2
 #endif
@@ -975,6 +1045,8 @@ struct DenseKV {                       // bf16 or fp32 K/V, the q and out dtype;
   static constexpr int kWavesPerEuGrouped = (kBf16 || D == 64) ? PKV_GROUPED_WAVES_PER_EU : 1;
   using Regs = PageRegs<kBf16, D>;
   using Seg = Segment<kBf16, D, kMulti_>;
+  template <bool kDefer>
+  using Held = HeldToken<kBf16, D, kDefer>;
   template <int kAux>
   __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -996,6 +1068,11 @@ struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
   static constexpr int kWavesPerEuGrouped = PKV_GROUPED_WAVES_PER_EU;
   using Regs = PageRegsQ8<D>;
   using Seg = SegmentQ8<D, false>;   // one query token, no window
+  template <bool>
+  struct Held {                      // no fused append on the 8-bit cache
+    uint32_t* lds;
+    __device__ void store(int) {}
+  };
   template <int kAux>
   __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -1103,6 +1180,8 @@ split_kernel(DecodeArgs a) {
   FlatCursor<KV::kMulti> cp;
   cp.seek(a, s_prefix, f0);
   typename KV::Seg seg[kNB];
+  typename KV::template Held<kNG == 1> held;
+  held.lds = reinterpret_cast<uint32_t*>(smem + held_offset(a.batch)) + wave * kHeldWords;
   PendingMerges pending, unused;
   bool open = false, bad = false;
   int seg_start = 0;
@@ -1124,13 +1203,17 @@ split_kernel(DecodeArgs a) {
     }
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     bad |= !ok;
-    // Every head block patches its registers; the first stores the token.
+    // Every head block patches its registers; the first one stores the token:
+    // at once on the chunk's last page (nothing follows to hold back), else
+    // after its tile stream (a second token in the same chunk pushes the
+    // first one out at once).
     if constexpr (KV::kFusedAppend) {
       if (seg[0].append && cp.j == cp.n - 1) {
         seg[0].patch(r, lane);
         if (ok && gblk == 0) {
-          const size_t head_off = static_cast<size_t>(cp.h) * kTile;
-          seg[0].store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+          held.store(lane);
+          seg[0].hold(held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
+                      page_stride, pg, lane, p == cnt - 1);
         }
       }
     }
@@ -1179,6 +1262,9 @@ split_kernel(DecodeArgs a) {
                                                 lane);
     }
   }
+  // Last, so that no wait of this wavefront (its loads, the arrival's wait
+  // for its partial stores) includes the token's stores.
+  if constexpr (KV::kFusedAppend) held.store(lane);
 }
 
 // Counts the arrivals of the listed pairs after this wavefront's partial
@@ -1346,6 +1432,8 @@ dyn_kernel(DecodeArgs a) {
   FlatCursor<KV::kMulti> cp;
   int cchunk = -1, ccnt = 0, cpos = 0;
   typename KV::Seg seg;
+  typename KV::template Held<true> held;
+  held.lds = reinterpret_cast<uint32_t*>(smem + held_offset(a.batch)) + wave * kHeldWords;
   bool open = false, bad = false;
   int seg_start = 0;
   auto close = [&]() {
@@ -1378,8 +1466,9 @@ dyn_kernel(DecodeArgs a) {
       if (seg.append && cp.j == cp.n - 1) {
         seg.patch(r, lane);
         if (ok) {
-          const size_t head_off = static_cast<size_t>(cp.h) * kTile;
-          seg.store_new_token(kp0 + head_off, vp0 + head_off, page_stride, pg, lane);
+          held.store(lane);
+          seg.hold(held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
+                   page_stride, pg, lane, false);
         }
       }
     }
@@ -1409,6 +1498,7 @@ dyn_kernel(DecodeArgs a) {
   if (took) resolve();   // (not reached: a take is resolved within its turn)
   if (open) close();
   if (pl.n > 0) flush_pending<KV::kOutBf16, D, KV::kMulti, 0>(a, pl, lane);
+  if constexpr (KV::kFusedAppend) held.store(lane);   // last: no wait of this wavefront includes it
   if (refused == last_take && lane == 0)
     __hip_atomic_store(a.work, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1687,7 +1777,7 @@ using SplitFn = void (*)(DecodeArgs);
 // The split kernel's LDS: the per-sequence page prefix and the per-wave sums
 // used to build it.
 size_t split_lds_bytes(int batch) {
-  return static_cast<size_t>(batch + 1 + kWavesPerGroup) * sizeof(int32_t);
+  return static_cast<size_t>(held_offset(batch) + kWavesPerGroup * kHeldWords) * sizeof(int32_t);
 }
 
 // The dynamic kernel's LDS: the same, then each wavefront's pending list.
@@ -1809,7 +1899,7 @@ int check_decode_shapes(const char* fn, int32_t n_q_heads, int32_t n_kv_heads, i
   if (n_q_heads / n_kv_heads > kMaxGroup)
     return fail(PKV_ERR_UNSUPPORTED, f + ": more than 64 query heads per KV head");
   if (batch < 0 || batch > kMaxBatch)
-    return fail(PKV_ERR_UNSUPPORTED, f + ": batch must be in [0, 16000]");
+    return fail(PKV_ERR_UNSUPPORTED, f + ": batch must be in [0, 15000]");
   if (max_blocks_per_seq < 1 || num_pages < 1)
     return fail(PKV_ERR_INVALID_ARG, f + ": max_blocks_per_seq and num_pages must be >= 1");
   if (static_cast<int64_t>(batch) * max_blocks_per_seq * n_kv_heads >= (int64_t{1} << 31))

@@ -18,7 +18,7 @@ int ok();
 constexpr int kBlock = 16;          // tokens per page (the only size built)
 constexpr int kWave = 64;           // CDNA wavefront
 constexpr int kWavesPerGroup = 4;   // wavefronts per workgroup of the decode kernels
-constexpr int kMaxBatch = 16000;    // keeps the per-workgroup length prefix in 64 KiB of LDS
+constexpr int kMaxBatch = 15000;    // keeps a decode workgroup's LDS (length prefix, held tokens) in 64 KiB
 constexpr int kMaxGroup = 64;       // query heads per KV head
 // Default lower bound on pages per chunk.  Chunks are otherwise sized to
 // give one per resident group of wavefronts; on long sequences that makes
@@ -109,10 +109,15 @@ constexpr int kDynChunksPerWave = 8;
 constexpr int kDynMinChunk = 16;
 // Pairs a wavefront of the dynamic kernel lists before counting their arrivals.
 constexpr int kMaxPending = 64;
-// LDS of the dynamic kernel: the prefix and per-wave sums (int32), then, 16-byte
-// aligned, each wavefront's list of pending pairs (kMaxPending int4 entries).
-__host__ __device__ inline int dyn_pending_offset(int batch) {   // in int32 units
-  return (batch + 1 + kWavesPerGroup + 3) & ~3;
+// LDS of the decode kernels (int32 units): the prefix [batch + 1] and the
+// per-wave sums, then, 16-byte aligned, each wavefront's held token of a
+// fused append (K row and V row of head_dim <= 128 elements: at most
+// kHeldWords words), then (dynamic kernel) each wavefront's list of pending
+// pairs (kMaxPending int4 entries).
+constexpr int kHeldWords = 128 * 4 / 4 + 128;
+__host__ __device__ inline int held_offset(int batch) { return (batch + 1 + kWavesPerGroup + 3) & ~3; }
+__host__ __device__ inline int dyn_pending_offset(int batch) {
+  return held_offset(batch) + kWavesPerGroup * kHeldWords;
 }
 
 }  // namespace pkv
