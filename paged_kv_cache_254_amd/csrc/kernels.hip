@@ -222,6 +222,10 @@ struct DecodeArgs {
   int32_t* prefix;
   // Dynamic schedule: the counter chunks are taken from (zero between launches).
   int32_t* work;
+  // Static schedule with the in-kernel merge: pairs whose chunks all belong to
+  // one workgroup are merged through LDS (wg_lds_offset: int32 offset of the
+  // partial slots in the kernel's dynamic LDS).
+  int32_t wg_merge, wg_lds_offset;
 };
 
 // Pages per sequence (those from its first attended block, see
@@ -400,6 +404,9 @@ __device__ inline void compute_page(PageRegs<kBf16, D>& r, int valid, bool cut, 
   O::pv(r.v, p, l, acc);
 }
 
+// The decode kernels' dynamic LDS, seen as floats (the workgroup-merge slots).
+extern __shared__ float lds_f32[];
+
 // Pairs whose partial this wavefront wrote and that it may have to merge:
 // only a chunk's first and last segments can belong to pairs that span
 // several chunks, so at most two.  Merged after the page loop, which keeps
@@ -416,6 +423,19 @@ struct PendingMerges {
     }
     n = n < 2 ? n + 1 : 2;
   }
+  // Pairs whose chunks all run in this workgroup (static schedule): their
+  // partials go to LDS slots, and the wavefront holding a pair's first chunk
+  // merges it after a workgroup barrier.  wg_base: float index in the
+  // dynamic LDS of this workgroup's slots (slot 2 w + k: wavefront w's first
+  // (k = 0) or last (k = 1) segment), partial rows float [8][cols][D] then
+  // lse float [8][cols]; -1 when off.  An index, not a pointer: a pointer
+  // kept across the page loop lives in a vector register.
+  int wg_base = -1;
+  int wg_first = -1;            // chunk of the workgroup's first wavefront
+  int nw = 0, wb = 0, wh = 0, wfirst = 0, wparts = 0;   // the pair this wavefront merges
+  __device__ bool in_workgroup(int first_chunk, int last_chunk) const {
+    return wg_base >= 0 && first_chunk >= wg_first && last_chunk < wg_first + kWavesPerGroup;
+  }
 };
 
 // The same for the dynamic schedule, where a wavefront takes any number of
@@ -425,6 +445,8 @@ struct PendingMerges {
 struct PendingList {
   int4* list;   // kMaxPending entries
   int n = 0;
+  int wg_base = -1, wg_first = -1, nw = 0, wb = 0, wh = 0, wfirst = 0, wparts = 0;
+  __device__ bool in_workgroup(int, int) const { return false; }   // chunks move between workgroups
   __device__ void add(int b, int h, int first, int nparts) {
     if ((threadIdx.x & (kWave - 1)) == 0) list[n] = make_int4(b, h, first, nparts);
     ++n;
@@ -460,6 +482,28 @@ __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pa
     const size_t row = out_row<kMulti>(a, b, h, g) * D;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, o[nb]);
+    return;
+  }
+  if (pending.in_workgroup(first_chunk, last_chunk)) {
+    // Slot 0 if the pair began before this chunk (the chunk's first
+    // segment), else 1; lanes of columns past the group store nothing.
+    const int which = seg_start < chunk * C ? 0 : 1;
+    const int cols = a.cols;
+    const int slot = (chunk - pending.wg_first) * 2 + which;
+    const int base = uni(pending.wg_base);
+    if (static_cast<int>(n) < cols) {
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+        *reinterpret_cast<f32x4*>(lds_f32 + base + slot * cols * D + n * D + 16 * nb + 4 * c) = o[nb];
+      if (c == 0) lds_f32[base + 2 * kWavesPerGroup * cols * D + slot * cols + n] = lse;
+    }
+    if (which == 1) {
+      pending.nw = 1;
+      pending.wb = b;
+      pending.wh = h;
+      pending.wfirst = first_chunk;
+      pending.wparts = last_chunk - first_chunk + 1;
+    }
     return;
   }
   // Device-scope stores: written through to the point where every XCD sees
@@ -727,27 +771,22 @@ __device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int g
   return (pm.n > 0 && o0 == pm.nparts0 - 1 ? 1 : 0) | (pm.n > 1 && o1 == pm.nparts1 - 1 ? 2 : 0);
 }
 
-template <bool kBf16, int D, bool kMulti, int kGroupParts = 0>
-__device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_chunk, int nparts, int lane) {
+// Merges nparts partials of one (sequence b, KV head h, head block gb) and
+// writes the output rows: out = sum_i w_i o_i / sum_i w_i, w_i = exp(lse_i -
+// max lse).  One pass, kMergeGroup parts per round trip: all their loads are
+// issued before any is used, and the running maximum rescales the sums (the
+// same identity as the page loop).  load(i, l, v) fetches part i's lse and
+// this lane's features (lane (c, n): features 16 nb + 4c .. +3 of column
+// gb * 16 + n); parts past nparts read zeros and weigh nothing.  The same
+// arithmetic serves partials in global memory and in LDS, so both give the
+// same bits.  32 f32x4 registers of loads per group by default; fewer where
+// the caller holds other live registers.
+template <bool kBf16, int D, bool kMulti, int kGroupParts, class Load>
+__device__ void merge_core(const DecodeArgs& a, int b, int h, int gb, int nparts, int lane, Load load) {
   using O = Ops<kBf16, D>;
-  int32_t* ctr = merge_counter(a, b, h, gb);
   const uint32_t c = lane >> 4, n = lane & 15;
   const int g = gb * 16 + static_cast<int>(n);   // column
   const bool g_ok = g < a.cols;
-  const uint32_t G = a.cols;                      // partial rows per slot
-  const size_t row0 = (static_cast<size_t>(first_chunk) + static_cast<size_t>(b) * a.n_kv + h) * G + gb * 16;
-  // One resource per array over the nparts slots' rows of this head block;
-  // part i is at scalar offset i * G rows.  Lanes past the group read
-  // neighbouring rows (or zeros past the range) and store nothing.
-  const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, nparts * G * D * 4, PKV_RSRC_WORD3);
-  const __amdgpu_buffer_rsrc_t rl =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_lse + row0, 0, nparts * G * 4, PKV_RSRC_WORD3);
-  // One pass, kMergeGroup parts per round trip: all their loads are issued
-  // before any is used, and the running maximum rescales the sums (the same
-  // identity as the page loop).  Parts past nparts read zeros (outside the
-  // range) and weigh nothing.  32 f32x4 registers of loads per group by
-  // default; fewer where the caller holds other live registers.
   constexpr int kMergeGroup = kGroupParts > 0 ? kGroupParts : 32 / O::NV;
   float mx = kNoKeysMax, den = 0.f;   // parts that saw no key have lse -inf and weigh 0
   f32x4 o[O::NV];
@@ -757,14 +796,7 @@ __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_
     float l[kMergeGroup];
     f32x4 v[kMergeGroup][O::NV];
 #pragma unroll
-    for (int u = 0; u < kMergeGroup; ++u) {
-      const uint32_t i = i0 + u;
-      l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * n, 4 * G * i, kDeviceScope));
-#pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb)
-        v[u][nb] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 ro, 4 * (n * D + 16 * nb + 4 * c), 4 * G * D * i, kDeviceScope));
-    }
+    for (int u = 0; u < kMergeGroup; ++u) load(i0 + u, l[u], v[u]);
     float gm = mx;
 #pragma unroll
     for (int u = 0; u < kMergeGroup; ++u) gm = i0 + u < nparts ? fmaxf(gm, l[u]) : gm;
@@ -787,7 +819,57 @@ __device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_
 #pragma unroll
     for (int nb = 0; nb < O::NV; ++nb) O::store_out(a.out, row + 16 * nb + 4 * c, o[nb] * inv);
   }
+}
+
+// The global merge: the partials of chunks first_chunk .. + nparts - 1, read
+// with device-scope loads (their writers may be on other XCDs); then the
+// pair's arrival counter is reset for the next call.
+template <bool kBf16, int D, bool kMulti, int kGroupParts = 0>
+__device__ void merge_pair(const DecodeArgs& a, int b, int h, int gb, int first_chunk, int nparts, int lane) {
+  using O = Ops<kBf16, D>;
+  int32_t* ctr = merge_counter(a, b, h, gb);
+  const uint32_t c = lane >> 4, n = lane & 15;
+  const uint32_t G = a.cols;                      // partial rows per slot
+  const size_t row0 = (static_cast<size_t>(first_chunk) + static_cast<size_t>(b) * a.n_kv + h) * G + gb * 16;
+  // One resource per array over the nparts slots' rows of this head block;
+  // part i is at scalar offset i * G rows.  Lanes past the group read
+  // neighbouring rows (or zeros past the range) and store nothing.
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + row0 * D, 0, nparts * G * D * 4, PKV_RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_lse + row0, 0, nparts * G * 4, PKV_RSRC_WORD3);
+  merge_core<kBf16, D, kMulti, kGroupParts>(a, b, h, gb, nparts, lane, [&](int i, float& l, f32x4 (&v)[O::NV]) {
+    l = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * n, 4 * G * i, kDeviceScope));
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb)
+      v[nb] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, 4 * (n * D + 16 * nb + 4 * c), 4 * G * D * i, kDeviceScope));
+  });
   if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The workgroup merge (one 16-column block, static schedule): part i of the
+// pair is chunk first + i, whose wavefront left it in its LDS slot 1 (i = 0:
+// the pair starts in that chunk) or 0 (the pair began earlier).
+template <bool kBf16, int D, bool kMulti>
+__device__ void merge_workgroup(const DecodeArgs& a, const PendingMerges& p, int lane) {
+  using O = Ops<kBf16, D>;
+  const int c = lane >> 4, n = lane & 15;
+  const int cols = a.cols;
+  const int nparts = p.wparts;
+  merge_core<kBf16, D, kMulti, 0>(a, p.wb, p.wh, 0, nparts, lane, [&](int i, float& l, f32x4 (&v)[O::NV]) {
+    if (i < nparts && n < cols) {
+      const int slot = (p.wfirst + i - p.wg_first) * 2 + (i == 0 ? 1 : 0);
+      const float* so = lds_f32 + p.wg_base + slot * cols * D;
+      l = lds_f32[p.wg_base + 2 * kWavesPerGroup * cols * D + slot * cols + n];
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) v[nb] = *reinterpret_cast<const f32x4*>(so + n * D + 16 * nb + 4 * c);
+    } else {
+      l = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) v[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  });
 }
 
 // Rows of sequences with no pages when the decode kernel merges its own
@@ -1183,6 +1265,13 @@ split_kernel(DecodeArgs a) {
   typename KV::template Held<kNG == 1> held;
   held.lds = reinterpret_cast<uint32_t*>(smem + held_offset(a.batch)) + wave * kHeldWords;
   PendingMerges pending, unused;
+  constexpr bool kWgMerge = kNG == 1 && kNB == 1;
+  if constexpr (kWgMerge) {
+    if (a.wg_merge) {
+      pending.wg_base = a.wg_lds_offset;
+      pending.wg_first = static_cast<int>(blockIdx.x) * kWavesPerGroup;
+    }
+  }
   bool open = false, bad = false;
   int seg_start = 0;
   auto compute = [&](Regs& r, int pg, int p) {
@@ -1248,6 +1337,15 @@ split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < kNB; ++i)
       if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].finish(a, seg_start, chunk, C, bad, lane, i == 0 ? pending : unused);
+  }
+  // Pairs whose chunks all ran in this workgroup: merged from LDS once every
+  // wavefront has left its partials there (wavefronts that returned early
+  // are not waited for by the barrier).
+  if constexpr (kWgMerge) {
+    if (a.wg_merge) {
+      __syncthreads();
+      if (pending.nw) merge_workgroup<KV::kOutBf16, D, KV::kMulti>(a, pending, lane);
+    }
   }
   if (pending.n > 0) {
 #pragma unroll
@@ -2048,6 +2146,19 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                                         decode_prefix_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
   a.work = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                       decode_work_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
+  // Workgroup merges (static schedule, one wavefront per chunk and one
+  // 16-column block, in-kernel merge on) when their LDS slots fit.
+  size_t lds = r.lds;
+  a.wg_merge = 0;
+  a.wg_lds_offset = 0;
+  if (fuse && r.schedule == PKV_SCHEDULE_STATIC && cols <= 16) {
+    const size_t wg = static_cast<size_t>(kWavesPerGroup) * 2 * cols * (head_dim + 1) * sizeof(float);
+    if (r.lds + wg <= kMaxLdsBytes) {
+      a.wg_merge = 1;
+      a.wg_lds_offset = static_cast<int32_t>(r.lds / sizeof(int32_t));
+      lds = r.lds + wg;
+    }
+  }
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
@@ -2066,7 +2177,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
       grid = (r.n_items + chunks_per_group - 1) / chunks_per_group;
       fn = split_fn(dtype, head_dim, cols, q8, multi);
     }
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * kWavesPerGroup), r.lds, s, a);
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kWave * kWavesPerGroup), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("split kernel launch", e);
   }
