@@ -226,6 +226,11 @@ struct DecodeArgs {
   // one workgroup are merged through LDS (wg_lds_offset: int32 offset of the
   // partial slots in the kernel's dynamic LDS).
   int32_t wg_merge, wg_lds_offset;
+  // Split kernel's per-wavefront LDS after the prefix (int32 words):
+  // held_cap slots of held_tok_words (fused append's tokens; 0 without
+  // append), then held_cap result slots of held_res_words (0: results are
+  // written at once); held_wave_words per wavefront in all.
+  int32_t held_cap, held_tok_words, held_res_words, held_wave_words;
 };
 
 // Pages per sequence (those from its first attended block, see
@@ -528,30 +533,75 @@ __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pa
   if (a.counters != nullptr && nparts <= a.fuse_max_parts) pending.add(b, h, first_chunk, nparts);
 }
 
-// The new token of a fused append, held until the wavefront has no tile loads
+// Results of segments that end inside the page loop (pairs that end in the
+// middle of the chunk), held in this wavefront's LDS until its tile stream
+// has drained, for the same reason as the new tokens below: a result
+// written at once holds back the waits for every later tile.  Slot i at
+// float index base + i * words: o rows [cols][D], lse [cols], then
+// (b, h, n_pages, seg_start) in the last four words; up to cap slots, a
+// result past them is written at once.  Indices, not pointers (see
+// PendingMerges::wg_base).
+struct HeldResults {
+  int n = 0, cap = 0, base = 0, words = 0;
+  template <int D>
+  __device__ void put(const DecodeArgs& a, int b, int h, int n_pages, int seg_start, const f32x4 (&o)[D / 16],
+                      float lse, int lane) {
+    const int c = lane >> 4, col = lane & 15;
+    const int cols = a.cols;
+    const int sb = uni(base + n * words);
+    if (col < cols) {
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+        *reinterpret_cast<f32x4*>(lds_f32 + sb + col * D + 16 * nb + 4 * c) = o[nb];
+      if (c == 0) lds_f32[sb + cols * D + col] = lse;
+    }
+    if (lane == 0) *reinterpret_cast<int4*>(lds_f32 + sb + words - 4) = make_int4(b, h, n_pages, seg_start);
+    ++n;
+  }
+  // Writes the held results (see emit_segment), in the order they ended.
+  template <bool kOutBf16, int D, bool kMulti, class Pending>
+  __device__ void emit_all(const DecodeArgs& a, int gb, int chunk, int C, int lane, Pending& pending) {
+    const int c = lane >> 4, col = lane & 15;
+    const int rc = min(col, a.cols - 1);   // lanes past the group read a valid row and write nothing
+    for (int i = 0; i < n; ++i) {
+      const int sb = uni(base + i * words);
+      const int4 d = *reinterpret_cast<const int4*>(lds_f32 + sb + words - 4);
+      f32x4 o[D / 16];
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) o[nb] = *reinterpret_cast<const f32x4*>(lds_f32 + sb + rc * D + 16 * nb + 4 * c);
+      const float lse = lds_f32[sb + a.cols * D + rc];
+      emit_segment<kOutBf16, D, kMulti>(a, uni(d.x), uni(d.y), gb, uni(d.z), uni(d.w), chunk, C, o, lse, lane,
+                                        pending);
+    }
+    n = 0;
+  }
+};
+
+// New tokens of a fused append, held until the wavefront has no tile loads
 // in flight.  Vector memory operations retire in order, so a store issued in
 // the middle of the tile stream holds back the waits for every later tile;
 // measured on MI355X the token's stores cost 8 us of the 181-us GQA layer
 // when issued at the pair's last page (writing the whole 8-KiB tile back
-// instead, in full lines, cost as much).  The token waits in this
-// wavefront's slot of LDS (K row, then V row as 32-bit words), which costs
-// no registers; LDS accesses have their own counter.
+// instead, in full lines, cost as much).  A token waits in a slot of this
+// wavefront's LDS (K row, then V row as 32-bit words, then its destination),
+// which costs no registers; LDS accesses have their own counter.  A token
+// handed to an occupied slot first pushes the slot's token out to the pool.
 // kDefer false (kernels whose sibling wavefronts share a chunk): the token is
 // stored as soon as it is handed over.
 template <bool kBf16, int D, bool kDefer = true>
 struct HeldToken {
   using O = Ops<kBf16, D>;
-  static constexpr int kSlotWords = D * O::ES / 4 + D;   // K row, then D words of V
-  bool on = false;
-  char* kbase;        // (page, KV head) tiles the token goes to
-  char* vbase;
-  int s_new;          // its slot
-  uint32_t* lds;      // this wavefront's kSlotWords words
+  static constexpr int kRowWords = D * O::ES / 4 + D;   // K row, then D words of V
+  static constexpr int kSlotWords = kRowWords + 8;      // + K and V tile addresses, slot of the token
+  static_assert(kSlotWords <= kHeldWords, "a held token fits its LDS slot");
+  uint32_t* lds;        // slot 0 of this wavefront; slot i at lds + i * kSlotWords
+  uint32_t mask = 0;    // slots holding a token (uniform)
 
   // K: the 16-byte pieces of slot s_new (lanes with lane % 16 == s_new, as
   // loaded); V: its element of every feature row (lanes with lane / 16 ==
   // s_new / 4).
-  __device__ void store_regs(const u32x4 (&k)[O::NK], const uint32_t (&v)[O::NV], int lane) const {
+  __device__ static void store_regs(const u32x4 (&k)[O::NK], const uint32_t (&v)[O::NV], char* kbase, char* vbase,
+                                    int s_new, int lane) {
     const int c = lane >> 4, n = lane & 15;
     const __amdgpu_buffer_rsrc_t kr =
         __builtin_amdgcn_make_buffer_rsrc(kbase, 0, kBlock * D * O::ES, PKV_RSRC_WORD3);
@@ -574,42 +624,61 @@ struct HeldToken {
     }
   }
 
-  // Takes the token: k[i] in lanes (c, any n) is K piece 4i + c; v[nb] in
-  // lanes (any c, n) is V element 16 nb + n.  now: store it at once (the
-  // caller has no more tiles to stream).
-  __device__ void take(const u32x4 (&k)[O::NK], const uint32_t (&v)[O::NV], int lane, bool now) {
-    on = true;
+  // Writes the token of slot i to the pool and frees the slot.
+  __device__ void store_slot(int i, int lane) {
+    mask &= ~(1u << i);
+    const int c = lane >> 4, n = lane & 15;
+    const uint32_t* w = lds + i * kSlotWords;
+    const u32x4* lk = reinterpret_cast<const u32x4*>(w);
+    u32x4 k[O::NK];
+    uint32_t v[O::NV];
+#pragma unroll
+    for (int j = 0; j < O::NK; ++j) k[j] = lk[4 * j + c];
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) v[nb] = w[D * O::ES / 4 + 16 * nb + n];
+    const u32x4 dst = *reinterpret_cast<const u32x4*>(w + kRowWords);
+    auto u = [](uint32_t x) { return static_cast<uint64_t>(static_cast<uint32_t>(uni(static_cast<int>(x)))); };
+    const uint64_t kb = (u(dst.y) << 32) | u(dst.x);
+    const uint64_t vb = (u(dst.w) << 32) | u(dst.z);
+    const int s_new = uni(static_cast<int>(w[kRowWords + 4]));
+    store_regs(k, v, reinterpret_cast<char*>(kb), reinterpret_cast<char*>(vb), s_new, lane);
+  }
+
+  // Takes the token bound for slot s_new of the tiles at kbase / vbase: k[i]
+  // in lanes (c, any n) is K piece 4i + c; v[nb] in lanes (any c, n) is V
+  // element 16 nb + n.  It is held in LDS slot `slot`, or stored at once if
+  // `now` (the caller has no more tiles to stream, or no slot).
+  __device__ void take(const u32x4 (&k)[O::NK], const uint32_t (&v)[O::NV], char* kbase, char* vbase, int s_new,
+                       int slot, int lane, bool now) {
     if (!kDefer || now) {
-      store_regs(k, v, lane);
-      on = false;
-    } else {
-      const int c = lane >> 4, n = lane & 15;
-      u32x4* lk = reinterpret_cast<u32x4*>(lds);
-      if (n == 0) {
+      store_regs(k, v, kbase, vbase, s_new, lane);
+      return;
+    }
+    if ((mask >> slot) & 1u) store_slot(slot, lane);
+    mask |= 1u << slot;
+    const int c = lane >> 4, n = lane & 15;
+    uint32_t* w = lds + slot * kSlotWords;
+    u32x4* lk = reinterpret_cast<u32x4*>(w);
+    if (n == 0) {
 #pragma unroll
-        for (int i = 0; i < O::NK; ++i) lk[4 * i + c] = k[i];
-      }
-      if (c == 0) {
+      for (int i = 0; i < O::NK; ++i) lk[4 * i + c] = k[i];
+    }
+    if (c == 0) {
 #pragma unroll
-        for (int nb = 0; nb < O::NV; ++nb) lds[D * O::ES / 4 + 16 * nb + n] = v[nb];
-      }
+      for (int nb = 0; nb < O::NV; ++nb) w[D * O::ES / 4 + 16 * nb + n] = v[nb];
+    }
+    if (lane == 0) {
+      const uint64_t kb = reinterpret_cast<uint64_t>(kbase), vb = reinterpret_cast<uint64_t>(vbase);
+      *reinterpret_cast<u32x4*>(w + kRowWords) = u32x4{static_cast<uint32_t>(kb), static_cast<uint32_t>(kb >> 32),
+                                                        static_cast<uint32_t>(vb), static_cast<uint32_t>(vb >> 32)};
+      w[kRowWords + 4] = static_cast<uint32_t>(s_new);
     }
   }
 
-  // Writes the held token to the pool, if any.
+  // Writes every held token to the pool, in slot order.
   __device__ void store(int lane) {
     if constexpr (kDefer) {
-      if (!on) return;
-      on = false;
-      const int c = lane >> 4, n = lane & 15;
-      const u32x4* lk = reinterpret_cast<const u32x4*>(lds);
-      u32x4 k[O::NK];
-      uint32_t v[O::NV];
-#pragma unroll
-      for (int i = 0; i < O::NK; ++i) k[i] = lk[4 * i + c];
-#pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) v[nb] = lds[D * O::ES / 4 + 16 * nb + n];
-      store_regs(k, v, lane);
+      while (mask != 0) store_slot(__builtin_ctz(mask), lane);
     }
   }
 };
@@ -697,17 +766,14 @@ struct Segment {
     }
   }
 
-  // Hands the new token (already in knew/vnew) to `held`, to be written to
-  // page pg of the pool (kpool/vpool point at head h of page 0) once the
-  // wavefront's tile stream has drained.
+  // Hands the new token (already in knew/vnew) to `held` (slot `slot`), to
+  // be written to page pg of the pool (kpool/vpool point at head h of page 0)
+  // once the wavefront's tile stream has drained, or at once if `now`.
   template <bool kDefer>
   __device__ void hold(HeldToken<kBf16, D, kDefer>& t, char* kpool, char* vpool, size_t page_stride, int pg,
-                       int lane, bool now) const {
+                       int slot, int lane, bool now) const {
     const size_t off = static_cast<size_t>(pg) * page_stride;
-    t.kbase = kpool + off;
-    t.vbase = vpool + off;
-    t.s_new = s_new;
-    t.take(knew, vnew, lane, now);
+    t.take(knew, vnew, kpool + off, vpool + off, s_new, slot, lane, now);
   }
 
   // Page j of the segment holds sequence tokens 16 (fb + j) .. +15.  Columns
@@ -727,15 +793,19 @@ struct Segment {
 
   // Normalises the segment's result in place and writes it (see
   // emit_segment); the segment is closed afterwards.
-  template <class Pending>
-  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
-                         Pending& pending) {
+  // Normalises the result in place and returns its natural-log lse.
+  __device__ float normalise(bool bad) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = bad ? NAN : (!kMulti || lt > 0.f ? 1.0f / lt : 0.f);   // no key seen: zero row, lse -inf
 #pragma unroll
     for (int nb = 0; nb < O::NV; ++nb) acc[nb] *= inv;
-    const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
+    return bad ? NAN : (m + __log2f(lt)) * kLn2;
+  }
+  template <class Pending>
+  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
+                         Pending& pending) {
+    const float lse = normalise(bad);
     emit_segment<kBf16, D, kMulti>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
   }
 };
@@ -1047,9 +1117,7 @@ struct SegmentQ8 {
     }
   }
 
-  template <class Pending>
-  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
-                         Pending& pending) {
+  __device__ float normalise(bool bad) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     float ct = corr + __shfl_xor(corr, 16);
@@ -1057,7 +1125,12 @@ struct SegmentQ8 {
     const float inv = bad ? NAN : (!kMulti || lt > 0.f ? 1.0f / lt : 0.f);   // no key seen: zero row, lse -inf
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb) acc[nb] = (acc[nb] - ct) * inv;
-    const float lse = bad ? NAN : (m + __log2f(lt)) * kLn2;
+    return bad ? NAN : (m + __log2f(lt)) * kLn2;
+  }
+  template <class Pending>
+  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
+                         Pending& pending) {
+    const float lse = normalise(bad);
     emit_segment<true, D, kMulti>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
   }
 };
@@ -1262,8 +1335,20 @@ split_kernel(DecodeArgs a) {
   FlatCursor<KV::kMulti> cp;
   cp.seek(a, s_prefix, f0);
   typename KV::Seg seg[kNB];
+  // This wavefront's LDS: held_cap token slots (fused append), then, with one
+  // 16-column block per chunk, as many result slots.
+  const int held_base = held_offset(a.batch) + wave * a.held_wave_words;
   typename KV::template Held<kNG == 1> held;
-  held.lds = reinterpret_cast<uint32_t*>(smem + held_offset(a.batch)) + wave * kHeldWords;
+  held.lds = reinterpret_cast<uint32_t*>(smem + held_base);
+  constexpr bool kHoldResults = kNG == 1 && kNB == 1;
+  HeldResults results;
+  if constexpr (kHoldResults) {
+    if (a.held_res_words > 0) {
+      results.cap = a.held_cap;
+      results.base = held_base + a.held_cap * a.held_tok_words;
+      results.words = a.held_res_words;
+    }
+  }
   PendingMerges pending, unused;
   constexpr bool kWgMerge = kNG == 1 && kNB == 1;
   if constexpr (kWgMerge) {
@@ -1276,9 +1361,15 @@ split_kernel(DecodeArgs a) {
   int seg_start = 0;
   auto compute = [&](Regs& r, int pg, int p) {
     if (open && (cp.b != seg[0].b || cp.h != seg[0].h)) {
+      if (kHoldResults && results.n < results.cap) {
+        const float lse = seg[0].normalise(bad);
+        results.put<D>(a, seg[0].b, seg[0].h, seg[0].n_pages, seg_start, seg[0].acc, lse, lane);
+      } else {
 #pragma unroll
-      for (int i = 0; i < kNB; ++i)
-        if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].finish(a, seg_start, chunk, C, bad, lane, i == 0 ? pending : unused);
+        for (int i = 0; i < kNB; ++i)
+          if (i == 0 || (gblk + i) * 16 < a.cols)
+            seg[i].finish(a, seg_start, chunk, C, bad, lane, i == 0 ? pending : unused);
+      }
       open = false;
     }
     if (!open) {
@@ -1294,15 +1385,18 @@ split_kernel(DecodeArgs a) {
     bad |= !ok;
     // Every head block patches its registers; the first one stores the token:
     // at once on the chunk's last page (nothing follows to hold back), else
-    // after its tile stream (a second token in the same chunk pushes the
-    // first one out at once).
+    // after its tile stream.  With results held, the token takes the slot
+    // its segment's result will take (at once if there is none left);
+    // otherwise slot 0, whose previous token is pushed out.
     if constexpr (KV::kFusedAppend) {
       if (seg[0].append && cp.j == cp.n - 1) {
         seg[0].patch(r, lane);
         if (ok && gblk == 0) {
-          held.store(lane);
+          const bool by_result = kHoldResults && results.cap > 0;
+          const int slot = by_result ? results.n : 0;
+          const bool now = p == cnt - 1 || (by_result ? results.n >= results.cap : a.held_cap == 0);
           seg[0].hold(held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
-                      page_stride, pg, lane, p == cnt - 1);
+                      page_stride, pg, slot, lane, now);
         }
       }
     }
@@ -1333,6 +1427,7 @@ split_kernel(DecodeArgs a) {
       ++p;
     }
   }
+  if constexpr (kHoldResults) results.emit_all<KV::kOutBf16, D, KV::kMulti>(a, gblk, chunk, C, lane, pending);
   if (open) {
 #pragma unroll
     for (int i = 0; i < kNB; ++i)
@@ -1564,9 +1659,8 @@ dyn_kernel(DecodeArgs a) {
       if (seg.append && cp.j == cp.n - 1) {
         seg.patch(r, lane);
         if (ok) {
-          held.store(lane);
           seg.hold(held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
-                   page_stride, pg, lane, false);
+                   page_stride, pg, 0, lane, false);
         }
       }
     }
@@ -2146,17 +2240,46 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                                         decode_prefix_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
   a.work = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                       decode_work_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
-  // Workgroup merges (static schedule, one wavefront per chunk and one
-  // 16-column block, in-kernel merge on) when their LDS slots fit.
+  // Split kernel LDS (static schedule; r.lds, checked above, holds the
+  // prefix and one token slot per wavefront):
+  // - workgroup merges (one wavefront per chunk and one 16-column block,
+  //   in-kernel merge on) when their slots fit;
+  // - then per wavefront as many slots (up to kMaxHeldSlots) of held tokens
+  //   and, with one 16-column block, held results as the rest allows.
   size_t lds = r.lds;
   a.wg_merge = 0;
   a.wg_lds_offset = 0;
-  if (fuse && r.schedule == PKV_SCHEDULE_STATIC && cols <= 16) {
-    const size_t wg = static_cast<size_t>(kWavesPerGroup) * 2 * cols * (head_dim + 1) * sizeof(float);
-    if (r.lds + wg <= kMaxLdsBytes) {
+  a.held_cap = 0;
+  a.held_tok_words = 0;
+  a.held_res_words = 0;
+  a.held_wave_words = kHeldWords;
+  if (r.schedule == PKV_SCHEDULE_STATIC) {
+    const bool one_block = cols <= 16;
+    size_t wg_words = 0;
+    if (fuse && one_block) {
+      const size_t wg = static_cast<size_t>(kWavesPerGroup) * 2 * cols * (head_dim + 1);
+      if (r.lds + wg * sizeof(float) <= kMaxLdsBytes) wg_words = wg;
+    }
+    const int es = dtype == PKV_F32 ? 4 : 2;
+    const int tok = k_new != nullptr && !q8 ? head_dim * es / 4 + head_dim + 8 : 0;   // HeldToken::kSlotWords
+    int res = one_block ? ((cols * (head_dim + 1) + 3) & ~3) + 4 : 0;
+    const size_t avail = kMaxLdsBytes / sizeof(int32_t) - held_offset(batch) - wg_words;
+    int cap = res > 0 ? static_cast<int>(std::min<size_t>(kMaxHeldSlots, avail / (kWavesPerGroup * (tok + res))))
+                      : 0;
+    if (cap == 0) {   // no results held: one token slot (fits, see r.lds)
+      res = 0;
+      cap = tok > 0 ? 1 : 0;
+    }
+    a.held_cap = cap;
+    a.held_tok_words = tok;
+    a.held_res_words = res;
+    a.held_wave_words = cap * (tok + res);
+    const size_t held_end = held_offset(batch) + static_cast<size_t>(kWavesPerGroup) * a.held_wave_words;
+    lds = held_end * sizeof(int32_t);
+    if (wg_words > 0) {
       a.wg_merge = 1;
-      a.wg_lds_offset = static_cast<int32_t>(r.lds / sizeof(int32_t));
-      lds = r.lds + wg;
+      a.wg_lds_offset = static_cast<int32_t>(held_end);
+      lds += wg_words * sizeof(float);
     }
   }
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);

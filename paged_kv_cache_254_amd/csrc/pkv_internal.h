@@ -110,11 +110,14 @@ constexpr int kDynMinChunk = 16;
 // Pairs a wavefront of the dynamic kernel lists before counting their arrivals.
 constexpr int kMaxPending = 64;
 // LDS of the decode kernels (int32 units): the prefix [batch + 1] and the
-// per-wave sums, then, 16-byte aligned, each wavefront's held token of a
-// fused append (K row and V row of head_dim <= 128 elements: at most
-// kHeldWords words), then (dynamic kernel) each wavefront's list of pending
-// pairs (kMaxPending int4 entries).
-constexpr int kHeldWords = 128 * 4 / 4 + 128;
+// per-wave sums, then, 16-byte aligned, each wavefront's held tokens of a
+// fused append (K row and V row of head_dim <= 128 elements and the token's
+// destination: at most kHeldWords words each) and (split kernel, one
+// wavefront per chunk) its held results, then (dynamic kernel) each
+// wavefront's list of pending pairs (kMaxPending int4 entries).
+constexpr int kHeldWords = 128 * 4 / 4 + 128 + 8;
+// Result and token slots per wavefront of the split kernel, at most.
+constexpr int kMaxHeldSlots = 8;
 __host__ __device__ inline int held_offset(int batch) { return (batch + 1 + kWavesPerGroup + 3) & ~3; }
 __host__ __device__ inline int dyn_pending_offset(int batch) {
   return held_offset(batch) + kWavesPerGroup * kHeldWords;

@@ -273,6 +273,11 @@ STEP = [
     ("step_mqa64_bf16", 2, 64, 1, 128, "bf16", [150, 17], 5, 1),
     ("step_g3_f32_128", 2, 6, 2, 128, "f32", [64, 5], 2, 2),
     ("step_g32_ragged", 5, 64, 2, 128, "bf16", [0, 15, 16, 47, 130], 4, 1),
+    # many pairs ending inside one chunk: more than a wavefront's LDS slots
+    # for results and tokens held until its page loop ends
+    ("step_many_pairs_gqa", 24, 8, 2, 128, "bf16", [(7 * i) % 61 for i in range(24)], 1, 1),
+    ("step_many_pairs_f32", 20, 4, 4, 64, "f32", [(11 * i) % 45 for i in range(20)], 2, 1),
+    ("step_many_pairs_g16", 10, 32, 2, 128, "bf16", [(13 * i) % 50 for i in range(10)], 2, 1),
 ]
 
 
