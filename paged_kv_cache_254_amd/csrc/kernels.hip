@@ -287,6 +287,12 @@ __device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 // vector loads of K/V tiles in flight.
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
+// Length of sequence b (b wave-uniform), read the same way: a vector load
+// here would be waited for together with every tile load issued before it.
+__device__ inline int seq_len_of(const DecodeArgs& a, int b) {
+  return ((const const_i32*)a.seq_lens)[b];
+}
+
 template <bool kBf16, int D>
 struct PageRegs {
   using O = Ops<kBf16, D>;
@@ -714,7 +720,7 @@ struct Segment {
     const int qi = kMulti ? g / a.group : 0;
     const int gq = g - qi * a.group;
     hq = h * a.group + gq;
-    len = a.seq_lens[b];
+    len = seq_len_of(a, b);
     q_len = kMulti ? a.q_len : 1;
     window = kMulti ? a.window : 0;
     hi = len - q_len + qi + 1;
@@ -1023,7 +1029,7 @@ struct SegmentQ8 {
     const int qi = kMulti ? g / a.group : 0;
     const int gq = g - qi * a.group;
     hq = h * a.group + gq;
-    len = a.seq_lens[b];
+    len = seq_len_of(a, b);
     q_len = kMulti ? a.q_len : 1;
     window = kMulti ? a.window : 0;
     hi = len - q_len + qi + 1;
@@ -1143,7 +1149,7 @@ struct FlatCursor {
   int f, b, h, j, n, pb, fb;   // fb: block of the pair's first page (window start; 0 for one query token)
   __device__ static int first_block_of(const DecodeArgs& a, int b) {
     if constexpr (!kMulti) return 0;
-    return a.window > 0 ? uni(first_block(a.seq_lens[b], a.q_len, a.window)) : 0;
+    return a.window > 0 ? uni(first_block(seq_len_of(a, b), a.q_len, a.window)) : 0;
   }
   __device__ void seek(const DecodeArgs& a, const int32_t* s_prefix, int f0) {
     f = f0;
