@@ -1703,20 +1703,28 @@ dyn_kernel(DecodeArgs a) {
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
 // pair spans several chunks: out = sum_i w_i o_i / sum_i w_i with
-// w_i = exp(lse_i - max lse).  One workgroup per row.  After a block-wide
-// maximum of the lse, the 256 threads form 256 / (D / 8) slices of D / 8
-// threads; thread (slice, t) accumulates features 8t .. 8t+7 (two 16-byte
-// loads) of every n_slices-th partial, and the slices are summed through
-// LDS.  Rows of empty sequences become zeros, rows of invalid lengths NaN.
-// The page prefix comes from the workspace, where the split kernel stored it.
+// w_i = exp(lse_i - max lse).  One workgroup per (row, 32-feature slice), so
+// a few long pairs still spread over the whole chip.  The 256 threads form
+// 32 lanes of 8 threads; thread (lane, t) takes features 4t .. 4t+3 of the
+// slice from every 32nd partial and merges them in one pass with a running
+// maximum (the log-sum-exp identity applied to its own partials), eight
+// partials per round trip; the 32 lanes' (max, sum, accumulator) are then
+// merged through LDS by the same identity.  Rows of empty sequences become
+// zeros, rows of invalid lengths NaN.  The page prefix comes from the
+// workspace, where the split kernel stored it.
+constexpr int kCombineSlice = 32;                       // features per workgroup
+constexpr int kCombineTpp = kCombineSlice / 4;          // threads per partial
+constexpr int kCombineLanes = 256 / kCombineTpp;        // partials in parallel
 template <bool kBf16>
 __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
-  __shared__ float s_red[256];
-  __shared__ f32x4 s_acc[2 * 256];
+  __shared__ f32x4 s_acc[256];
+  __shared__ float s_m[256];
   __shared__ float s_den[256];
   const int32_t* s_prefix = a.prefix;   // stored by the split kernel
   const int G = a.cols;                       // partial rows per slot
-  const int row = blockIdx.x;                 // (b * q_len + qi) * n_q + hq
+  const int n_fs = D / kCombineSlice;
+  const int row = blockIdx.x / n_fs;          // (b * q_len + qi) * n_q + hq
+  const int f0 = (blockIdx.x - row * n_fs) * kCombineSlice;
   const int b = row / (a.q_len * a.n_q);
   const int bq = row - b * a.q_len * a.n_q;
   const int qi = bq / a.n_q;
@@ -1725,11 +1733,18 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   const int g = qi * a.group + (hq - h * a.group);   // column
   const int pair = b * a.n_kv + h;
   const int n = s_prefix[b + 1] - s_prefix[b];
-  const size_t row0 = static_cast<size_t>(row) * D;
+  const size_t row0 = static_cast<size_t>(row) * D + f0;
   const int tid = threadIdx.x;
-  auto store = [&](int d, float x) {
-    if (kBf16) static_cast<__bf16*>(a.out)[row0 + d] = static_cast<__bf16>(x);
-    else static_cast<float*>(a.out)[row0 + d] = x;
+  const int t = tid % kCombineTpp;
+  const int lane = tid / kCombineTpp;
+  auto store4 = [&](int d, f32x4 x) {
+    if (kBf16) {
+      __bf16* o = static_cast<__bf16*>(a.out) + row0 + d;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(x[e]);
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row0 + d) = x;
+    }
   };
   // With counters on, the decode kernel wrote the empty rows and merged the
   // pairs of at most fuse_max_parts chunks.
@@ -1737,7 +1752,7 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   if (n == 0) {
     if (fused) return;
     const float fill = (a.seq_lens[b] == 0) ? 0.f : NAN;
-    for (int d = tid; d < D; d += blockDim.x) store(d, fill);
+    if (tid < kCombineTpp) store4(4 * tid, f32x4{fill, fill, fill, fill});
     return;
   }
   const int total = a.n_kv * s_prefix[a.batch];
@@ -1750,69 +1765,62 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   const int nparts = c1 - c0 + 1;
   if (fused && nparts <= a.fuse_max_parts) return;
   const float* lse = a.part_lse + slot0 * G + g;
-  const float* po = a.part_o + (slot0 * G + g) * D;
+  const float* po = a.part_o + (slot0 * G + g) * D + f0 + 4 * t;
   const size_t stride_o = static_cast<size_t>(G) * D;
 
-  float mx = -INFINITY;
-  for (int s = tid; s < nparts; s += blockDim.x) mx = fmaxf(mx, lse[static_cast<size_t>(s) * G]);
-  s_red[tid] = mx;
-  __syncthreads();
-  for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-    if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-    __syncthreads();
-  }
-  mx = s_red[0];
-
-  const int per_slice = D / 8;              // threads per slice
-  const int n_slices = blockDim.x / per_slice;
-  const int t = tid % per_slice;
-  const int slice = tid / per_slice;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  // Sixteen partials per iteration, so each thread has 32 16-byte loads in
-  // flight and a row of up to 16 x n_slices partials (256 at head_dim 128)
-  // costs one round trip after the maximum's: the merge is bound by the
-  // latency of reading partials written from other XCDs, not by bandwidth
-  // (measured on MI355X: 64 rows x 256 partials took 9.4 us with four per
-  // iteration).  Partials past the end weigh zero and are not read.
-  constexpr int kUnroll = 16;
-  for (int s0 = slice; s0 < nparts; s0 += kUnroll * n_slices) {
-    float wgt[kUnroll];
-    f32x4 v0[kUnroll], v1[kUnroll];
+  // A maximum of -inf (no partial yet, or only empty ones) is replaced by 0
+  // in the exponents, so empty partials weigh 0 and a NaN lse stays NaN.
+  float m = -INFINITY, den = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // Eight partials per round trip: up to 256 partials per row cost one trip.
+  // The merge is bound by the latency of reading partials written from
+  // other XCDs, not by bandwidth.
+  constexpr int kUnroll = 8;
+  for (int s0 = lane; s0 < nparts; s0 += kUnroll * kCombineLanes) {
+    float l[kUnroll];
+    f32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int s = s0 + u * n_slices;
-      const bool ok = s < nparts;
-      const f32x4* src = reinterpret_cast<const f32x4*>(po + static_cast<size_t>(ok ? s : 0) * stride_o + 8 * t);
-      wgt[u] = 0.f;
-      v0[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ok) {
-        wgt[u] = __expf(lse[static_cast<size_t>(s) * G] - mx);
-        v0[u] = src[0];
-        v1[u] = src[1];
+      const int s = s0 + u * kCombineLanes;
+      l[u] = -INFINITY;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s < nparts) {
+        l[u] = lse[static_cast<size_t>(s) * G];
+        v[u] = *reinterpret_cast<const f32x4*>(po + static_cast<size_t>(s) * stride_o);
       }
     }
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) mn = fmaxf(mn, l[u]);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float r = __expf(m - ms);
+    acc *= r;
+    den *= r;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      acc0 += wgt[u] * v0[u];
-      acc1 += wgt[u] * v1[u];
-      den += wgt[u];
+      const float w = __expf(l[u] - ms);
+      acc += w * v[u];
+      den += w;
     }
+    m = mn;
   }
-  s_acc[2 * tid] = acc0;
-  s_acc[2 * tid + 1] = acc1;
+  s_acc[tid] = acc;
+  s_m[tid] = m;
   s_den[tid] = den;
   __syncthreads();
-  if (tid < D) {
-    const int tt = tid / 8, e = tid % 8;
-    float num = 0.f, dsum = 0.f;
-    for (int sl = 0; sl < n_slices; ++sl) {
-      const f32x4 v = s_acc[2 * (sl * per_slice + tt) + e / 4];
-      num += v[e % 4];
-      dsum += s_den[sl * per_slice];
+  if (tid < kCombineTpp) {
+    float mx = -INFINITY;
+    for (int ln = 0; ln < kCombineLanes; ++ln) mx = fmaxf(mx, s_m[ln * kCombineTpp + tid]);
+    const float ms = mx == -INFINITY ? 0.f : mx;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float dsum = 0.f;
+    for (int ln = 0; ln < kCombineLanes; ++ln) {
+      const int i = ln * kCombineTpp + tid;
+      const float w = __expf(s_m[i] - ms);
+      num += w * s_acc[i];
+      dsum += w * s_den[i];
     }
-    store(tid, num / dsum);
+    store4(4 * tid, num / dsum);
   }
 }
 
@@ -2312,7 +2320,8 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   }
   if (run_combine) {
     auto fn_c = dtype == PKV_F32 ? combine_kernel<false> : combine_kernel<true>;
-    hipLaunchKernelGGL(fn_c, dim3(batch * q_len * n_q_heads), dim3(256), 0, s, a, head_dim);
+    hipLaunchKernelGGL(fn_c, dim3(batch * q_len * n_q_heads * (head_dim / kCombineSlice)), dim3(256), 0, s, a,
+                       head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
