@@ -100,3 +100,28 @@ def test_large_groups_and_mha(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, 
     again, _ = _decode(pkv, w, c, n_items, mc, dec=dec)
     assert torch.equal(again, out)
     assert _counters_zero(dec)
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached,n_items", [
+    ("cb_300_bf16", 2, 8, 2, 128, "bf16", [4700, 30], 700),   # 294 one-page chunks per pair of sequence 0
+    ("cb_282_f32_64", 2, 4, 1, 64, "f32", [4500, 0], 300),    # head_dim 64: two 32-feature slices per row
+])
+def test_combine_kernel_rows_of_many_partials(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items):
+    # More than 256 partials per row: the combine kernel's loop takes a
+    # second round trip.  Fused mode sends these pairs to the combine kernel
+    # (more than 96 chunks); mode 1 merges every pair there; the split-only
+    # call followed by pkv_lse_combine takes the same kernel.
+    w, c, ref = _case(pkv, name, B, Hq, Hkv, D, dtype, cached, 74)
+    if cached[1] == 0:
+        c.seq_lens[1] = 0
+        ref[1] = 0.0
+    H.log(f"combine kernel: {name}")
+    for mode in (0, 1):
+        out, _ = _decode(pkv, w, c, n_items, 1, combine_mode=mode)
+        H.assert_close(H.f64(out), ref, dtype, f"{name} mode {mode}")
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, W.torch_dtype(w), c.max_blocks, n_items, 1)
+    out = torch.full_like(c.q, float("nan"))
+    dec.split(c.q, c.k_pages, c.v_pages, c.bt, c.seq_lens, w.scale, out)
+    dec.combine(c.seq_lens, out, c.max_blocks)
+    torch.cuda.synchronize()
+    H.assert_close(H.f64(out), ref, dtype, f"{name} split + combine")
