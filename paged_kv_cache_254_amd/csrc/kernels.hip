@@ -2297,6 +2297,10 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
     }
   }
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
+  // One combine workgroup per 32-feature slice of an output row.
+  const int64_t grid_c = static_cast<int64_t>(batch) * q_len * n_q_heads * (head_dim / kCombineSlice);
+  if (run_combine && grid_c > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, f + ": too many output rows for the combine kernel");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (do_split) {
     const bool multi = q_len > 1 || window > 0;
@@ -2320,8 +2324,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   }
   if (run_combine) {
     auto fn_c = dtype == PKV_F32 ? combine_kernel<false> : combine_kernel<true>;
-    hipLaunchKernelGGL(fn_c, dim3(batch * q_len * n_q_heads * (head_dim / kCombineSlice)), dim3(256), 0, s, a,
-                       head_dim);
+    hipLaunchKernelGGL(fn_c, dim3(static_cast<uint32_t>(grid_c)), dim3(256), 0, s, a, head_dim);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }
