@@ -75,6 +75,10 @@ CASES = [
     (2, 32, 8, 128, "bf16", [333, 90], 2, 64, 6, 2),           # window of 64, 8 columns
     (2, 8, 2, 128, "bf16", [30, 50], 3, 100, 3, 1),            # window longer than the sequences
     (3, 8, 2, 128, "bf16", [1700, 45, 19], 4, 0, 260, 1),      # > 96 chunks: combine kernel too
+    # 103 one-page chunks per pair, so the combine kernel merges; the 32 query
+    # tokens' windows start in different pages, so the first chunks hold
+    # empty (lse -inf) rows for the later queries
+    (2, 4, 2, 128, "bf16", [3000, 70], 32, 1600, 300, 1),
 ]
 
 
