@@ -148,47 +148,67 @@ def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0):
     L = S["layers"][0]
     rng = np.random.default_rng(0)
     pick = list(rng.permutation(w.batch))
-    done, secs, kv_bytes, toks = 0, 0.0, 0, 0
-    for b in pick:
+    multi = q_len > 1 or window > 0
+    read = multi_kv_tokens(S["att"], q_len, window) if multi else S["att"]
+
+    def host_inputs(b):
+        """Host copies of sequence b's pages (relabelled 0..n-1) and rows; not timed."""
         nblk = (int(S["att"][b]) + 15) // 16
         pages = torch.from_numpy(S["bt_np"][b, :nblk].astype(np.int64)).to(L.k_pages.device)
-        qb = L.q[b:b + 1].double().cpu().numpy()
         bt = np.arange(nblk, dtype=np.int32)[None, :]
-        multi = q_len > 1 or window > 0
+        qb = L.q[b:b + 1].double().cpu().numpy()
         if multi:
-            kp = L.k_pages.index_select(0, pages).double().cpu().numpy()
-            vp = L.v_pages.index_select(0, pages).double().cpu().numpy()
-            t0 = time.perf_counter()
+            return (qb, L.k_pages.index_select(0, pages).double().cpu().numpy(),
+                    L.v_pages.index_select(0, pages).double().cpu().numpy(), bt)
+        if kv == "u8":
+            return (qb, L.k_pages.index_select(0, pages).cpu().numpy(), L.v_pages.index_select(0, pages).cpu().numpy(),
+                    L.meta.index_select(0, pages).cpu().numpy(), bt, L.k_new[b:b + 1].float().cpu().numpy(),
+                    L.v_new[b:b + 1].float().cpu().numpy())
+        return (qb, L.k_pages.index_select(0, pages).double().cpu().numpy(),
+                L.v_pages.index_select(0, pages).double().cpu().numpy(), bt,
+                L.k_new[b:b + 1].double().cpu().numpy(), L.v_new[b:b + 1].double().cpu().numpy())
+
+    def run_oracle(b, x):
+        if multi:
+            qb, kp, vp, bt = x
             OA.decode_multi(qb, kp, vp, bt, [int(S["att"][b])], q_len, w.n_q_heads, w.n_kv_heads, 16, w.scale,
                             window)
         elif kv == "u8":
-            kp = L.k_pages.index_select(0, pages).cpu().numpy()
-            vp = L.v_pages.index_select(0, pages).cpu().numpy()
-            mp = L.meta.index_select(0, pages).cpu().numpy()
-            kn = L.k_new[b:b + 1].float().cpu().numpy()
-            vn = L.v_new[b:b + 1].float().cpu().numpy()
-            t0 = time.perf_counter()
+            qb, kp, vp, mp, bt, kn, vn = x
             k2, v2, m2 = KQ.append(kp, vp, mp, bt, [int(S["cached"][b])], kn, vn, 16)
             KQ.decode(qb, k2, v2, m2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
         else:
-            kp = L.k_pages.index_select(0, pages).double().cpu().numpy()
-            vp = L.v_pages.index_select(0, pages).double().cpu().numpy()
-            kn = L.k_new[b:b + 1].double().cpu().numpy()
-            vn = L.v_new[b:b + 1].double().cpu().numpy()
-            t0 = time.perf_counter()
+            qb, kp, vp, bt, kn, vn = x
             k2, v2 = OA.append(kp, vp, bt, [int(S["cached"][b])], kn, vn, 16)
             OA.decode(qb, k2, v2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
-        secs += time.perf_counter() - t0
-        done += 1
-        read = multi_kv_tokens(S["att"], q_len, window) if multi else S["att"]
-        kv_bytes += int(read[b]) * S["kv_bytes_layer"] // int(read.sum())
-        toks += q_len
-        if secs >= budget_s:
-            break
+
+    # Whole sequences in a seeded order until the budget is used.  A layer the
+    # oracle finishes within the budget is run again (from host copies kept
+    # after the first pass, at most 8 GiB of them), so the timing covers about
+    # budget_s of CPU work either way.
+    kept, kept_bytes, cap = {}, 0, 8 << 30
+    done, passes, secs, kv_bytes = 0, 0, 0.0, 0
+    while secs < budget_s and passes < 64:
+        for b in pick:
+            x = kept.get(b)
+            if x is None:
+                x = host_inputs(b)
+                nb = sum(a.nbytes for a in x)
+                if kept_bytes + nb <= cap:
+                    kept[b] = x
+                    kept_bytes += nb
+            t0 = time.perf_counter()
+            run_oracle(b, x)
+            secs += time.perf_counter() - t0
+            done += 1
+            kv_bytes += int(read[b]) * S["kv_bytes_layer"] // int(read.sum())
+            if secs >= budget_s:
+                break
+        passes += 1
+    what = f"{q_len}-token decode" if multi else "append + decode"
     return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.batch} sequences of one layer "
-                      f"({f'{q_len}-token decode' if q_len > 1 or window > 0 else 'append + decode'}, "
-                      f"all {w.n_q_heads} query heads), {kv_bytes / 2**20:.0f} MiB of KV, {secs:.1f} s",
+            "sample": f"{done} whole-sequence runs over {min(done, w.batch)} of the {w.batch} sequences of one layer "
+                      f"({what}, all {w.n_q_heads} query heads), {kv_bytes / 2**20:.0f} MiB of KV, {secs:.1f} s",
             "seconds": secs}
 
 
