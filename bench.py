@@ -456,8 +456,11 @@ def main():
             "algorithmic_bytes_per_launch": S["kv_bytes_layer"],
         },
         "split_median_ms": round(float(np.median(split_ms)), 5),
+        "split_min_ms": round(float(np.min(split_ms)), 5),
+        "split_max_ms": round(float(np.max(split_ms)), 5),
         "combine_avg_ms": None if one_kernel or multi else round(float(np.mean(comb_ms)), 5),
         "hbm_read_probe_gbs": None if probe is None else round(probe, 1),
+        "pct_of_read_probe": None if probe is None else round(100 * value / probe, 1),
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),
     }
