@@ -1703,28 +1703,30 @@ dyn_kernel(DecodeArgs a) {
 
 // Merge the partials of one output row (sequence b, query head hq) whose KV
 // pair spans several chunks: out = sum_i w_i o_i / sum_i w_i with
-// w_i = exp(lse_i - max lse).  One workgroup per (row, 32-feature slice), so
-// a few long pairs still spread over the whole chip.  The 256 threads form
-// 32 lanes of 8 threads; thread (lane, t) takes features 4t .. 4t+3 of the
-// slice from every 32nd partial and merges them in one pass with a running
-// maximum (the log-sum-exp identity applied to its own partials), eight
-// partials per round trip; the 32 lanes' (max, sum, accumulator) are then
-// merged through LDS by the same identity.  Rows of empty sequences become
-// zeros, rows of invalid lengths NaN.  The page prefix comes from the
-// workspace, where the split kernel stored it.
-constexpr int kCombineSlice = 32;                       // features per workgroup
-constexpr int kCombineTpp = kCombineSlice / 4;          // threads per partial
-constexpr int kCombineLanes = 256 / kCombineTpp;        // partials in parallel
+// w_i = exp(lse_i - max lse).  One workgroup per (row, slice of F features),
+// F = D / n_fs: with few rows (a few long pairs) a row is split into slices
+// of down to 32 features so the merge still spreads over the chip; with many
+// rows a workgroup takes a whole row.  The 256 threads form 256 / (F / 4)
+// partial lanes of F / 4 threads; thread (lane, t) takes features 4t .. 4t+3
+// of the slice from every lane-count-th partial and merges them in one pass
+// with a running maximum (the log-sum-exp identity applied to its own
+// partials), eight partials per round trip; the lanes' (max, sum,
+// accumulator) are then merged through LDS by the same identity.  Rows of
+// empty sequences become zeros, rows of invalid lengths NaN.  The page prefix
+// comes from the workspace, where the split kernel stored it.
+constexpr int kCombineMinSlice = 32;   // features per workgroup, at the finest split
 template <bool kBf16>
-__global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
+__global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D, int n_fs) {
   __shared__ f32x4 s_acc[256];
   __shared__ float s_m[256];
   __shared__ float s_den[256];
   const int32_t* s_prefix = a.prefix;   // stored by the split kernel
   const int G = a.cols;                       // partial rows per slot
-  const int n_fs = D / kCombineSlice;
+  const int F = D / n_fs;                     // features of this workgroup
+  const int tpp = F / 4;                      // threads per partial
+  const int n_lanes = 256 / tpp;              // partials in parallel
   const int row = blockIdx.x / n_fs;          // (b * q_len + qi) * n_q + hq
-  const int f0 = (blockIdx.x - row * n_fs) * kCombineSlice;
+  const int f0 = (blockIdx.x - row * n_fs) * F;
   const int b = row / (a.q_len * a.n_q);
   const int bq = row - b * a.q_len * a.n_q;
   const int qi = bq / a.n_q;
@@ -1735,8 +1737,8 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   const int n = s_prefix[b + 1] - s_prefix[b];
   const size_t row0 = static_cast<size_t>(row) * D + f0;
   const int tid = threadIdx.x;
-  const int t = tid % kCombineTpp;
-  const int lane = tid / kCombineTpp;
+  const int t = tid % tpp;
+  const int lane = tid / tpp;
   auto store4 = [&](int d, f32x4 x) {
     if (kBf16) {
       __bf16* o = static_cast<__bf16*>(a.out) + row0 + d;
@@ -1752,7 +1754,7 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   if (n == 0) {
     if (fused) return;
     const float fill = (a.seq_lens[b] == 0) ? 0.f : NAN;
-    if (tid < kCombineTpp) store4(4 * tid, f32x4{fill, fill, fill, fill});
+    if (tid < tpp) store4(4 * tid, f32x4{fill, fill, fill, fill});
     return;
   }
   const int total = a.n_kv * s_prefix[a.batch];
@@ -1772,16 +1774,16 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   // in the exponents, so empty partials weigh 0 and a NaN lse stays NaN.
   float m = -INFINITY, den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // Eight partials per round trip: up to 256 partials per row cost one trip.
-  // The merge is bound by the latency of reading partials written from
-  // other XCDs, not by bandwidth.
+  // Eight partials per round trip: with 32-feature slices, up to 256
+  // partials per row cost one trip.  The merge is bound by the latency of
+  // reading partials written from other XCDs, not by bandwidth.
   constexpr int kUnroll = 8;
-  for (int s0 = lane; s0 < nparts; s0 += kUnroll * kCombineLanes) {
+  for (int s0 = lane; s0 < nparts; s0 += kUnroll * n_lanes) {
     float l[kUnroll];
     f32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int s = s0 + u * kCombineLanes;
+      const int s = s0 + u * n_lanes;
       l[u] = -INFINITY;
       v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (s < nparts) {
@@ -1808,20 +1810,29 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeArgs a, int D) {
   s_m[tid] = m;
   s_den[tid] = den;
   __syncthreads();
-  if (tid < kCombineTpp) {
+  if (tid < tpp) {
     float mx = -INFINITY;
-    for (int ln = 0; ln < kCombineLanes; ++ln) mx = fmaxf(mx, s_m[ln * kCombineTpp + tid]);
+    for (int ln = 0; ln < n_lanes; ++ln) mx = fmaxf(mx, s_m[ln * tpp + tid]);
     const float ms = mx == -INFINITY ? 0.f : mx;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float dsum = 0.f;
-    for (int ln = 0; ln < kCombineLanes; ++ln) {
-      const int i = ln * kCombineTpp + tid;
+    for (int ln = 0; ln < n_lanes; ++ln) {
+      const int i = ln * tpp + tid;
       const float w = __expf(s_m[i] - ms);
       num += w * s_acc[i];
       dsum += w * s_den[i];
     }
     store4(4 * tid, num / dsum);
   }
+}
+
+// Slices per combine row: rows are split (down to 32 features) only while
+// the grid would stay below 512 workgroups, so a few long pairs spread over
+// the chip and a large batch keeps one workgroup per row.
+inline int combine_slices(int64_t rows, int head_dim) {
+  int n_fs = 1;
+  while (n_fs * 2 * kCombineMinSlice <= head_dim && rows * n_fs * 2 <= 512) n_fs *= 2;
+  return n_fs;
 }
 
 // kv_append: one wavefront per (sequence, KV head); a bit copy of the new key
@@ -2297,8 +2308,10 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
     }
   }
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
-  // One combine workgroup per 32-feature slice of an output row.
-  const int64_t grid_c = static_cast<int64_t>(batch) * q_len * n_q_heads * (head_dim / kCombineSlice);
+  // One combine workgroup per slice of an output row.
+  const int64_t combine_rows = static_cast<int64_t>(batch) * q_len * n_q_heads;
+  const int n_fs = combine_slices(combine_rows, head_dim);
+  const int64_t grid_c = combine_rows * n_fs;
   if (run_combine && grid_c > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, f + ": too many output rows for the combine kernel");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -2324,7 +2337,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   }
   if (run_combine) {
     auto fn_c = dtype == PKV_F32 ? combine_kernel<false> : combine_kernel<true>;
-    hipLaunchKernelGGL(fn_c, dim3(static_cast<uint32_t>(grid_c)), dim3(256), 0, s, a, head_dim);
+    hipLaunchKernelGGL(fn_c, dim3(static_cast<uint32_t>(grid_c)), dim3(256), 0, s, a, head_dim, n_fs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("combine kernel launch", e);
   }

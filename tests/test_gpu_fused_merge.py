@@ -125,3 +125,18 @@ def test_combine_kernel_rows_of_many_partials(pkv, name, B, Hq, Hkv, D, dtype, c
     dec.combine(c.seq_lens, out, c.max_blocks)
     torch.cuda.synchronize()
     H.assert_close(H.f64(out), ref, dtype, f"{name} split + combine")
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached", [
+    ("cb_rows_bf16", 6, 64, 8, 128, "bf16", [300, 17, 95, 250, 40, 1000]),   # 384 rows: one workgroup per row
+    ("cb_rows_f32_64", 5, 64, 4, 64, "f32", [120, 0, 77, 400, 33]),           # 320 rows, head_dim 64
+])
+def test_combine_kernel_many_rows(pkv, name, B, Hq, Hkv, D, dtype, cached):
+    # Enough output rows that the combine kernel gives each row one workgroup
+    # (the split into feature slices is for a few long rows).
+    w, c, ref = _case(pkv, name, B, Hq, Hkv, D, dtype, cached, 75)
+    H.log(f"combine kernel, many rows: {name}")
+    out, dec = _decode(pkv, w, c, 60, 2, combine_mode=1)
+    H.assert_close(H.f64(out), ref, dtype, name)
+    again, _ = _decode(pkv, w, c, 60, 2, dec=dec)
+    assert torch.equal(again, out)
