@@ -105,6 +105,7 @@ def test_large_groups_and_mha(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items, 
 @pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached,n_items", [
     ("cb_300_bf16", 2, 8, 2, 128, "bf16", [4700, 30], 700),   # 294 one-page chunks per pair of sequence 0
     ("cb_282_f32_64", 2, 4, 1, 64, "f32", [4500, 0], 300),    # head_dim 64: two 32-feature slices per row
+    ("cb_300_f32_128", 2, 8, 2, 128, "f32", [4700, 30], 700),  # fp32 rows in four 32-feature slices
 ])
 def test_combine_kernel_rows_of_many_partials(pkv, name, B, Hq, Hkv, D, dtype, cached, n_items):
     # More than 256 partials per row: the combine kernel's loop takes a
@@ -130,6 +131,7 @@ def test_combine_kernel_rows_of_many_partials(pkv, name, B, Hq, Hkv, D, dtype, c
 @pytest.mark.parametrize("name,B,Hq,Hkv,D,dtype,cached", [
     ("cb_rows_bf16", 6, 64, 8, 128, "bf16", [300, 17, 95, 250, 40, 1000]),   # 384 rows: one workgroup per row
     ("cb_rows_f32_64", 5, 64, 4, 64, "f32", [120, 0, 77, 400, 33]),           # 320 rows, head_dim 64
+    ("cb_rows_f32_128", 5, 64, 8, 128, "f32", [200, 9, 77, 500, 33]),         # 320 fp32 rows of 128 features
 ])
 def test_combine_kernel_many_rows(pkv, name, B, Hq, Hkv, D, dtype, cached):
     # Enough output rows that the combine kernel gives each row one workgroup
