@@ -290,9 +290,8 @@ def main():
                       args.min_chunk, device=device, combine_mode=1 if args.separate_combine else 0,
                       schedule=args.schedule)
     # One kernel per layer when every pair can be merged inside the decode
-    # kernel (a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks).
-    # (the library's rule: a pair spans at most ceil(max_blocks / min_chunk) + 1
-    # chunks, and pairs of at most 96 are merged inside the decode kernel)
+    # kernel: a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks, and
+    # the library merges pairs of at most 96 chunks there.
     one_kernel = not args.separate_combine and -(-S["mb"] // dec.min_chunk_pages) + 1 <= 96
     layers = S["layers"]
     n_layers = w.n_layers
