@@ -106,3 +106,37 @@ def test_one_token_equals_single_token_decode(pkv):
     dec.attn_multi(c.q[:, None].contiguous(), c.k_pages, c.v_pages, c.bt, c.seq_lens, 1, w.scale, b)
     torch.cuda.synchronize()
     assert torch.equal(a, b[:, 0])
+
+
+@pytest.mark.parametrize("T,window", [(4, 0), (4, 1024)])
+def test_full_size_sampled_multi(pkv, T, window):
+    # The full-size GQA layer with q_len query tokens per sequence (and a
+    # sliding window), the library's default launch, checked on sampled
+    # sequences against the oracle run on just their pages.
+    w = W.get("llama3_8b_gqa")
+    c = H.setup(w, device="cuda")
+    # every attended token must be cached: append the step's token first
+    # (the other slots past each length stay NaN)
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
+    torch.cuda.synchronize()
+    att = c.attended.astype(np.int64)
+    B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+    q = torch.stack([W.make_q(w, t, "cuda") for t in range(T)], dim=1).contiguous()
+    rng = np.random.default_rng(12)
+    bs = sorted({0, B - 1, int(np.argmax(att)), int(np.argmin(att)), int(rng.integers(B))})
+    host = {}
+    for b in bs:
+        nblk = (int(att[b]) + 15) // 16
+        pages = torch.from_numpy(c.bt_np[b, :nblk].astype(np.int64)).cuda()
+        host[b] = (H.f64(c.k_pages.index_select(0, pages)), H.f64(c.v_pages.index_select(0, pages)), nblk)
+    dec = pkv.Decoder(B, Hq * T, Hkv, D, W.torch_dtype(w), c.max_blocks)
+    out = torch.full((B, T, Hq, D), float("nan"), dtype=W.torch_dtype(w), device="cuda")
+    H.log(f"multi full T={T} W={window} (n_items={dec.n_items})")
+    dec.attn_multi(q, c.k_pages, c.v_pages, c.bt, c.seq_lens, T, w.scale, out, window)
+    torch.cuda.synchronize()
+    for b in bs:
+        kp, vp, nblk = host[b]
+        sub = np.arange(nblk, dtype=np.int32)[None, :]
+        ref = OA.decode_multi(H.f64(q[b:b + 1]), kp, vp, sub, [int(att[b])], T, Hq, Hkv, 16, w.scale, window)
+        mx, mean, rel = H.assert_close(H.f64(out[b:b + 1]), ref, "bf16", f"multi full b={b}")
+        H.log(f"  b={b} ({int(att[b])} tokens): max abs {mx:.2e} rel RMS {rel:.2e}")

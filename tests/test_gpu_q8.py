@@ -162,3 +162,54 @@ def test_q8_rejects_mismatched_calls(pkv):
         dec(d.q, d.kc, d.vc, d.bt, d.lens, w.scale, out)
     with pytest.raises(pkv.PkvError):      # misaligned meta
         dec.attn_q8(d.q, d.kc, d.vc, d.meta.view(-1)[1:], d.bt, d.lens, w.scale, out)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_mha", "llama3_8b_gqa"])
+def test_full_size_sampled_q8(pkv, name):
+    # The full-size layer on the 8-bit cache in the benchmark's launch
+    # configuration (library defaults, quantizing append then decode), checked
+    # on sampled sequences against the oracle run on just their pages.
+    w = W.get(name)
+    cached = W.cached_lens(w).astype(np.int64)
+    att = cached + 1
+    P = W.pool_pages(w)
+    pool = OraclePool(P, W.free_order(w))
+    for b in range(w.batch):
+        pool.reserve(b, int(att[b]))
+    mb = int(max((att + 15) // 16))
+    bt_np = pool.block_table(range(w.batch), mb)
+    H.log(f"q8 full {name}: setup")
+    kc, vc, meta = W.make_q8_pools(w, 0, "cuda")
+    held = np.zeros((P, 16), dtype=bool)
+    for b in range(w.batch):
+        t = np.arange(int(cached[b]))
+        held[bt_np[b, t // 16], t % 16] = True
+    meta[torch.from_numpy(~held).cuda()[:, None, None, :].expand_as(meta)] = float("nan")
+    q = W.make_q(w, 0, "cuda")
+    k_new, v_new = W.make_new_kv(w, 0, "cuda")
+    rng = np.random.default_rng(11)
+    bs = sorted({0, w.batch - 1, int(np.argmax(att)), int(np.argmin(att)), int(rng.integers(w.batch))})
+    host = {}
+    for b in bs:   # host copies of the sampled sequences' pages, taken before the step
+        nblk = (int(att[b]) + 15) // 16
+        pages = torch.from_numpy(bt_np[b, :nblk].astype(np.int64)).cuda()
+        host[b] = (pages, kc.index_select(0, pages).cpu().numpy(), vc.index_select(0, pages).cpu().numpy(),
+                   meta.index_select(0, pages).cpu().numpy())
+    bt = torch.from_numpy(bt_np).cuda()
+    lens = torch.from_numpy(att.astype(np.int32)).cuda()
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.uint8, mb)
+    out = torch.full_like(q, float("nan"))
+    H.log(f"q8 full {name}: step (n_items={dec.n_items})")
+    dec.step_q8(q, k_new, v_new, kc, vc, meta, bt, lens, w.scale, out)
+    torch.cuda.synchronize()
+    for b in bs:
+        pages, kp, vp, mp = host[b]
+        sub = np.arange(len(pages), dtype=np.int32)[None, :]
+        k2, v2, m2 = KQ.append(kp, vp, mp, sub, [int(cached[b])], k_new[b:b + 1].float().cpu().numpy(),
+                               v_new[b:b + 1].float().cpu().numpy(), 16)
+        ref = KQ.decode(q[b:b + 1].double().cpu().numpy(), k2, v2, m2, sub, [int(att[b])], w.n_q_heads,
+                        w.n_kv_heads, 16, w.scale)
+        mx, mean, rel = H.assert_close(H.f64(out[b:b + 1]), ref, "bf16", f"q8 full {name} b={b}")
+        H.log(f"  b={b} ({int(att[b])} tokens): max abs {mx:.2e} rel RMS {rel:.2e}")
+        assert same_bits(kc.index_select(0, pages), k2) and same_bits(vc.index_select(0, pages), v2)
+        assert same_bits(meta.index_select(0, pages), m2)
