@@ -23,7 +23,10 @@ Modules:
                    codes, exact grid round trips, the half-step bound, and the
                    decode above run on explicitly dequantized pools).
 
-Parity status: every function here has at least one pin in
-``tests/test_oracle_*.py``; none is "parity unpinned".
+Parity status: every function here is called by at least one pin in
+``tests/test_oracle_*.py``, and ``tests/test_oracle_mutations.py`` plants a
+plausible mistake in each (a dropped term, a wrong index, a swapped operand,
+a reversed order) and checks that one of those pins fails; none is "parity
+unpinned".
 """
 from . import attention, kv_bytes, kv_quant, page_pool  # noqa: F401

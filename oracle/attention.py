@@ -22,13 +22,15 @@ What is computed, and where the pages define it:
   to physical blocks ("Inference Engines" chapter 17, "The Breakthrough";
   CS336 notes, "PagedAttention (vLLM)").  Token t of sequence b is slot t % bs
   of physical page block_table[b][t // bs].
-* The online softmax keeps a running maximum and sum so that partial results
-  over different key blocks can be rescaled and combined exactly
-  (byteknotlabs "Efficient inference", section "FlashAttention: exact attention
-  without the matrix"; its formula was lost from the page).  ``partial`` and
-  ``lse_combine`` are that identity written out: a partial over a token range is
-  its normalised output plus the natural log of its softmax denominator, and
-  the combine reweights partials by exp(lse - max lse).
+* Split attention: the page on FlashAttention (byteknotlabs "Efficient
+  inference", section "FlashAttention: exact attention without the matrix")
+  states that attention over a long key sequence can be computed block by
+  block, tracking the largest score and the sum of exponentials seen so far,
+  and that the per-block results then merge into the exact answer (the
+  formula itself did not survive on the page).  ``partial`` and
+  ``lse_combine`` write that merge out: a partial over a token range is its
+  normalised output plus the natural log of its softmax denominator, and the
+  merge weighs each partial by exp(lse - max lse).
 * Appending: each decode step writes the new token's K and V into each layer's
   cache (docs section "What the KV cache stores per layer").
 * Several query tokens at once (``decode_multi``): the last q_len cached
@@ -50,19 +52,6 @@ import numpy as np
 
 def _as_f64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
-
-
-def key_tile(k_pages: np.ndarray, page: int, head: int) -> np.ndarray:
-    """The [bs][D] keys held by one (page, KV head): element (t, c * X + x)
-    sits at k_pages[page, head, c, t, x]."""
-    chunks, bs, x = k_pages.shape[2], k_pages.shape[3], k_pages.shape[4]
-    return k_pages[page, head].transpose(1, 0, 2).reshape(bs, chunks * x)
-
-
-def value_tile(v_pages: np.ndarray, page: int, head: int) -> np.ndarray:
-    """The [bs][D] values held by one (page, KV head): element (t, d) sits at
-    v_pages[page, head, d, t]."""
-    return v_pages[page, head].T
 
 
 def gather(k_pages, v_pages, block_table_row, n_tokens: int,
@@ -194,15 +183,6 @@ def decode_multi(q, k_pages, v_pages, block_table, seq_lens, q_len: int, n_q_hea
                 h = hq // group
                 out[b, i, hq] = attend(q[b, i, hq], K[lo:hi, h, :], V[lo:hi, h, :], scale)
     return out
-
-
-def decode_one(q, k_pages, v_pages, block_table_row, seq_len: int, b: int, hq: int,
-               n_q_heads: int, n_kv_heads: int, block_size: int, scale: float) -> np.ndarray:
-    """One output row out[b, hq] (for sampled checks at full size)."""
-    group = n_q_heads // n_kv_heads
-    h = hq // group
-    K, V = gather(k_pages[:, h:h + 1], v_pages[:, h:h + 1], block_table_row, seq_len, block_size)
-    return attend(q[b, hq], K[:, 0, :], V[:, 0, :], scale)
 
 
 def copy_blocks(k_pages, v_pages, src_pages, dst_pages):

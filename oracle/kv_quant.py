@@ -68,12 +68,6 @@ def dequantize_vector(codes, scale, zero) -> np.ndarray:
     return np.float64(scale) * (np.asarray(codes, dtype=np.float64) - np.float64(zero))
 
 
-def pool_shapes(num_pages: int, n_kv: int, head_dim: int, block_size: int = 16):
-    """Shapes of (k_codes, v_codes, meta) for a pool of num_pages pages."""
-    return ((num_pages, n_kv, head_dim // 16, block_size, 16), (num_pages, n_kv, head_dim, block_size),
-            (num_pages, n_kv, 4, block_size))
-
-
 def append(k_codes, v_codes, meta, block_table, positions, k_new, v_new, block_size: int):
     """Copies of the pools with each sequence's new token quantized into slot
     positions[b] % block_size of page block_table[b][positions[b] // block_size],

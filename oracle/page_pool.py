@@ -1,9 +1,11 @@
 """On-demand page allocation and block tables (oracle; test infrastructure only).
 
-The pages describe the allocator only in outline: each sequence's cache is a
-set of fixed-size blocks (16 tokens by default) that need not be contiguous,
-allocated as the sequence grows rather than reserved for a worst-case length,
-with a per-request block table from logical block to physical block
+The pages sketch the allocator without fixing its policy: a sequence's
+cache is held in blocks of a fixed token count (16 unless configured
+otherwise), which may sit anywhere in memory and are handed out one at a time
+as the sequence grows, instead of one slab sized for the longest possible
+sequence; a table per request translates logical block numbers into
+physical ones
 ("Inference Engines" chapter 17, "The Breakthrough"; evaltude docs
 "Transformer inference mechanics", "FlashAttention versus PagedAttention";
 CS336 lecture 10 notes, "PagedAttention (vLLM)").

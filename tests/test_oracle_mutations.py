@@ -214,3 +214,109 @@ def test_multi_query_order_reversed_is_caught(monkeypatch):
     orig = A.query_range
     monkeypatch.setattr(A, "query_range", lambda n, T, i, w: orig(n, T, T - 1 - i, w))   # planted
     assert any(_fails(TM.test_all_tokens_as_queries_is_causal_self_attention, *c) for c in _SELF)
+
+
+# ----------------------------------------------- byte accounting, copies, pool
+from collections import deque  # noqa: E402
+
+from oracle import page_pool as PP  # noqa: E402
+
+from . import test_oracle_page_pool as TP  # noqa: E402
+
+
+def test_gqa_ratio_inverted_is_caught(monkeypatch):
+    orig = KB.mha_to_gqa_ratio
+    monkeypatch.setattr(KB, "mha_to_gqa_ratio", lambda hq, hkv: 1.0 / orig(hq, hkv))   # planted
+    assert any(_fails(TB.test_mha_gqa_ratio_matches_pages, c) for c in TB.GOLDEN["ratios"])
+
+
+def test_attended_bytes_per_cached_token_is_caught(monkeypatch):
+    monkeypatch.setattr(KB, "attended_kv_bytes",
+                        lambda lens, hkv, d, p: sum(max(int(n) - 1, 0) for n in lens) * 2 * hkv * d * p)   # planted
+    assert _fails(TB.test_one_llama2_layer_of_the_32gb_example_is_one_gib)
+
+
+def test_copy_blocks_wrong_direction_is_caught(monkeypatch):
+    orig = A.copy_blocks
+    monkeypatch.setattr(A, "copy_blocks", lambda k, v, s, d: orig(k, v, d, s))   # planted: dst -> src
+    assert _fails(T.test_copy_blocks_then_fork_decode_equals_unshared_cache)
+
+
+def test_pool_takes_from_the_back_is_caught(monkeypatch):
+    orig = PP.PagePool.reserve
+
+    def reserve_back(self, seq_id, n_tokens, block_size=16):
+        self.free = deque(reversed(self.free))       # planted: pops the end of the free list
+        try:
+            return orig(self, seq_id, n_tokens, block_size)
+        finally:
+            self.free = deque(reversed(self.free))
+    monkeypatch.setattr(PP.PagePool, "reserve", reserve_back)
+    assert _fails(TP.test_hand_worked_sequence_of_operations)
+    assert _fails(TP.test_tiny_workload_layout)
+
+
+def test_pool_release_to_the_front_is_caught(monkeypatch):
+    def release_front(self, seq_id):
+        for p in self.seqs.pop(seq_id):
+            self.refs[p] -= 1
+            if self.refs[p] == 0:
+                self.free.appendleft(p)              # planted
+    monkeypatch.setattr(PP.PagePool, "release", release_front)
+    assert _fails(TP.test_hand_worked_sequence_of_operations)
+
+
+def test_fork_without_reference_count_is_caught(monkeypatch):
+    def fork_norefs(self, parent, child):
+        self.seqs[child] = list(self.seqs[parent])   # planted: shared pages not counted
+    monkeypatch.setattr(PP.PagePool, "fork", fork_norefs)
+    assert _fails(TP.test_fork_and_copy_on_write)
+
+
+def test_write_into_shared_block_without_copy_is_caught(monkeypatch):
+    def rfw_nocopy(self, seq_id, position, block_size=16):
+        self.reserve(seq_id, position + 1, block_size)
+        return None                                  # planted: never copies
+    monkeypatch.setattr(PP.PagePool, "reserve_for_write", rfw_nocopy)
+    assert _fails(TP.test_fork_and_copy_on_write)
+
+
+def test_block_table_zero_padding_is_caught(monkeypatch):
+    orig = PP.PagePool.block_table
+    monkeypatch.setattr(PP.PagePool, "block_table",
+                        lambda self, ids, mb: np.maximum(orig(self, ids, mb), 0))   # planted: pads with page 0
+    assert _fails(TP.test_hand_worked_sequence_of_operations)
+
+
+def test_quant_decode_interleaved_head_map_is_caught(monkeypatch):
+    def decode_interleaved(q, k_codes, v_codes, meta, block_table, seq_lens, n_q_heads, n_kv_heads,
+                           block_size, scale):
+        q = np.asarray(q, dtype=np.float64)
+        out = np.zeros(q.shape)
+        for b in range(q.shape[0]):
+            n = int(seq_lens[b])
+            if n == 0:
+                continue
+            K, V = KQ.gather(k_codes, v_codes, meta, block_table[b], n, block_size)
+            for hq in range(n_q_heads):
+                h = hq % n_kv_heads                  # planted: interleaved instead of contiguous groups
+                out[b, hq] = A.attend(q[b, hq], K[:, h], V[:, h], scale)
+        return out
+    monkeypatch.setattr(KQ, "decode", decode_interleaved)
+    assert _fails(TQ.test_decode_equals_decode_of_dequantized_pools, 8, 2, 64, [40, 5, 17])
+
+
+def test_quant_gather_dropped_last_token_is_caught(monkeypatch):
+    orig = KQ.gather
+    monkeypatch.setattr(KQ, "gather", lambda kc, vc, m, row, n, bs: tuple(
+        x[: max(n - 1, 0)] for x in orig(kc, vc, m, row, n, bs)))   # planted
+    assert _fails(TQ.test_decode_brute_force_tiny)
+
+
+def test_quant_append_slot_off_by_one_is_caught(monkeypatch):
+    orig_append = KQ.append
+
+    def append_next_slot(kc, vc, meta, bt, positions, kn, vn, bs):
+        return orig_append(kc, vc, meta, bt, [int(p) + 1 for p in positions], kn, vn, bs)   # planted: off by one
+    monkeypatch.setattr(KQ, "append", append_next_slot)
+    assert _fails(TQ.test_append_writes_exactly_the_slot)
