@@ -10,8 +10,9 @@ value = algorithmic KV bytes read per step / step time, where the algorithmic
 bytes are 2 (K and V) x head_dim x element size per attended token per KV head
 per layer (the per-token KV formula of the pages' chapter 17 equation M_kv).
 
-Prints one JSON line.  Default workload: batch 16 x 4096 tokens, 32/32 heads,
-head_dim 128, bf16 (one layer of the Llama-2-7B example).
+Prints one JSON line.  Default workload: the Llama-3-8B-shaped decode step,
+32 layers of a GQA cache (32 query / 8 KV heads, head_dim 128, bf16) for 256
+sequences with lognormal lengths (median 2000), one new token each.
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama2_7b_mha")
+    ap.add_argument("--workload", default="llama3_8b_step")
     ap.add_argument("--n-items", type=int, default=0)
     ap.add_argument("--min-chunk", type=int, default=0)
     ap.add_argument("--schedule", type=int, default=0, choices=[0, 1, 2],
@@ -132,84 +133,139 @@ def setup(w, device, kv="dense", q_len=1, window=0):
                 kv_bytes_layer=kv_bytes_layer, grown=grown, n_copies=n_copies)
 
 
-def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0):
-    """The oracle, as it stands, on a bounded sample: whole sequences of layer 0
-    (append + decode for every query head; with q_len > 1 or a window, the
-    multi-token decode), until the time budget is used."""
-    import torch
-    import workloads as W
+def _oracle_worker(task):
+    """One baseline worker process: loads its sequences' host inputs (not
+    timed), then runs the oracle over them, whole sequences in order and again
+    from the start, until `budget` seconds of its own compute are used.
+    Returns (KV bytes covered, seconds, runs)."""
+    files, budget, mode, meta = task
+    import time as _t
+    import numpy as _np
     from oracle import attention as OA
     from oracle import kv_quant as KQ
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    xs = []
+    for f in files:
+        with _np.load(f) as z:
+            xs.append({k: z[k] for k in z.files})
+    secs, kv, runs = 0.0, 0, 0
+    while secs < budget and xs:
+        for x in xs:
+            t0 = _t.perf_counter()
+            bt = _np.arange(x["k"].shape[0], dtype=_np.int32)[None, :]
+            att = [int(x["att"])]
+            if mode == "multi":
+                OA.decode_multi(x["q"], x["k"], x["v"], bt, att, meta["q_len"], meta["hq"], meta["hkv"], 16,
+                                meta["scale"], meta["window"])
+            elif mode == "u8":
+                k2, v2, m2 = KQ.append(x["k"], x["v"], x["m"], bt, [int(x["cached"])], x["kn"], x["vn"], 16)
+                KQ.decode(x["q"], k2, v2, m2, bt, att, meta["hq"], meta["hkv"], 16, meta["scale"])
+            else:
+                k2, v2 = OA.append(x["k"], x["v"], bt, [int(x["cached"])], x["kn"], x["vn"], 16)
+                OA.decode(x["q"], k2, v2, bt, att, meta["hq"], meta["hkv"], 16, meta["scale"])
+            secs += _t.perf_counter() - t0
+            kv += int(x["bytes"])
+            runs += 1
+            if secs >= budget:
+                break
+    return kv, secs, runs
+
+
+def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0, max_workers=16):
+    """The oracle, as it stands, on a bounded sample of layer 0: whole
+    sequences (append + decode for every query head; with q_len > 1 or a
+    window, the multi-token decode), run in parallel worker processes, one
+    single-threaded process per core (process parallelism over sequences).
+    Each worker runs its share of the sample, repeatedly, for about budget_s
+    seconds of compute; value = KV bytes covered by all workers / the longest
+    worker's compute time.  cores = the number of workers."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    n_workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     L = S["layers"][0]
     rng = np.random.default_rng(0)
     pick = list(rng.permutation(w.batch))
     multi = q_len > 1 or window > 0
     read = multi_kv_tokens(S["att"], q_len, window) if multi else S["att"]
-
-    def host_inputs(b):
-        """Host copies of sequence b's pages (relabelled 0..n-1) and rows; not timed."""
-        nblk = (int(S["att"][b]) + 15) // 16
-        pages = torch.from_numpy(S["bt_np"][b, :nblk].astype(np.int64)).to(L.k_pages.device)
-        bt = np.arange(nblk, dtype=np.int32)[None, :]
-        qb = L.q[b:b + 1].double().cpu().numpy()
-        if multi:
-            return (qb, L.k_pages.index_select(0, pages).double().cpu().numpy(),
-                    L.v_pages.index_select(0, pages).double().cpu().numpy(), bt)
-        if kv == "u8":
-            return (qb, L.k_pages.index_select(0, pages).cpu().numpy(), L.v_pages.index_select(0, pages).cpu().numpy(),
-                    L.meta.index_select(0, pages).cpu().numpy(), bt, L.k_new[b:b + 1].float().cpu().numpy(),
-                    L.v_new[b:b + 1].float().cpu().numpy())
-        return (qb, L.k_pages.index_select(0, pages).double().cpu().numpy(),
-                L.v_pages.index_select(0, pages).double().cpu().numpy(), bt,
-                L.k_new[b:b + 1].double().cpu().numpy(), L.v_new[b:b + 1].double().cpu().numpy())
-
-    def run_oracle(b, x):
-        if multi:
-            qb, kp, vp, bt = x
-            OA.decode_multi(qb, kp, vp, bt, [int(S["att"][b])], q_len, w.n_q_heads, w.n_kv_heads, 16, w.scale,
-                            window)
-        elif kv == "u8":
-            qb, kp, vp, mp, bt, kn, vn = x
-            k2, v2, m2 = KQ.append(kp, vp, mp, bt, [int(S["cached"][b])], kn, vn, 16)
-            KQ.decode(qb, k2, v2, m2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
-        else:
-            qb, kp, vp, bt, kn, vn = x
-            k2, v2 = OA.append(kp, vp, bt, [int(S["cached"][b])], kn, vn, 16)
-            OA.decode(qb, k2, v2, bt, [int(S["att"][b])], w.n_q_heads, w.n_kv_heads, 16, w.scale)
-
-    # Whole sequences in a seeded order until the budget is used.  A layer the
-    # oracle finishes within the budget is run again (from host copies kept
-    # after the first pass, at most 8 GiB of them), so the timing covers about
-    # budget_s of CPU work either way.
-    kept, kept_bytes, cap = {}, 0, 8 << 30
-    done, passes, secs, kv_bytes = 0, 0, 0.0, 0
-    while secs < budget_s and passes < 64:
+    mode = "multi" if multi else ("u8" if kv == "u8" else "dense")
+    # host inputs of whole sequences (pages relabelled 0..n-1), float32 (exact
+    # for bf16) or the 8-bit codes, written to files the workers load; at most
+    # 2 GiB of them, at least one sequence per worker where the batch allows
+    tmp = tempfile.mkdtemp(prefix="pkv_oracle_")
+    files, total, cap = [], 0, 2 << 30
+    try:
         for b in pick:
-            x = kept.get(b)
-            if x is None:
-                x = host_inputs(b)
-                nb = sum(a.nbytes for a in x)
-                if kept_bytes + nb <= cap:
-                    kept[b] = x
-                    kept_bytes += nb
-            t0 = time.perf_counter()
-            run_oracle(b, x)
-            secs += time.perf_counter() - t0
-            done += 1
-            kv_bytes += int(read[b]) * S["kv_bytes_layer"] // int(read.sum())
-            if secs >= budget_s:
+            nblk = (int(S["att"][b]) + 15) // 16
+            pages = __import__("torch").from_numpy(S["bt_np"][b, :nblk].astype(np.int64)).to(L.k_pages.device)
+            x = {"att": np.int64(S["att"][b]), "cached": np.int64(S["cached"][b]),
+                 "bytes": np.int64(int(read[b]) * S["kv_bytes_layer"] // int(read.sum())),
+                 "q": L.q[b:b + 1].float().cpu().numpy()}
+            if kv == "u8":
+                x.update(k=L.k_pages.index_select(0, pages).cpu().numpy(),
+                         v=L.v_pages.index_select(0, pages).cpu().numpy(),
+                         m=L.meta.index_select(0, pages).cpu().numpy(),
+                         kn=L.k_new[b:b + 1].float().cpu().numpy(), vn=L.v_new[b:b + 1].float().cpu().numpy())
+            else:
+                x.update(k=L.k_pages.index_select(0, pages).float().cpu().numpy(),
+                         v=L.v_pages.index_select(0, pages).float().cpu().numpy(),
+                         kn=L.k_new[b:b + 1].float().cpu().numpy(), vn=L.v_new[b:b + 1].float().cpu().numpy())
+            nb = sum(a.nbytes for a in x.values())
+            if files and total + nb > cap and len(files) >= n_workers:
                 break
-        passes += 1
+            f = os.path.join(tmp, f"seq{b}.npz")
+            np.savez(f, **x)
+            files.append(f)
+            total += nb
+        n_workers = min(n_workers, len(files))
+        shares = [files[i::n_workers] for i in range(n_workers)]
+        meta = {"hq": w.n_q_heads, "hkv": w.n_kv_heads, "scale": w.scale, "q_len": q_len, "window": window}
+        env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for k in env:
+            os.environ[k] = "1"
+        try:
+            with cf.ProcessPoolExecutor(n_workers, mp_context=mp.get_context("spawn")) as ex:
+                res = list(ex.map(_oracle_worker, [(sh, budget_s, mode, meta) for sh in shares]))
+        finally:
+            for k, v in env.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    kv_bytes = sum(r[0] for r in res)
+    secs = max(r[1] for r in res)
+    runs = sum(r[2] for r in res)
     what = f"{q_len}-token decode" if multi else "append + decode"
-    return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} whole-sequence runs over {min(done, w.batch)} of the {w.batch} sequences of one layer "
-                      f"({what}, all {w.n_q_heads} query heads), {kv_bytes / 2**20:.0f} MiB of KV, {secs:.1f} s",
+    return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": n_workers, "kind": "oracle",
+            "sample": f"{runs} whole-sequence runs over {len(files)} of the {w.batch} sequences of layer 0 "
+                      f"({what}, all {w.n_q_heads} query heads) in {n_workers} single-threaded worker processes, "
+                      f"{kv_bytes / 2**20:.0f} MiB of KV in {secs:.1f} s (longest worker)",
             "seconds": secs}
+
+
+def gather_probe(w, S, dec, device, steps):
+    """The gather probe (the decode kernel's tile stream, no arithmetic) on the
+    same pools, block table and chunks, rotating the pool copies as the timed
+    steps do: GB/s of algorithmic KV bytes."""
+    import torch
+    import paged_kv_cache_254_amd as pkv
+    sink = torch.empty(max(1, dec.n_items), dtype=torch.int32, device=device)
+    layers = S["layers"]
+    n = max(len(layers), steps)
+    for i in range(len(layers)):
+        L = layers[i]
+        pkv.gather_probe(L.k_pages, L.v_pages, S["bt"], S["seq_lens"], sink, dec.n_items, dec.min_chunk_pages)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(n):
+        L = layers[i % len(layers)]
+        pkv.gather_probe(L.k_pages, L.v_pages, S["bt"], S["seq_lens"], sink, dec.n_items, dec.min_chunk_pages)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / n
+    return S["kv_bytes_layer"] / (ms / 1e3) / 1e9, ms
 
 
 def hbm_probe(device):
@@ -422,6 +478,9 @@ def main():
     traffic = None if multi else traffic_for(w.name, args.kv)   # counters are taken on the one-token decode
 
     probe = None if args.no_probe else hbm_probe(device)
+    gprobe = None
+    if not args.no_probe and not multi and not u8:
+        gprobe = gather_probe(w, S, dec, device, args.steps * n_layers)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -470,6 +529,9 @@ def main():
         "combine_avg_ms": None if one_kernel or multi else round(float(np.mean(comb_ms)), 5),
         "hbm_read_probe_gbs": None if probe is None else round(probe, 1),
         "pct_of_read_probe": None if probe is None else round(100 * value / probe, 1),
+        "gather_probe_gbs": None if gprobe is None else round(gprobe[0], 1),
+        "gather_probe_ms": None if gprobe is None else round(gprobe[1], 5),
+        "pct_of_gather_probe": None if gprobe is None else round(100 * achieved / gprobe[0], 1),
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),
     }

@@ -186,14 +186,20 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  *
  * workspace: device, 256-byte aligned, at least
  * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)
- * bytes (n_items after defaults are applied).  Layout: the partials, then
- * (256-byte aligned) 16 * batch * n_kv_heads bytes of arrival counters, then
- * 4 * (batch + 1) bytes where the split kernel stores the per-sequence page
- * prefix for the combine kernel, then one int32 chunk counter for the
- * dynamic schedule.  Partials and prefix are overwritten by every call; the
- * counters must be zero before the first call that uses the workspace (e.g.
- * a zero-filled allocation), and every call leaves them zero.  Calls that
- * overlap in time must not share a workspace.
+ * bytes (n_items after defaults are applied).  Layout: the partials from
+ * offset 0, then (256-byte aligned) 4 * (batch + 1) bytes where the split
+ * kernel stores the per-sequence page prefix for the combine kernel.  The
+ * counters are at the END of the workspace, counted backwards from its last
+ * int32 word (word workspace_bytes / 4 - 1): that word is the dynamic
+ * schedule's chunk counter, and the 4 * batch * n_kv_heads words below it
+ * are the arrival counters, (b, h, head block j) at word
+ * workspace_bytes / 4 - 2 - ((b * n_kv_heads + h) * 4 + j).  Their place
+ * depends only on workspace_bytes, so one workspace, sized for the largest
+ * batch, serves calls with any smaller batch (continuous batching).
+ * Partials and prefix are overwritten by every call; the counters must be
+ * zero before the first call that uses the workspace (e.g. a zero-filled
+ * allocation), and every call leaves them zero.  Calls that overlap in time
+ * must not share a workspace.
  * opts (nullable): n_items <= 0 means, for groups of at most 16 query heads
  * (one wavefront per chunk), one chunk per wavefront of one workgroup per CU
  * (4 x CUs), and for larger groups as many chunks as the device holds at
@@ -412,6 +418,24 @@ int pkv_copy_blocks(void* k_pages, void* v_pages, const int32_t* src_pages,
  * >= 4 * n_blocks bytes); pkv_copy_probe copies bytes (multiple of 16).
  * ------------------------------------------------------------------------ */
 int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_blocks, void* stream);
+/* Gather probe: the decode kernel's own tile stream with no arithmetic, for
+ * the bandwidth the memory system gives the workload's scattered (page, KV
+ * head) tiles ("Transformer inference mechanics", "Knowledge check": measure
+ * KV traffic and achieved bandwidth before naming a bottleneck).  It walks
+ * the same chunks of the flattened (sequence, KV head, page) order as
+ * pkv_paged_decode_attn with one query head per KV head (n_items and
+ * min_chunk_pages as in pkv_decode_opts, <= 0 for the defaults), reads every
+ * attended page's K and V tiles through the block table with the decode
+ * kernel's loads, and writes one XOR of the bytes per chunk to sink (device
+ * uint32 [n_items], sink_bytes >= 4 * n_items).  k_pages / v_pages are laid
+ * out as for the dense decode, except that consecutive pages may sit
+ * page_stride_bytes apart (0: n_kv_heads tiles, the library's layout; a
+ * larger multiple of 16 models a padded page).  Dense dtypes only; page ids
+ * outside [0, num_pages) and invalid lengths are skipped. */
+int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* block_table,
+                     const int32_t* seq_lens, int32_t n_kv_heads, int32_t head_dim, int32_t batch,
+                     int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, int64_t page_stride_bytes,
+                     int32_t n_items, int32_t min_chunk_pages, void* sink, size_t sink_bytes, void* stream);
 int pkv_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 
 #ifdef __cplusplus

@@ -215,6 +215,8 @@ struct DecodeArgs {
   float scale_log2;
   // Non-null: the chunk that finishes a pair of at most fuse_max_parts
   // chunks last merges its partials (one counter per pair and head block).
+  // Points at the workspace's last int32 word; the counters lie below it
+  // (see merge_counter).
   int32_t* counters;
   int32_t fuse_max_parts;
   // Per-sequence page prefix [batch + 1] in the workspace: written by the
@@ -819,19 +821,37 @@ struct Segment {
 // Arrival of this wavefront's partials for (b, h, head block gb).  The
 // partials were written with device-scope stores; once they have completed
 // (vmcnt 0: every vector memory operation of this wavefront done), one lane
-// counts the arrival with a device-scope atomic.  The wavefront that brings
+// counts the arrival with a device-scope atomic.
+//
+// Why this orders the merge on gfx950 without agent-scope fences: a fence
+// with release semantics at agent scope is, on this architecture, an L2
+// write-back of lines written with the default policy followed by a wait
+// for vmcnt 0, and an acquire fence is an invalidation of the caches
+// between the wave and memory.  Every access of this protocol carries the
+// agent-scope policy bits itself instead: the partial stores are written
+// through the writer's L2 (and are counted complete by vmcnt only once the
+// device-coherent level has them), the counter atomic is performed at that
+// level, and the merge's loads do not hit a stale line in the reader's L1
+// or L2.  The wait for vmcnt 0 before the atomic is the release's wait; the
+// control dependence of the loads on the atomic's result, plus the
+// compiler barriers around both, keeps every load after it.  The
+// write-back and invalidation are then redundant; as fences they cover
+// whole caches and cost 30 % on the 16 x 4096 MHA layer.  The wavefront that brings
 // the count to nparts reads the nparts partials with device-scope loads,
 // merges them in chunk order (out = sum_i w_i o_i / sum_i w_i, w_i =
 // exp(lse_i - max lse), the combine kernel's formula) and resets the counter
 // for the next call.  No wavefront waits for another.
 __device__ inline int32_t* merge_counter(const DecodeArgs& a, int b, int h, int gb) {
-  return a.counters + (static_cast<size_t>(b) * a.n_kv + h) * kMaxWavesPerChunk + gb;
+  return a.counters - 1 - ((static_cast<ptrdiff_t>(b) * a.n_kv + h) * kMaxWavesPerChunk + gb);
 }
 
 // Counts this wavefront's arrivals for its (at most two) pending pairs, both
 // atomics in flight together, after all its stores have completed; returns
 // a bit per pending pair for which it arrived last.
 __device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int gb, int lane) {
+  // Compiler-level barrier: the partial stores stay before the wait, and
+  // (below) the merge's loads after the atomic's result.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   int o0 = 0, o1 = 0;
   if (lane == 0) {
@@ -844,6 +864,7 @@ __device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int g
   }
   o0 = __shfl(o0, 0);
   o1 = __shfl(o1, 0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return (pm.n > 0 && o0 == pm.nparts0 - 1 ? 1 : 0) | (pm.n > 1 && o1 == pm.nparts1 - 1 ? 2 : 0);
 }
 
@@ -1472,6 +1493,7 @@ split_kernel(DecodeArgs a) {
 // list.  kGroupParts: partials per round trip of the merge (0: the default).
 template <bool kOutBf16, int D, bool kMulti, int kGroupParts>
 __device__ void flush_pending(const DecodeArgs& a, PendingList& pl, int lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   for (int base = 0; base < pl.n; base += kWave) {
     const int i = base + lane;
@@ -1481,6 +1503,7 @@ __device__ void flush_pending(const DecodeArgs& a, PendingList& pl, int lane) {
     if (in)
       old = __hip_atomic_fetch_add(merge_counter(a, e.x, e.y, 0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t last = __builtin_amdgcn_ballot_w64(in && old == e.w - 1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     while (last != 0) {
       const int k = __builtin_ctzll(last);
       last &= last - 1;
@@ -1964,6 +1987,81 @@ copy_blocks_kernel(char* k_pages, char* v_pages, const int32_t* src, const int32
   }
 }
 
+// Gather probe: the decode kernel's tile stream with no arithmetic.  The
+// same chunks of the flattened (sequence, KV head, page) order, the same
+// page-id reads, the same per-tile buffer loads (cache policy, ring depth,
+// whole ring turns), but each tile is only folded into an XOR that keeps
+// the loads live.  Its rate is what the memory system sustains for the
+// workload's own tile list, the ceiling the decode kernel is held to.
+// page_stride: bytes between consecutive pages of the pools (n_kv tiles for
+// the library's layout; larger values model padded page layouts).
+template <bool kBf16, int D, int kDepth>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu<kBf16, D>)))
+gather_probe_kernel(DecodeArgs a, size_t page_stride, uint32_t* sink) {
+  using O = Ops<kBf16, D>;
+  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int kBufs = kDepth + 1;
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, 1, 0, s_prefix, smem + a.batch + 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uni(threadIdx.x / kWave);
+  const int chunk = static_cast<int>(blockIdx.x) * kWavesPerGroup + wave;
+  if (chunk >= a.n_items) return;
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int64_t f64 = static_cast<int64_t>(chunk) * C;
+  uint32_t acc = 0;
+  if (f64 < total) {
+    const int f0 = static_cast<int>(f64);
+    const int cnt = static_cast<int>(min(f64 + C, static_cast<int64_t>(total))) - f0;
+    const char* kp0 = static_cast<const char*>(a.k_pages);
+    const char* vp0 = static_cast<const char*>(a.v_pages);
+    const int c = lane >> 4, n = lane & 15;
+    FlatCursor<false> ld;
+    ld.seek(a, s_prefix, f0);
+    int issued = 0;
+    PageRegs<kBf16, D> buf[kBufs];
+    auto issue = [&](PageRegs<kBf16, D>& r) {
+      const bool in = issued < cnt;
+      const int pg = ((const const_i32*)(a.block_table + static_cast<size_t>(ld.b) * a.max_blocks))[ld.j];
+      const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+      const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
+      load_page<kBf16, D>(r, kp0 + off, vp0 + off, 16u * lane, O::ES * (n * kBlock + 4 * c), in && ok ? kTile : 0);
+      if (in) {
+        ++issued;
+        if (issued < cnt) ld.next(a, s_prefix);
+      }
+    };
+    auto fold = [&](const PageRegs<kBf16, D>& r) {
+#pragma unroll
+      for (int i = 0; i < O::NK; ++i) acc ^= r.k[i].x ^ r.k[i].y ^ r.k[i].z ^ r.k[i].w;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) {
+        acc ^= r.v[nb].x ^ r.v[nb].y;
+        if constexpr (!kBf16) acc ^= r.v[nb].z ^ r.v[nb].w;
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) issue(buf[s]);
+    int p = 0;
+    while (p < cnt) {
+#pragma unroll
+      for (int s = 0; s < kBufs; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf[(s + kDepth) % kBufs]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < cnt) fold(buf[s]);
+        ++p;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), off));
+  if (lane == 0) sink[chunk] = acc;
+}
+
 __global__ void __launch_bounds__(256)
 read_probe_kernel(const u32x4* __restrict__ buf, size_t n16, uint32_t* sink) {
   uint32_t x = 0;
@@ -2261,15 +2359,14 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   // max_blocks_per_seq pages spans at most ceil(max_blocks / min_chunk) + 1).
   const bool fuse = do_split && do_combine && r.combine_mode == 0;
   const int64_t max_parts = (static_cast<int64_t>(max_blocks_per_seq) + r.min_chunk - 1) / r.min_chunk + 1;
-  a.counters = fuse ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                                 decode_counters_offset(batch, cols, n_kv_heads, head_dim,
-                                                                        r.n_items))
-                    : nullptr;
+  // The counters are counted backwards from the workspace's last int32
+  // word, which is the dynamic schedule's chunk counter.
+  int32_t* tail = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (workspace_bytes & ~size_t{3})) - 1;
+  a.counters = fuse ? tail : nullptr;
   a.fuse_max_parts = kFuseMaxParts;
   a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                         decode_prefix_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
-  a.work = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                      decode_work_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
+  a.work = tail;
   // Split kernel LDS (static schedule; r.lds, checked above, holds the
   // prefix and one token slot per wavefront):
   // - workgroup merges (one wavefront per chunk and one 16-column block,
@@ -2592,6 +2689,62 @@ int pkv_copy_blocks(void* k_pages, void* v_pages, const int32_t* src_pages,
                      static_cast<char*>(v_pages), src_pages, dst_pages, n_pairs, n_kv_heads, tile, num_pages);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv::hip_fail("copy_blocks launch", e);
+  return ok();
+}
+
+int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* block_table,
+                     const int32_t* seq_lens, int32_t n_kv_heads, int32_t head_dim, int32_t batch,
+                     int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, int64_t page_stride_bytes,
+                     int32_t n_items, int32_t min_chunk_pages, void* sink, size_t sink_bytes, void* stream) {
+  int st = pkv::check_decode_shapes("pkv_gather_probe", n_kv_heads, n_kv_heads, head_dim, pkv::kBlock, batch,
+                                    max_blocks_per_seq, num_pages, dtype);
+  if (st != PKV_OK) return st;
+  if (dtype == PKV_U8) return fail(PKV_ERR_UNSUPPORTED, "pkv_gather_probe: dense caches only (PKV_F32, PKV_BF16)");
+  const int64_t tile = static_cast<int64_t>(pkv::kBlock) * head_dim * (dtype == PKV_BF16 ? 2 : 4);
+  const int64_t stride = page_stride_bytes > 0 ? page_stride_bytes : tile * n_kv_heads;
+  if (stride < tile * n_kv_heads || stride % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe: page_stride_bytes must be 0 or a multiple of 16 of at "
+                                     "least n_kv_heads tiles");
+  if (batch == 0) return ok();
+  if (!k_pages || !v_pages || !block_table || !seq_lens || !sink || !pkv::aligned(k_pages, 16) ||
+      !pkv::aligned(v_pages, 16) || !pkv::aligned(block_table, 4) || !pkv::aligned(seq_lens, 4) ||
+      !pkv::aligned(sink, 4))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe: NULL or misaligned pointer");
+  pkv_decode_opts o{n_items, min_chunk_pages, 0, PKV_SCHEDULE_STATIC};
+  pkv::Resolved r;
+  st = pkv::resolve_opts(dtype, head_dim, 1, batch, max_blocks_per_seq, n_kv_heads, &o, &r);
+  if (st != PKV_OK) return st;
+  if (sink_bytes < static_cast<size_t>(r.n_items) * 4)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe: sink needs 4 * n_items bytes (" +
+                                         std::to_string(r.n_items) + " items)");
+  pkv::DecodeArgs a{};
+  a.k_pages = const_cast<void*>(k_pages);
+  a.v_pages = const_cast<void*>(v_pages);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.n_q = n_kv_heads;
+  a.n_kv = n_kv_heads;
+  a.group = 1;
+  a.q_len = 1;
+  a.cols = 1;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.n_items = r.n_items;
+  a.min_chunk = r.min_chunk;
+  const size_t lds = pkv::split_lds_bytes(batch);
+  if (lds > pkv::kMaxLdsBytes) return fail(PKV_ERR_UNSUPPORTED, "pkv_gather_probe: batch too large");
+  using Fn = void (*)(pkv::DecodeArgs, size_t, uint32_t*);
+  const Fn fn = dtype == PKV_BF16
+                    ? (head_dim == 128 ? pkv::gather_probe_kernel<true, 128, pkv::kPrefetchPages>
+                                       : pkv::gather_probe_kernel<true, 64, pkv::kPrefetchPages>)
+                    : (head_dim == 128 ? pkv::gather_probe_kernel<false, 128, 1>
+                                       : pkv::gather_probe_kernel<false, 64, 1>);
+  const int grid = (r.n_items + pkv::kWavesPerGroup - 1) / pkv::kWavesPerGroup;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(pkv::kWave * pkv::kWavesPerGroup), lds, static_cast<hipStream_t>(stream),
+                     a, static_cast<size_t>(stride), static_cast<uint32_t*>(sink));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::hip_fail("gather probe launch", e);
   return ok();
 }
 

@@ -76,30 +76,32 @@ constexpr int kFuseMaxParts = 96;
 constexpr int kMaxWavesPerChunk = 4;
 
 // Workspace layout: partial outputs [slots][group][head_dim] f32, partial
-// lse [slots][group] f32, then (256-byte aligned) one arrival counter per
-// (sequence, KV head, head block), int32, then the per-sequence page prefix
-// [batch + 1] int32 that the split kernel stores for the combine kernel.
-__host__ __device__ inline int64_t decode_counters_offset(int64_t batch, int64_t group, int64_t n_kv,
-                                                          int64_t head_dim, int64_t n_items) {
+// lse [slots][group] f32, then (256-byte aligned) the per-sequence page
+// prefix [batch + 1] int32 that the split kernel stores for the combine
+// kernel.  The counters sit at the END of the workspace, counted backwards
+// from its last int32 word: that word is the dynamic schedule's chunk
+// counter, and the words before it hold one arrival counter per (sequence,
+// KV head, head block), (b, h, gb) at word -(2 + (b * n_kv + h) * 4 + gb).
+// Their place depends only on the workspace's size, never on the batch, so
+// a workspace sized for batch B serves later calls with any batch <= B:
+// every call leaves its counters zero, and no call's partials or prefix
+// reach a word another call uses as a counter.
+__host__ __device__ inline int64_t decode_prefix_offset(int64_t batch, int64_t group, int64_t n_kv,
+                                                        int64_t head_dim, int64_t n_items) {
   const int64_t parts = decode_slots(batch, n_kv, n_items) * group * (head_dim + 1) * 4;
   return (parts + 255) & ~int64_t{255};
 }
 __host__ __device__ inline int64_t decode_counters_count(int64_t batch, int64_t n_kv) {
   return batch * n_kv * kMaxWavesPerChunk;
 }
-__host__ __device__ inline int64_t decode_prefix_offset(int64_t batch, int64_t group, int64_t n_kv,
-                                                        int64_t head_dim, int64_t n_items) {
-  return decode_counters_offset(batch, group, n_kv, head_dim, n_items) + decode_counters_count(batch, n_kv) * 4;
-}
-// After the prefix: the dynamic schedule's chunk counter (int32; zero
-// between launches, like the arrival counters).
-__host__ __device__ inline int64_t decode_work_offset(int64_t batch, int64_t group, int64_t n_kv,
-                                                      int64_t head_dim, int64_t n_items) {
-  return decode_prefix_offset(batch, group, n_kv, head_dim, n_items) + (batch + 1) * 4;
+// Bytes of the counters at the workspace's end (arrival counters and the chunk counter).
+__host__ __device__ inline int64_t decode_tail_bytes(int64_t batch, int64_t n_kv) {
+  return (decode_counters_count(batch, n_kv) + 1) * 4;
 }
 __host__ __device__ inline int64_t decode_workspace_end(int64_t batch, int64_t group, int64_t n_kv,
                                                         int64_t head_dim, int64_t n_items) {
-  return decode_work_offset(batch, group, n_kv, head_dim, n_items) + 4;
+  return decode_prefix_offset(batch, group, n_kv, head_dim, n_items) + (batch + 1) * 4 +
+         decode_tail_bytes(batch, n_kv);
 }
 
 // Dynamic schedule (pkv_decode_opts.schedule): one workgroup per CU; by

@@ -199,10 +199,15 @@ class Decoder:
         self.shape = (batch, n_q_heads, n_kv_heads, head_dim)
         self.max_blocks = max_blocks
 
+    def _check_batch(self, B: int):
+        if B > self.shape[0]:
+            raise ValueError(f"batch {B} is larger than the {self.shape[0]} this Decoder's workspace was sized for")
+
     def _args(self, q, k_pages, v_pages, block_table, seq_lens, scale, out, stream):
         if not (q.dtype == k_pages.dtype == v_pages.dtype == out.dtype) or _dtype_code(q) == PKV_U8:
             raise TypeError("dense decode: q, k_pages, v_pages and out must share dtype bf16 or float32")
         B, Hq, D = q.shape
+        self._check_batch(B)
         return (_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hq,
                 k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B,
                 block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
@@ -218,6 +223,7 @@ class Decoder:
                 _dtype_code(q) == PKV_U8:
             raise TypeError("dense decode step: all tensors must share dtype bf16 or float32")
         B, Hq, D = q.shape
+        self._check_batch(B)
         return (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                 _ptr(seq_lens), Hq, k_pages.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream),
                 B, block_table.shape[1], k_pages.shape[0], _dtype_code(q), _ptr(self.workspace),
@@ -239,7 +245,9 @@ class Decoder:
                                                      stream)), "pkv_paged_decode_split")
 
     def combine(self, seq_lens, out, max_blocks: int, stream=None):
-        B, Hq, Hkv, D = self.shape
+        _, Hq, Hkv, D = self.shape
+        B = out.shape[0]
+        self._check_batch(B)
         check(lib.pkv_lse_combine(_ptr(self.workspace), self.workspace.numel(), _ptr(seq_lens), B, Hq, Hkv, D,
                                   BLOCK_SIZE, max_blocks, _ptr(out), _dtype_code(out),
                                   _opts(self.n_items, self.min_chunk_pages, self.combine_mode, self.schedule), _stream(stream)),
@@ -254,6 +262,7 @@ class Decoder:
         if not (q.dtype == k_pages.dtype == v_pages.dtype == out.dtype) or _dtype_code(q) == PKV_U8:
             raise TypeError("decode_multi: q, k_pages, v_pages and out must share dtype bf16 or float32")
         B, T, Hq, D = q.shape
+        self._check_batch(B)
         if T != q_len or self.shape[1] != Hq * q_len:
             raise ValueError("q must be [B][q_len][Hq][D] and the Decoder built for Hq * q_len heads")
         check(lib.pkv_paged_decode_multi(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens),
@@ -270,6 +279,7 @@ class Decoder:
                 v_codes.dtype != torch.uint8 or meta.dtype != torch.float32:
             raise TypeError("8-bit decode: q and out bf16, k_codes and v_codes uint8, meta float32")
         B, Hq, D = q.shape
+        self._check_batch(B)
         return (_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(meta), _ptr(block_table), _ptr(seq_lens), Hq,
                 k_codes.shape[1], D, BLOCK_SIZE, float(scale), _ptr(out), _stream(stream), B, block_table.shape[1],
                 k_codes.shape[0], _ptr(self.workspace), self.workspace.numel(),
@@ -292,14 +302,14 @@ class Decoder:
         return out
 
     def counters(self):
-        """(arrival counters [B][Hkv][4], chunk counter) int32 views into the workspace."""
+        """(arrival counters [B][Hkv][4], chunk counter) int32 copies of the
+        counters, which sit at the workspace's end counted backwards."""
         import torch
         B, Hq, Hkv, D = self.shape
-        slots = self.n_items + B * Hkv
-        parts = slots * (Hq // Hkv) * (D + 1) * 4
-        off = (parts + 255) // 256 * 256
-        i = self.workspace[: self.ws_bytes].view(torch.int32)
-        return i[off // 4: off // 4 + B * Hkv * 4].view(B, Hkv, 4), i[self.ws_bytes // 4 - 1]
+        i = self.workspace.view(torch.int32)
+        end = i.numel()
+        n = B * Hkv * 4
+        return i[end - 1 - n: end - 1].flip(0).view(B, Hkv, 4).clone(), i[end - 1].clone()
 
     def partials(self):
         """Views (partial_o [slots][G][D], partial_lse [slots][G]) into the workspace."""
@@ -329,3 +339,18 @@ def hbm_read_probe(buf, sink, n_blocks: int, stream=None) -> None:
 def copy_probe(dst, src, stream=None) -> None:
     check(lib.pkv_copy_probe(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream)),
           "pkv_copy_probe")
+
+
+def gather_probe(k_pages, v_pages, block_table, seq_lens, sink, n_items: int = 0, min_chunk_pages: int = 0,
+                 page_stride_bytes: int = 0, num_pages: int = 0, stream=None) -> None:
+    """The decode kernel's tile stream without arithmetic (see pkv_gather_probe).
+    k_pages [P][Hkv][D/X][16][X] (or a padded buffer with page_stride_bytes and
+    num_pages given); sink: device int32 with at least n_items entries."""
+    B = block_table.shape[0]
+    P = num_pages if num_pages > 0 else k_pages.shape[0]
+    Hkv = k_pages.shape[1]
+    D = k_pages.shape[2] * k_pages.shape[4]
+    check(lib.pkv_gather_probe(_ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hkv, D, B,
+                               block_table.shape[1], P, _dtype_code(k_pages), int(page_stride_bytes), int(n_items),
+                               int(min_chunk_pages), _ptr(sink), sink.numel() * sink.element_size(), _stream(stream)),
+          "pkv_gather_probe")

@@ -44,12 +44,9 @@ def _decode(pkv, w, c, n_items, min_chunk, combine_mode=0, dec=None):
 
 
 def _counters_zero(dec):
-    # layout tail: counters (16 bytes per sequence and KV head), then the
-    # page prefix (4 bytes per sequence, plus one)
-    B, Hq, Hkv, D = dec.shape
-    end = dec.ws_bytes - 4 * (B + 1)
-    ctr = dec.workspace[end - 16 * B * Hkv: end]
-    return int(ctr.count_nonzero().item()) == 0
+    # the arrival counters and the chunk counter sit at the workspace's end
+    arrivals, work = dec.counters()
+    return int(arrivals.count_nonzero().item()) == 0 and int(work) == 0
 
 
 def test_repeated_calls_on_one_workspace(pkv):

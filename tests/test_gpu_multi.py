@@ -115,20 +115,25 @@ def test_full_size_sampled_multi(pkv, T, window):
     # sequences against the oracle run on just their pages.
     w = W.get("llama3_8b_gqa")
     c = H.setup(w, device="cuda")
-    # every attended token must be cached: append the step's token first
-    # (the other slots past each length stay NaN)
-    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
-    torch.cuda.synchronize()
     att = c.attended.astype(np.int64)
     B, Hq, Hkv, D = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
     q = torch.stack([W.make_q(w, t, "cuda") for t in range(T)], dim=1).contiguous()
     rng = np.random.default_rng(12)
     bs = sorted({0, B - 1, int(np.argmax(att)), int(np.argmin(att)), int(rng.integers(B))})
+    # host copies of the sampled sequences' pages before any HIP call; the
+    # oracle appends the step's token to them itself
     host = {}
     for b in bs:
         nblk = (int(att[b]) + 15) // 16
         pages = torch.from_numpy(c.bt_np[b, :nblk].astype(np.int64)).cuda()
-        host[b] = (H.f64(c.k_pages.index_select(0, pages)), H.f64(c.v_pages.index_select(0, pages)), nblk)
+        sub = np.arange(nblk, dtype=np.int32)[None, :]
+        kp, vp = OA.append(H.f64(c.k_pages.index_select(0, pages)), H.f64(c.v_pages.index_select(0, pages)), sub,
+                           [int(c.cached[b])], H.f64(c.k_new[b:b + 1]), H.f64(c.v_new[b:b + 1]), 16)
+        host[b] = (kp, vp, nblk)
+    # every attended token must be cached: append the step's token first
+    # (the other slots past each length stay NaN)
+    pkv.kv_append(c.k_new, c.v_new, c.k_pages, c.v_pages, c.bt, c.positions)
+    torch.cuda.synchronize()
     dec = pkv.Decoder(B, Hq * T, Hkv, D, W.torch_dtype(w), c.max_blocks)
     out = torch.full((B, T, Hq, D), float("nan"), dtype=W.torch_dtype(w), device="cuda")
     H.log(f"multi full T={T} W={window} (n_items={dec.n_items})")
