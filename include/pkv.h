@@ -255,6 +255,25 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
                     size_t workspace_bytes, const pkv_decode_opts* opts);
 
+/* pkv_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call without the workspace argument.  Its workspace is a fixed
+ * 16 MiB array in the library's device code (16777216 bytes, one per GPU,
+ * held until the process ends); the call allocates nothing and calls no
+ * allocating routine.  Shapes whose workspace (pkv_decode_resolve) exceeds
+ * 16 MiB are refused with PKV_ERR_WORKSPACE before anything is launched;
+ * the five workloads of this library's tests fit (the largest, a 131072-token
+ * MQA layer, needs 8.5 MB).  The first call on a device also launches one
+ * fill kernel on `stream` that zeroes the array.  Every call on a GPU shares
+ * that GPU's array, so calls that overlap in time on one GPU race (as calls
+ * sharing a workspace do): serialize them, e.g. on one stream.  Same
+ * arguments, options, results and pool writes as pkv_decode_step. */
+int pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                            void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                            int32_t dtype, const pkv_decode_opts* opts);
+
 /* The split half of pkv_decode_step alone (same arguments): the fused append
  * and the decode kernel, leaving multi-chunk rows to pkv_lse_combine exactly
  * as pkv_paged_decode_split does. */

@@ -78,6 +78,8 @@ SIGNATURES = {
     "pkv_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                        _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz,
                                        ctypes.POINTER(DecodeOpts)]),
+    "pkv_decode_step_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                               _vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(DecodeOpts)]),
     "pkv_decode_step_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
                                              _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz,
                                              ctypes.POINTER(DecodeOpts)]),

@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "pkv_internal.h"
@@ -44,6 +45,14 @@
 #ifndef PKV_PREFETCH_PAGES
 #define PKV_PREFETCH_PAGES 2
 #endif
+
+// Device scratch for callers that cannot allocate (pkv_decode_step_noalloc):
+// the decode workspace of those calls, one array per GPU the library runs
+// on, held until the process ends.  Host code never uses this name as an
+// address: the per-device address comes from hipGetSymbolAddress (see
+// scratch_of_current_device).
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace pkv {
 namespace {
@@ -2277,6 +2286,45 @@ int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, 
   return PKV_OK;
 }
 
+// Zero fill of n 32-bit words (the scratch's first use on a device).
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t* p, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+// The scratch array's address on the current device.  Set up once per
+// device, with that device current: the address comes from
+// hipGetSymbolAddress (each GPU holds its own copy of the array at its own
+// address), and the array is cleared once by a fill kernel on the caller's
+// stream, since the decode's counters must be zero before its first use
+// (every call leaves them zero afterwards).  A kernel, not hipMemsetAsync, so
+// that a first call made under graph capture records no memset node.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "scratch: device index above " + std::to_string(kMaxScratchDevices - 1));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (ptr == nullptr || !aligned(ptr, 256)) return fail(PKV_ERR_HIP, "scratch: unexpected symbol address");
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                       kScratchBytes / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("scratch clear launch", e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
 int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                   const void* k_new, const void* v_new,
                   const void* k_pages, const void* v_pages, const void* meta, const int32_t* block_table,
@@ -2284,7 +2332,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                   int32_t block_size, float scale, void* out, void* stream, int32_t batch,
                   int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, void* workspace,
                   size_t workspace_bytes, const pkv_decode_opts* opts, int32_t q_len = 1,
-                  int32_t window = 0) {
+                  int32_t window = 0, bool use_scratch = false) {
   int st = check_decode_shapes(fn, n_q_heads, n_kv_heads, head_dim, block_size, batch,
                                max_blocks_per_seq, num_pages, dtype);
   if (st != PKV_OK) return st;
@@ -2296,8 +2344,9 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   if (q_len > 1 && k_new != nullptr)
     return fail(PKV_ERR_INVALID_ARG, f + ": the fused append takes one token per sequence");
   if (batch == 0) return ok();
-  if (!seq_lens || !out || !workspace || !aligned(seq_lens, 4) || !aligned(out, 16) ||
-      !aligned(workspace, 256))
+  if (use_scratch) workspace_bytes = kScratchBytes;   // the device array, resolved after the checks
+  if (!seq_lens || !out || (!use_scratch && (!workspace || !aligned(workspace, 256))) || !aligned(seq_lens, 4) ||
+      !aligned(out, 16))
     return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned seq_lens/out/workspace");
   if (do_split && (!q || !k_pages || !v_pages || !block_table || !aligned(q, 16) ||
                    !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(block_table, 4)))
@@ -2324,7 +2373,14 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   const int64_t need = pkv_decode_workspace_bytes(batch, n_q_heads * q_len, n_kv_heads, head_dim, r.n_items);
   if (need < 0) return static_cast<int>(need);
   if (workspace_bytes < static_cast<size_t>(need))
-    return fail(PKV_ERR_WORKSPACE, f + ": workspace needs " + std::to_string(need) + " bytes");
+    return fail(PKV_ERR_WORKSPACE, f + (use_scratch ? ": these shapes need " + std::to_string(need) +
+                                                          " bytes of scratch, above the library's fixed " +
+                                                          std::to_string(kScratchBytes) + " bytes"
+                                                    : ": workspace needs " + std::to_string(need) + " bytes"));
+  if (use_scratch) {
+    st = scratch_of_current_device(static_cast<hipStream_t>(stream), &workspace);
+    if (st != PKV_OK) return st;
+  }
 
   const int64_t slots = decode_slots(batch, n_kv_heads, r.n_items);
   DecodeArgs a;
@@ -2573,6 +2629,18 @@ int pkv_decode_step_split(const void* q, const void* k_new, const void* v_new, v
                             v_pages, nullptr, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim,
                             block_size, scale, out, stream, batch, max_blocks_per_seq, num_pages,
                             dtype, workspace, workspace_bytes, opts);
+}
+
+int pkv_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                            const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,
+                            void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
+                            int32_t dtype, const pkv_decode_opts* opts) {
+  if (batch > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_noalloc: k_new and v_new are required");
+  return pkv::decode_common(true, true, "pkv_decode_step_noalloc", q, k_new, v_new, k_pages, v_pages, nullptr,
+                            block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out, stream,
+                            batch, max_blocks_per_seq, num_pages, dtype, nullptr, 0, opts, 1, 0, true);
 }
 
 int pkv_lse_combine(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens,
