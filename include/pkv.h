@@ -447,14 +447,18 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_bloc
  * attended page's K and V tiles through the block table with the decode
  * kernel's loads, and writes one XOR of the bytes per chunk to sink (device
  * uint32 [n_items], sink_bytes >= 4 * n_items).  k_pages / v_pages are laid
- * out as for the dense decode, except that consecutive pages may sit
- * page_stride_bytes apart (0: n_kv_heads tiles, the library's layout; a
- * larger multiple of 16 models a padded page).  Dense dtypes only; page ids
- * outside [0, num_pages) and invalid lengths are skipped. */
+ * out as for the dense decode, except that the tile of (page p, KV head h)
+ * starts p * page_stride_bytes + h * head_stride_bytes after each base
+ * (0 and 0: n_kv_heads tiles and one tile, the library's layout; larger
+ * multiples of 16 model padded pages, or K and V interleaved per head with
+ * v_pages = k_pages + one tile and a head stride of two tiles).  Dense
+ * dtypes only; page ids outside [0, num_pages) and invalid lengths are
+ * skipped. */
 int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* block_table,
                      const int32_t* seq_lens, int32_t n_kv_heads, int32_t head_dim, int32_t batch,
                      int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, int64_t page_stride_bytes,
-                     int32_t n_items, int32_t min_chunk_pages, void* sink, size_t sink_bytes, void* stream);
+                     int64_t head_stride_bytes, int32_t n_items, int32_t min_chunk_pages, void* sink,
+                     size_t sink_bytes, void* stream);
 int pkv_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 
 #ifdef __cplusplus

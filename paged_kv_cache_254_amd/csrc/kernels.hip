@@ -1496,6 +1496,251 @@ split_kernel(DecodeArgs a) {
   if constexpr (KV::kFusedAppend) held.store(lane);
 }
 
+// Query tiles wider than the split kernel takes (more than 64 columns per KV
+// head: a prefill chunk, or a long drafted run), for pkv_paged_decode_multi.
+// There is enough independent work without splitting the keys: one
+// wavefront owns a tile of kNB * 16 columns (query tokens x query heads) of
+// one (sequence, KV head) and runs the online softmax over every page its
+// columns attend, from the first tile's window start to its last query
+// token, then writes its output rows; no partials, no merge.  The four
+// wavefronts of a workgroup take four adjacent tiles of one (sequence, KV
+// head) and read the same pages at about the same time.  Every tile of a
+// pair runs on one XCD: the hardware hands workgroup i to XCD i mod 8, so
+// workgroup i takes pair 8 * (s / n_wg) + i mod 8 (s = i / 8, n_wg
+// workgroups per pair), and the pair's K/V are read from HBM about once,
+// then served by that XCD's L2.
+//
+// The page step is arranged for the matrix cores: the score products of
+// every block first, then masks (only on pages where some column's range
+// [lo, hi) starts or ends, under one uniform branch), then the
+// exponentials and the PV products, all in one basic block.  A column's
+// running maximum is set from the first page where it sees a key (its sum
+// and accumulator are still zero then, so nothing is rescaled) and is not
+// raised afterwards: later scores may exceed it by up to kPrefillHeadroom
+// (log2 units), so the exponentials stay <= 2^64, far inside the fp32 and
+// bf16 range, and the accumulators are touched only by the matrix cores.
+// If a score ever exceeds that (scores of very different sizes in one
+// tile), the tile is redone exactly: one pass for every column's true
+// maximum, then the accumulation again from zero with that maximum fixed.
+constexpr float kPrefillHeadroom = 64.0f;
+
+template <bool kBf16, int D, int kNB>
+struct PrefillTile {
+  using O = Ops<kBf16, D>;
+  u32x4 q[kNB][O::NK];
+  int hi[kNB], lo[kNB];      // keys [lo, hi) of this lane's column
+  float m[kNB], l[kNB];
+  f32x4 acc[kNB][O::NV];
+
+  __device__ void reset() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      m[k] = kNoKeysMax;
+      l[k] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Scores of page r in log2 units, masked to each column's key range when
+  // `cut`; pm: this lane's maximum per block.
+  __device__ void scores(const PageRegs<kBf16, D>& r, bool cut, int tok0, float scale_log2, int c,
+                         float (&x)[kNB][4], float (&pm)[kNB]) const {
+    f32x4 s[kNB];
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) s[k] = O::qk(r.k, q[k]);
+#pragma unroll
+    for (int k = 0; k < kNB; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[k][i] = s[k][i] * scale_log2;
+    if (cut) {
+#pragma unroll
+      for (int k = 0; k < kNB; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tok0 + 4 * c + i;
+          const bool in = (t < hi[k]) & (t >= lo[k]);
+          x[k][i] = in ? x[k][i] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) pm[k] = fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3]));
+  }
+
+  // One page of the accumulation.  Returns true (wave-uniform) if some
+  // score exceeded its column's maximum by more than kPrefillHeadroom.
+  // fixed: the maxima are exact already (the redo pass).
+  __device__ bool page(PageRegs<kBf16, D>& r, int valid, bool cut, int tok0, float scale_log2, int c, bool fixed) {
+    float x[kNB][4], pm[kNB];
+    scores(r, cut, tok0, scale_log2, c, x, pm);
+    if (valid < kBlock) {
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::mask_v(r.v[nb], c, valid);
+    }
+    bool init = false, over = false;
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      const bool unset = m[k] == kNoKeysMax;
+      init |= unset & (pm[k] > kNoKeysMax);
+      over |= !unset & (pm[k] > m[k] + kPrefillHeadroom);
+    }
+    if (!fixed && __builtin_amdgcn_ballot_w64(init) != 0) {
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[k][i] - m[k]);
+      O::pv(r.v, p, l[k], acc[k]);
+    }
+    return __builtin_amdgcn_ballot_w64(over) != 0;
+  }
+
+  // Exact per-column maximum over page r (the redo pass).
+  __device__ void page_max(const PageRegs<kBf16, D>& r, bool cut, int tok0, float scale_log2, int c) {
+    float x[kNB][4], pm[kNB];
+    scores(r, cut, tok0, scale_log2, c, x, pm);
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      m[k] = fmaxf(m[k], cm);
+    }
+  }
+};
+
+#ifndef PKV_PREFILL_WAVES_PER_EU
+#define PKV_PREFILL_WAVES_PER_EU 1
+#endif
+template <bool kBf16, int D, int kNB, int kDepth>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
+prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_groups) {
+  using O = Ops<kBf16, D>;
+  using Regs = PageRegs<kBf16, D>;
+  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int kBufs = kDepth + 1;
+  constexpr int kCols = kNB * 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uni(threadIdx.x / kWave);
+  const int i = static_cast<int>(blockIdx.x);
+  const int slot = i >> 3;
+  const int pg_group = slot / wg_per_pair;
+  if (pg_group >= n_pair_groups) return;
+  const int pair = pg_group * 8 + (i & 7);
+  const int tile = (slot - pg_group * wg_per_pair) * kWavesPerGroup + wave;
+  if (pair >= a.batch * a.n_kv || tile >= tiles_per_pair) return;
+  const int b = pair / a.n_kv;
+  const int h = pair - b * a.n_kv;
+  const int g0 = tile * kCols;                          // first column of the tile
+  const int len = seq_len_of(a, b);
+  const bool len_ok = len >= a.q_len && len <= a.max_blocks * kBlock;
+  // Keys the tile's columns attend: from the window start of its first
+  // query token to its last query token.
+  const int qi0 = g0 / a.group;
+  const int qi1 = min(a.q_len - 1, (min(g0 + kCols, a.cols) - 1) / a.group);
+  const int hi = len - a.q_len + qi1 + 1;
+  const int lo = a.window > 0 ? max(0, len - a.q_len + qi0 + 1 - a.window) : 0;
+  const int fb = len_ok ? lo / kBlock : 0;
+  const int cnt = len_ok && hi > 0 ? (hi - 1) / kBlock + 1 - fb : 0;
+  // The tile's smallest causal bound (its first query token) and largest
+  // window start (its last query token): pages wholly inside [lo1, hi0)
+  // need no masks.
+  const int hi0 = len - a.q_len + qi0 + 1;
+  const int lo1 = a.window > 0 ? max(0, hi - a.window) : 0;
+  const int c = lane >> 4, n = lane & 15;
+
+  // Query operands and key ranges per block; column g = (query token qi,
+  // query head gq); columns past the tile's end hold zeros and write nothing.
+  PrefillTile<kBf16, D, kNB> t;
+#pragma unroll
+  for (int k = 0; k < kNB; ++k) {
+    const int g = g0 + 16 * k + n;
+    const bool g_ok = g < a.cols;
+    const int qi = g / a.group;
+    const int hq = h * a.group + (g - qi * a.group);
+    const size_t qrow = g_ok ? (static_cast<size_t>(b) * a.q_len + qi) * a.n_q + hq : 0;
+    const char* qb = static_cast<const char*>(a.q) + qrow * D * O::ES;
+#pragma unroll
+    for (int j = 0; j < O::NK; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * j + c));
+      t.q[k][j] = g_ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+    t.hi[k] = len - a.q_len + qi + 1;
+    t.lo[k] = a.window > 0 ? max(0, t.hi[k] - a.window) : 0;
+  }
+  const const_i32* row = (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks);
+  const char* kp0 = static_cast<const char*>(a.k_pages);
+  const char* vp0 = static_cast<const char*>(a.v_pages);
+  bool bad = !len_ok;
+  auto load = [&](Regs& r, int j) {
+    const int pg = j < cnt ? row[fb + j] : -1;
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    const size_t off = (static_cast<size_t>(ok ? pg : 0) * a.n_kv + h) * kTile;
+    load_page<kBf16, D>(r, kp0 + off, vp0 + off, 16u * lane, O::ES * (n * kBlock + 4 * c), ok ? kTile : 0);
+    return pg;
+  };
+  // The accumulation over the tile's pages through a ring kDepth pages
+  // deep; returns true if some score overran its column's maximum.
+  auto run = [&](bool fixed) {
+    Regs buf[kBufs];
+    int page_of[kBufs];
+    int issued = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) page_of[s] = load(buf[s], issued++);
+    int p = 0;
+    while (p < cnt) {
+#pragma unroll
+      for (int s = 0; s < kBufs; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        page_of[(s + kDepth) % kBufs] = load(buf[(s + kDepth) % kBufs], issued++);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < cnt) {
+          bad |= static_cast<unsigned>(page_of[s]) >= static_cast<unsigned>(a.num_pages);
+          const int tok0 = kBlock * (fb + p);
+          const bool cut = tok0 + kBlock > hi0 || tok0 < lo1;
+          overflow |= t.page(buf[s], len - tok0, cut, tok0, a.scale_log2, c, fixed);
+        }
+        ++p;
+      }
+    }
+    return overflow;
+  };
+  t.reset();
+  if (run(false)) {
+    // Rare: redo the tile with every column's exact maximum.
+    t.reset();
+    for (int p = 0; p < cnt; ++p) {
+      Regs r;
+      load(r, p);
+      const int tok0 = kBlock * (fb + p);
+      t.page_max(r, tok0 + kBlock > hi0 || tok0 < lo1, tok0, a.scale_log2, c);
+    }
+    run(true);
+  }
+  // A length of 0 gives zero rows (no key seen), an invalid one NaN rows.
+  bad = bad && len != 0;
+#pragma unroll
+  for (int k = 0; k < kNB; ++k) {
+    float lt = t.l[k] + __shfl_xor(t.l[k], 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = bad ? NAN : (lt > 0.f ? 1.0f / lt : 0.f);
+    const int g = g0 + 16 * k + n;
+    if (g < a.cols) {
+      const size_t orow = out_row<true>(a, b, h, g) * D;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) O::store_out(a.out, orow + 16 * nb + 4 * c, t.acc[k][nb] * inv);
+    }
+  }
+}
+
 // Counts the arrivals of the listed pairs after this wavefront's partial
 // stores have completed (one lane per pair, up to 64 atomics in flight
 // together), merges the pairs for which it arrived last, and empties the
@@ -2002,12 +2247,14 @@ copy_blocks_kernel(char* k_pages, char* v_pages, const int32_t* src, const int32
 // whole ring turns), but each tile is only folded into an XOR that keeps
 // the loads live.  Its rate is what the memory system sustains for the
 // workload's own tile list, the ceiling the decode kernel is held to.
-// page_stride: bytes between consecutive pages of the pools (n_kv tiles for
-// the library's layout; larger values model padded page layouts).
+// page_stride / head_stride: bytes between consecutive pages and between
+// the KV heads of a page (n_kv tiles and one tile in the library's layout;
+// other values model padded pages, or K and V tiles interleaved per head
+// when v_pages = k_pages + one tile and head_stride = two tiles).
 template <bool kBf16, int D, int kDepth>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 __attribute__((amdgpu_waves_per_eu(kSplitWavesPerEu<kBf16, D>)))
-gather_probe_kernel(DecodeArgs a, size_t page_stride, uint32_t* sink) {
+gather_probe_kernel(DecodeArgs a, size_t page_stride, size_t head_stride, uint32_t* sink) {
   using O = Ops<kBf16, D>;
   constexpr int kTile = kBlock * D * O::ES;
   constexpr int kBufs = kDepth + 1;
@@ -2036,7 +2283,7 @@ gather_probe_kernel(DecodeArgs a, size_t page_stride, uint32_t* sink) {
       const bool in = issued < cnt;
       const int pg = ((const const_i32*)(a.block_table + static_cast<size_t>(ld.b) * a.max_blocks))[ld.j];
       const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-      const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * kTile;
+      const size_t off = static_cast<size_t>(ok ? pg : 0) * page_stride + static_cast<size_t>(ld.h) * head_stride;
       load_page<kBf16, D>(r, kp0 + off, vp0 + off, 16u * lane, O::ES * (n * kBlock + 4 * c), in && ok ? kTile : 0);
       if (in) {
         ++issued;
@@ -2325,6 +2572,61 @@ int scratch_of_current_device(hipStream_t stream, void** out) {
   return PKV_OK;
 }
 
+#ifndef PKV_PREFILL_DEPTH
+#define PKV_PREFILL_DEPTH 2
+#endif
+// 16-column blocks (query tokens x query heads of one KV head) per
+// wavefront of the prefill kernel, and its ring depth.  Four blocks fit the
+// register file (bf16: 256 VGPRs + 236 AGPRs at head_dim 128, no scratch);
+// fp32 at head_dim 128 takes two, with one page ahead.
+#ifndef PKV_PREFILL_BLOCKS
+#define PKV_PREFILL_BLOCKS 4
+#endif
+constexpr int kPrefillBlocks = PKV_PREFILL_BLOCKS;
+constexpr int kPrefillDepth = PKV_PREFILL_DEPTH;
+inline int prefill_blocks(int dtype, int head_dim) { return dtype == PKV_F32 && head_dim == 128 ? 2 : kPrefillBlocks; }
+
+int launch_prefill(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                   const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float scale,
+                   void* out, hipStream_t stream, int32_t batch, int32_t max_blocks, int32_t num_pages,
+                   int32_t dtype, int32_t q_len, int32_t window) {
+  DecodeArgs a{};
+  a.q = q;
+  a.k_pages = const_cast<void*>(k_pages);
+  a.v_pages = const_cast<void*>(v_pages);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.batch = batch;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.group = n_q_heads / n_kv_heads;
+  a.q_len = q_len;
+  a.window = window;
+  a.cols = q_len * a.group;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  a.scale_log2 = scale * kLog2e;
+  const int tile_cols = prefill_blocks(dtype, head_dim) * 16;
+  const int tiles = (a.cols + tile_cols - 1) / tile_cols;
+  const int wg_per_pair = (tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t pairs = static_cast<int64_t>(batch) * n_kv_heads;
+  const int64_t groups = (pairs + 7) / 8;
+  const int64_t grid = groups * wg_per_pair * 8;
+  if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_multi: too many query tiles");
+  using Fn = void (*)(DecodeArgs, int, int, int);
+  const Fn fn = dtype == PKV_BF16
+                    ? (head_dim == 128 ? prefill_kernel<true, 128, kPrefillBlocks, kPrefillDepth>
+                                       : prefill_kernel<true, 64, kPrefillBlocks, kPrefillDepth>)
+                    : (head_dim == 128 ? prefill_kernel<false, 128, 2, 1>
+                                       : prefill_kernel<false, 64, kPrefillBlocks, kPrefillDepth>);
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kWave * kWavesPerGroup), 0, stream, a, tiles,
+                     wg_per_pair, static_cast<int>(groups));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("prefill kernel launch", e);
+  return ok();
+}
+
 int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
                   const void* k_new, const void* v_new,
                   const void* k_pages, const void* v_pages, const void* meta, const int32_t* block_table,
@@ -2339,11 +2641,27 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   std::string f(fn);
   if (q_len < 1 || window < 0)
     return fail(PKV_ERR_INVALID_ARG, f + ": q_len must be >= 1 and window >= 0");
-  if (static_cast<int64_t>(q_len) * (n_q_heads / n_kv_heads) > kMaxGroup)
-    return fail(PKV_ERR_UNSUPPORTED, f + ": q_len * (n_q_heads / n_kv_heads) above 64");
+  // Wide query tiles (more than 64 columns per KV head): the prefill kernel,
+  // one call of pkv_paged_decode_multi, dense caches, no workspace.
+  const bool wide = static_cast<int64_t>(q_len) * (n_q_heads / n_kv_heads) > kMaxGroup;
+  if (wide && (!do_split || !do_combine || dtype == PKV_U8 || use_scratch))
+    return fail(PKV_ERR_UNSUPPORTED, f + ": q_len * (n_q_heads / n_kv_heads) above 64 is taken by "
+                                         "pkv_paged_decode_multi on a dense cache only");
+  if (wide && static_cast<int64_t>(q_len) * n_q_heads > (int64_t{1} << 20))
+    return fail(PKV_ERR_UNSUPPORTED, f + ": q_len * n_q_heads above 2^20");
   if (q_len > 1 && k_new != nullptr)
     return fail(PKV_ERR_INVALID_ARG, f + ": the fused append takes one token per sequence");
   if (batch == 0) return ok();
+  if (wide) {
+    if (!seq_lens || !out || !q || !k_pages || !v_pages || !block_table || !aligned(seq_lens, 4) ||
+        !aligned(out, 16) || !aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+        !aligned(block_table, 4))
+      return fail(PKV_ERR_INVALID_ARG, f + ": NULL or misaligned q/k_pages/v_pages/block_table/seq_lens/out");
+    if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, f + ": scale is not finite");
+    return launch_prefill(q, k_pages, v_pages, block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, scale, out,
+                          static_cast<hipStream_t>(stream), batch, max_blocks_per_seq, num_pages, dtype, q_len,
+                          window);
+  }
   if (use_scratch) workspace_bytes = kScratchBytes;   // the device array, resolved after the checks
   if (!seq_lens || !out || (!use_scratch && (!workspace || !aligned(workspace, 256))) || !aligned(seq_lens, 4) ||
       !aligned(out, 16))
@@ -2763,16 +3081,19 @@ int pkv_copy_blocks(void* k_pages, void* v_pages, const int32_t* src_pages,
 int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* block_table,
                      const int32_t* seq_lens, int32_t n_kv_heads, int32_t head_dim, int32_t batch,
                      int32_t max_blocks_per_seq, int32_t num_pages, int32_t dtype, int64_t page_stride_bytes,
-                     int32_t n_items, int32_t min_chunk_pages, void* sink, size_t sink_bytes, void* stream) {
+                     int64_t head_stride_bytes, int32_t n_items, int32_t min_chunk_pages, void* sink,
+                     size_t sink_bytes, void* stream) {
   int st = pkv::check_decode_shapes("pkv_gather_probe", n_kv_heads, n_kv_heads, head_dim, pkv::kBlock, batch,
                                     max_blocks_per_seq, num_pages, dtype);
   if (st != PKV_OK) return st;
   if (dtype == PKV_U8) return fail(PKV_ERR_UNSUPPORTED, "pkv_gather_probe: dense caches only (PKV_F32, PKV_BF16)");
   const int64_t tile = static_cast<int64_t>(pkv::kBlock) * head_dim * (dtype == PKV_BF16 ? 2 : 4);
-  const int64_t stride = page_stride_bytes > 0 ? page_stride_bytes : tile * n_kv_heads;
-  if (stride < tile * n_kv_heads || stride % 16 != 0)
-    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe: page_stride_bytes must be 0 or a multiple of 16 of at "
-                                     "least n_kv_heads tiles");
+  const int64_t hstride = head_stride_bytes > 0 ? head_stride_bytes : tile;
+  const int64_t stride = page_stride_bytes > 0 ? page_stride_bytes : hstride * n_kv_heads;
+  if (hstride < tile || hstride % 16 != 0 || stride < hstride * n_kv_heads || stride % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe: head_stride_bytes must be 0 or a multiple of 16 of at "
+                                     "least one tile, page_stride_bytes 0 or a multiple of 16 of at least "
+                                     "n_kv_heads head strides");
   if (batch == 0) return ok();
   if (!k_pages || !v_pages || !block_table || !seq_lens || !sink || !pkv::aligned(k_pages, 16) ||
       !pkv::aligned(v_pages, 16) || !pkv::aligned(block_table, 4) || !pkv::aligned(seq_lens, 4) ||
@@ -2802,7 +3123,7 @@ int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* bl
   a.min_chunk = r.min_chunk;
   const size_t lds = pkv::split_lds_bytes(batch);
   if (lds > pkv::kMaxLdsBytes) return fail(PKV_ERR_UNSUPPORTED, "pkv_gather_probe: batch too large");
-  using Fn = void (*)(pkv::DecodeArgs, size_t, uint32_t*);
+  using Fn = void (*)(pkv::DecodeArgs, size_t, size_t, uint32_t*);
   const Fn fn = dtype == PKV_BF16
                     ? (head_dim == 128 ? pkv::gather_probe_kernel<true, 128, pkv::kPrefetchPages>
                                        : pkv::gather_probe_kernel<true, 64, pkv::kPrefetchPages>)
@@ -2810,7 +3131,7 @@ int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* bl
                                        : pkv::gather_probe_kernel<false, 64, 1>);
   const int grid = (r.n_items + pkv::kWavesPerGroup - 1) / pkv::kWavesPerGroup;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(pkv::kWave * pkv::kWavesPerGroup), lds, static_cast<hipStream_t>(stream),
-                     a, static_cast<size_t>(stride), static_cast<uint32_t*>(sink));
+                     a, static_cast<size_t>(stride), static_cast<size_t>(hstride), static_cast<uint32_t*>(sink));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv::hip_fail("gather probe launch", e);
   return ok();

@@ -342,15 +342,33 @@ def copy_probe(dst, src, stream=None) -> None:
 
 
 def gather_probe(k_pages, v_pages, block_table, seq_lens, sink, n_items: int = 0, min_chunk_pages: int = 0,
-                 page_stride_bytes: int = 0, num_pages: int = 0, stream=None) -> None:
-    """The decode kernel's tile stream without arithmetic (see pkv_gather_probe).
-    k_pages [P][Hkv][D/X][16][X] (or a padded buffer with page_stride_bytes and
-    num_pages given); sink: device int32 with at least n_items entries."""
+                 stream=None) -> None:
+    """The decode kernel's tile stream without arithmetic (see pkv_gather_probe),
+    on pools in the library's layout, k_pages [P][Hkv][D/X][16][X]; sink:
+    device int32 with at least n_items entries."""
     B = block_table.shape[0]
-    P = num_pages if num_pages > 0 else k_pages.shape[0]
     Hkv = k_pages.shape[1]
     D = k_pages.shape[2] * k_pages.shape[4]
     check(lib.pkv_gather_probe(_ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hkv, D, B,
-                               block_table.shape[1], P, _dtype_code(k_pages), int(page_stride_bytes), int(n_items),
+                               block_table.shape[1], k_pages.shape[0], _dtype_code(k_pages), 0, 0, int(n_items),
                                int(min_chunk_pages), _ptr(sink), sink.numel() * sink.element_size(), _stream(stream)),
           "pkv_gather_probe")
+
+
+def paged_decode_multi(q, k_pages, v_pages, block_table, seq_lens, q_len: int, scale, out, window: int = 0,
+                       workspace=None, n_items: int = 0, min_chunk_pages: int = 0, stream=None):
+    """pkv_paged_decode_multi: the last q_len cached tokens of each sequence
+    attend causally (optional sliding window).  q, out: [B][q_len][Hq][D].
+    Query tiles of more than 64 columns per KV head (q_len x Hq / Hkv) run the
+    prefill kernel and need no workspace; smaller ones need one sized for
+    Hq * q_len query heads (or use Decoder.attn_multi)."""
+    B, T, Hq, D = q.shape
+    if T != q_len:
+        raise ValueError("q must be [B][q_len][Hq][D]")
+    ws, ws_bytes = (0, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    check(lib.pkv_paged_decode_multi(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), Hq,
+                                     k_pages.shape[1], D, BLOCK_SIZE, q_len, window, float(scale), _ptr(out),
+                                     _stream(stream), B, block_table.shape[1], k_pages.shape[0], _dtype_code(q),
+                                     ws or None, ws_bytes, _opts(n_items, min_chunk_pages, 0, 0)),
+          "pkv_paged_decode_multi")
+    return out
