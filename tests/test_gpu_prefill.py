@@ -130,3 +130,30 @@ def test_full_size_prefill_gqa(pkv, T, window):
     H.log(f"  {len(got)} rows of {len(bs)} sequences: max {mx:.2e} mean {mean:.2e} rel {rel:.2e}")
     del c, q, out
     torch.cuda.empty_cache()
+
+
+def test_prefill_huge_score_takes_the_exact_redo(pkv):
+    """One key late in each sequence is 30 times a query vector, so scores
+    jump by hundreds (log2 units) past the running maxima set on the first
+    pages: the tile is redone with exact maxima.  Against the oracle."""
+    B, Hq, Hkv, D, T = 2, 8, 2, 128, 24
+    lens = [300, 160]
+    w = W.custom("prefill_huge", B, Hq, Hkv, D, "bf16", lens, seed=214)
+    c = H.setup(w, device="cuda", gen_device="cpu")
+    g = torch.Generator().manual_seed(215)
+    q = torch.randn((B, T, Hq, D), generator=g).to(torch.bfloat16)
+    k = c.k_pages.cpu()
+    X = k.shape[4]
+    for b, n in enumerate(lens):
+        t = n - 8                                          # seen by the last 8 query tokens only
+        p, s = int(c.bt_np[b, t // 16]), t % 16
+        for h in range(Hkv):
+            k[p, h, :, s, :] = (30.0 * q[b, T - 1, h * (Hq // Hkv)].float()).to(torch.bfloat16).view(D // X, X)
+    c.k_pages = k.cuda()
+    att = np.array(lens, dtype=np.int64)
+    ref = OA.decode_multi(H.f64(q), H.f64(c.k_pages), H.f64(c.v_pages), c.bt_np, att, T, Hq, Hkv, 16, w.scale, 0)
+    out = torch.full((B, T, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pkv.paged_decode_multi(q.cuda(), c.k_pages, c.v_pages, c.bt, torch.from_numpy(att.astype(np.int32)).cuda(), T,
+                           w.scale, out, 0)
+    torch.cuda.synchronize()
+    H.assert_close(H.f64(out), ref, "bf16", "prefill huge score")
