@@ -1741,6 +1741,267 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
   }
 }
 
+// Split-KV decode for 33 to 64 columns per KV head (MQA, or several query
+// tokens of a large group), bf16.  One wavefront computes all 64 columns of
+// every page it loads (four 16-column blocks, the prefill kernel's page
+// step), so each tile is loaded once per workgroup and the per-page work
+// (page id, buffer resources, masks, cursors) is done once per page; the
+// kernel with one wavefront per 16-column block repeated it four times and
+// streamed a quarter as many distinct pages.  A chunk is a workgroup's:
+// its four wavefronts take the chunk's pages in turn (wavefront w the pages
+// w, w + 4, ...), so they stream four neighbouring pages of the same pair
+// at a time.  The four walk the chunk's segments (the runs of pages of one
+// (sequence, KV head) pair) together; at the end of each segment they
+// merge their four partial softmax states through LDS, one 16-column block
+// per round, and wavefront j writes block j of the segment's result: the
+// output rows when the pair lies in this chunk, else the chunk's partial,
+// merged with the pair's other chunks by the last to arrive (the same
+// slots, counters and merge as the other split kernels, per block j).
+// Running maxima are set on a column's first keys and not raised in the
+// page loop, with the prefill kernel's headroom; a segment that overruns
+// it is recomputed by that wavefront with exact maxima before the merge.
+// The number of segment ends is the same for the four wavefronts, so they
+// pass the same number of workgroup barriers.
+template <bool kBf16, int D, bool kMulti, int kDepth>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(1)))
+wide_kernel(DecodeArgs a) {
+  using O = Ops<kBf16, D>;
+  using Regs = PageRegs<kBf16, D>;
+  constexpr int kNB = 4;
+  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int kBufs = kDepth + 1;
+  constexpr int kSlotWords = 16 * (D + 2);   // one wavefront's block: rows [16][D], maxima [16], sums [16]
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, a.q_len, a.window, s_prefix, smem + a.batch + 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uni(threadIdx.x / kWave);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.batch; i += blockDim.x) a.prefix[i] = s_prefix[i];
+  if (a.counters != nullptr && blockIdx.x == 0 && wave == 0) write_empty_rows(a, s_prefix, D, kBf16, lane);
+  const int chunk = static_cast<int>(blockIdx.x);
+  if (chunk >= a.n_items) return;                       // the whole workgroup
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int64_t f64 = static_cast<int64_t>(chunk) * C;
+  if (f64 >= total) return;                             // the whole workgroup
+  const int f0 = static_cast<int>(f64);
+  const int fend = static_cast<int>(min(f64 + C, static_cast<int64_t>(total)));
+  const int c = lane >> 4, n = lane & 15;
+  float* mlds = reinterpret_cast<float*>(smem) + a.wg_lds_offset;
+  const size_t page_stride = static_cast<size_t>(kTile) * a.n_kv;
+  char* kp0 = static_cast<char*>(a.k_pages);
+  char* vp0 = static_cast<char*>(a.v_pages);
+  auto bt_row = [&](int b) { return (const const_i32*)(a.block_table + static_cast<size_t>(b) * a.max_blocks); };
+
+  // ---- segments of the chunk (the same walk in every wavefront)
+  FlatCursor<kMulti> sg;
+  sg.seek(a, s_prefix, f0);
+  int seg_start = 0, seg_hi = 0, len = 0;              // pair's first flat page; end of the segment in the chunk
+  PrefillTile<kBf16, D, kNB> t;
+  bool bad = false, overflow = false;
+  PendingMerges pending;
+  // A segment's bounds (scalar), then its query operands and state; split
+  // so that the segment's first tile loads are in flight while the query
+  // rows arrive.
+  auto bounds = [&]() {
+    seg_start = a.n_kv * sg.pb + sg.h * sg.n;
+    seg_hi = min(seg_start + sg.n, fend);
+    len = seq_len_of(a, sg.b);
+  };
+  auto open = [&]() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      const int g = 16 * k + n;
+      const bool g_ok = g < a.cols;
+      const int qi = kMulti ? g / a.group : 0;
+      const int hq = sg.h * a.group + (g - qi * a.group);
+      const int ql = kMulti ? a.q_len : 1;
+      const size_t qrow = g_ok ? (static_cast<size_t>(sg.b) * ql + qi) * a.n_q + hq : 0;
+      const char* qb = static_cast<const char*>(a.q) + qrow * D * O::ES;
+#pragma unroll
+      for (int j = 0; j < O::NK; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * j + c));
+        t.q[k][j] = g_ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+      t.hi[k] = len - ql + qi + 1;
+      t.lo[k] = kMulti && a.window > 0 ? max(0, t.hi[k] - a.window) : 0;
+    }
+    t.reset();
+    bad = false;
+    overflow = false;
+  };
+  // Page f of the flattened order, in this segment: its tile id, first
+  // token, masks; the fused append's token is put into the registers of the
+  // pair's last page and stored to the pool.
+  auto page_at = [&](Regs& r, int pg, int f, bool fixed) {
+    const int j = f - seg_start;                       // page of the pair
+    const int tok0 = kBlock * (sg.fb + j);
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    bad |= !ok;
+    if constexpr (!kMulti) {
+      if (a.k_new != nullptr && j == sg.n - 1) {
+        const int s_new = (len - 1) & (kBlock - 1);
+        const size_t row = (static_cast<size_t>(sg.b) * a.n_kv + sg.h) * D;
+        u32x4 kn[O::NK];
+        uint32_t vn[O::NV];
+        const char* kb = static_cast<const char*>(a.k_new) + row * O::ES;
+#pragma unroll
+        for (int i = 0; i < O::NK; ++i) kn[i] = *reinterpret_cast<const u32x4*>(kb + 16 * (4 * i + c));
+#pragma unroll
+        for (int nb = 0; nb < O::NV; ++nb) {
+          if constexpr (kBf16) vn[nb] = static_cast<const uint16_t*>(a.v_new)[row + 16 * nb + n];
+          else vn[nb] = static_cast<const uint32_t*>(a.v_new)[row + 16 * nb + n];
+        }
+        if (n == s_new) {
+#pragma unroll
+          for (int i = 0; i < O::NK; ++i) r.k[i] = kn[i];
+        }
+        if (c == (s_new >> 2)) {
+#pragma unroll
+          for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::insert_v(r.v[nb], s_new & 3, vn[nb]);
+        }
+        if (ok && !fixed) {
+          const size_t off = static_cast<size_t>(pg) * page_stride + static_cast<size_t>(sg.h) * kTile;
+          HeldToken<kBf16, D, false>::store_regs(kn, vn, kp0 + off, vp0 + off, s_new, lane);
+        }
+      }
+    }
+    const bool cut = kMulti ? (tok0 + kBlock > len - a.q_len + 1 || (a.window > 0 && tok0 < len - a.window))
+                            : tok0 + kBlock > len;
+    return t.page(r, len - tok0, cut, tok0, a.scale_log2, c, fixed);
+  };
+  auto load_flat = [&](Regs& r, int f) {              // page f of this segment, loaded and waited for
+    const int pg = bt_row(sg.b)[sg.fb + (f - seg_start)];
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    load_page<kBf16, D, PKV_KV_LOAD_AUX>(r, kp0 + (static_cast<size_t>(ok ? pg : 0) * a.n_kv + sg.h) * kTile,
+                                         vp0 + (static_cast<size_t>(ok ? pg : 0) * a.n_kv + sg.h) * kTile,
+                                         16u * lane, O::ES * (n * kBlock + 4 * c), ok ? kTile : 0);
+    return pg;
+  };
+  // End of a segment: exact redo if it overran, then the four-way merge
+  // and block `wave` of the result written out.
+  auto close = [&]() {
+    if (overflow) {
+      const int seg_lo = max(seg_start, f0);
+      const int first = seg_lo + ((wave - (seg_lo - f0)) % 4 + 4) % 4;
+      t.reset();
+      for (int f = first; f < seg_hi; f += 4) {
+        Regs r;
+        load_flat(r, f);
+        const int tok0 = kBlock * (sg.fb + f - seg_start);
+        const bool cut = kMulti ? (tok0 + kBlock > len - a.q_len + 1 || (a.window > 0 && tok0 < len - a.window))
+                                : tok0 + kBlock > len;
+        t.page_max(r, cut, tok0, a.scale_log2, c);
+      }
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        t.l[k] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < O::NV; ++nb) t.acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      for (int f = first; f < seg_hi; f += 4) {
+        Regs r;
+        const int pg = load_flat(r, f);
+        page_at(r, pg, f, true);
+      }
+    }
+    f32x4 res[O::NV];
+    float rm = kNoKeysMax, rl = 0.f;
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+      float lt = t.l[j] + __shfl_xor(t.l[j], 16);
+      lt += __shfl_xor(lt, 32);
+      float* slot = mlds + wave * kSlotWords;
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) *reinterpret_cast<f32x4*>(slot + n * D + 16 * nb + 4 * c) = t.acc[j][nb];
+      if (c == 0) {
+        slot[16 * D + n] = t.m[j];
+        slot[16 * D + 16 + n] = bad ? NAN : lt;
+      }
+      __syncthreads();
+      if (wave == j) {
+        float mw[kWavesPerGroup];
+        float mx = kNoKeysMax;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) {
+          mw[w] = mlds[w * kSlotWords + 16 * D + n];
+          mx = fmaxf(mx, mw[w]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < O::NV; ++nb) res[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        rl = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) {
+          const float e = __builtin_amdgcn_exp2f(mw[w] - mx);
+          rl += e * mlds[w * kSlotWords + 16 * D + 16 + n];
+#pragma unroll
+          for (int nb = 0; nb < O::NV; ++nb)
+            res[nb] += e * *reinterpret_cast<const f32x4*>(mlds + w * kSlotWords + n * D + 16 * nb + 4 * c);
+        }
+        rm = mx;
+      }
+      __syncthreads();
+    }
+    // Block `wave` of the segment's result (nothing for blocks past the group).
+    if (16 * wave < a.cols) {
+      const bool nan_row = rl != rl;
+      const float inv = nan_row ? NAN : (rl > 0.f ? 1.0f / rl : 0.f);   // no key seen: zero row, lse -inf
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) res[nb] *= inv;
+      const float lse = nan_row ? NAN : (rm + __log2f(rl)) * kLn2;
+      emit_segment<kBf16, D, kMulti>(a, sg.b, sg.h, wave, sg.n, seg_start, chunk, C, res, lse, lane, pending);
+    }
+  };
+
+  // ---- segment by segment: this wavefront's pages of the segment (every
+  // fourth page of the chunk, from f0 + wave) through a ring kDepth pages
+  // deep, then the segment's end.  One copy of each in the code.
+  bounds();
+  for (;;) {
+    const int seg_lo = max(seg_start, f0);
+    const int first = seg_lo + ((wave - (seg_lo - f0)) % 4 + 4) % 4;
+    const int mine = first < seg_hi ? (seg_hi - first + 3) / 4 : 0;
+    const const_i32* row = bt_row(sg.b) + sg.fb + (first - seg_start);
+    Regs buf[kBufs];
+    int page_of[kBufs];
+    int issued = 0;
+    auto issue = [&](Regs& r, int& pg_out) {
+      const int pg = issued < mine ? row[4 * issued] : -1;
+      const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+      const size_t off = (static_cast<size_t>(ok ? pg : 0) * a.n_kv + sg.h) * kTile;
+      load_page<kBf16, D, PKV_KV_LOAD_AUX>(r, kp0 + off, vp0 + off, 16u * lane, O::ES * (n * kBlock + 4 * c),
+                                           ok ? kTile : 0);
+      pg_out = pg;
+      ++issued;
+    };
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s]);
+    open();
+    int p = 0;
+    while (p < mine) {
+#pragma unroll
+      for (int s = 0; s < kBufs; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf[(s + kDepth) % kBufs], page_of[(s + kDepth) % kBufs]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < mine) overflow |= page_at(buf[s], page_of[s], first + 4 * p, false);
+        ++p;
+      }
+    }
+    close();                                          // every wavefront closes every segment
+    if (seg_hi >= fend) break;
+    sg.seek(a, s_prefix, seg_hi);                     // the chunk's next segment
+    bounds();
+  }
+  if (pending.n > 0 && 16 * wave < a.cols) {
+    const int last = arrive(a, pending, wave, lane);
+    if (last & 1) merge_pair<kBf16, D, kMulti>(a, pending.b0, pending.h0, wave, pending.first0, pending.nparts0, lane);
+    if (last & 2) merge_pair<kBf16, D, kMulti>(a, pending.b1, pending.h1, wave, pending.first1, pending.nparts1, lane);
+  }
+}
+
 // Counts the arrivals of the listed pairs after this wavefront's partial
 // stores have completed (one lane per pair, up to 64 atomics in flight
 // together), merges the pairs for which it arrived last, and empties the
@@ -2422,7 +2683,24 @@ SplitFn dyn_fn(int dtype, int head_dim, bool q8) {
 
 // cols: MFMA columns per KV head (query tokens x query heads); multi: more
 // than one query token or a sliding window (dense caches only).
+// 33 to 64 columns per KV head on a bf16 cache: the wide kernel (one
+// wavefront per page for all four 16-column blocks, pages of a chunk taken
+// in turn by the workgroup's four wavefronts).
+#ifndef PKV_WIDE_DEPTH
+#define PKV_WIDE_DEPTH 2
+#endif
+inline bool uses_wide(int dtype, int cols, bool q8) { return !q8 && dtype == PKV_BF16 && cols > 32; }
+// Its LDS: the page prefix, then four wavefronts' merge slots of 16 columns.
+size_t wide_lds_bytes(int batch, int head_dim) {
+  return (static_cast<size_t>(held_offset(batch)) + kWavesPerGroup * 16 * (head_dim + 2)) * sizeof(int32_t);
+}
+
 SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
+  if (uses_wide(dtype, cols, q8)) {
+    if (multi)
+      return head_dim == 128 ? wide_kernel<true, 128, true, PKV_WIDE_DEPTH> : wide_kernel<true, 64, true, PKV_WIDE_DEPTH>;
+    return head_dim == 128 ? wide_kernel<true, 128, false, PKV_WIDE_DEPTH> : wide_kernel<true, 64, false, PKV_WIDE_DEPTH>;
+  }
   if (cols > 16 && cols <= 32) return multi ? split_fn_wide<true>(dtype, head_dim, q8) : split_fn_wide<false>(dtype, head_dim, q8);
   switch (waves_per_chunk(cols)) {
     case 1: return multi ? split_fn_ng<1, true>(dtype, head_dim, q8) : split_fn_ng<1, false>(dtype, head_dim, q8);
@@ -2506,7 +2784,8 @@ int resolve_opts(int32_t dtype, int32_t head_dim, int32_t group, int32_t batch, 
                                      "(query tokens x group) and a batch whose page prefix fits its LDS");
   r->schedule = (sched == PKV_SCHEDULE_DYNAMIC) ? PKV_SCHEDULE_DYNAMIC : PKV_SCHEDULE_STATIC;
   const bool dyn = r->schedule == PKV_SCHEDULE_DYNAMIC;
-  r->lds = dyn ? dyn_lds_bytes(batch) : split_lds_bytes(batch);
+  r->lds = dyn ? dyn_lds_bytes(batch) : uses_wide(dtype, group, dtype == PKV_U8) ? wide_lds_bytes(batch, head_dim)
+                                                                             : split_lds_bytes(batch);
   r->min_chunk = (opts && opts->min_chunk_pages > 0) ? opts->min_chunk_pages
                  : dyn                                ? kDynMinChunk
                                                       : default_min_chunk(group, dtype == PKV_U8);
@@ -2781,6 +3060,12 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
       a.wg_merge = 1;
       a.wg_lds_offset = static_cast<int32_t>(held_end);
       lds += wg_words * sizeof(float);
+    }
+    if (uses_wide(dtype, cols, q8)) {   // its own LDS: prefix, then the merge slots
+      a.wg_merge = 0;
+      a.held_cap = 0;
+      a.wg_lds_offset = held_offset(batch);
+      lds = r.lds;
     }
   }
   const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
