@@ -344,9 +344,6 @@ def main():
     if u8 and w.dtype != "bf16":
         print("--kv u8 takes a bf16 workload (its q and out stay bf16)", file=sys.stderr)
         sys.exit(2)
-    if u8 and args.unfused:
-        print("--kv u8 always appends with its own (quantizing) kernel; --unfused does not apply", file=sys.stderr)
-        sys.exit(2)
     T, window = args.q_len, args.window
     multi = T > 1 or window > 0
     if multi and (u8 or args.unfused or args.separate_combine or T < 1 or window < 0):
@@ -395,22 +392,40 @@ def main():
                     ev[3 * li + 1].record(stream)
                     ev[3 * li + 2].record(stream)
                 continue
+            if u8 and args.unfused:
+                # the quantizing append kernel, then the decode over the 8-bit cache
+                pkv.kv_append_q8(L.k_new, L.v_new, L.k_pages, L.v_pages, L.meta, S["bt"], S["positions"], stream)
+                if ev is not None:
+                    ev[3 * li].record(stream)
+                if ev is None or one_kernel:
+                    dec.attn_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+                    if ev is not None:
+                        ev[3 * li + 1].record(stream)
+                else:
+                    dec.split_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+                    if ev is not None:
+                        ev[3 * li + 1].record(stream)
+                    dec.combine(S["seq_lens"], L.out, S["mb"], stream)
+                if ev is not None:
+                    ev[3 * li + 2].record(stream)
+                continue
             if u8:
-                if ev is None:
+                if ev is None or one_kernel:
+                    # the library's step: quantizing append fused into the decode kernel
+                    if ev is not None:
+                        ev[3 * li].record(stream)
                     dec.step_q8(L.q, L.k_new, L.v_new, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"],
                                 w.scale, L.out, stream)
+                    if ev is not None:
+                        ev[3 * li + 1].record(stream)
+                        ev[3 * li + 2].record(stream)
                     continue
-                # timed halves: the quantizing append, then the decode kernel (and combine)
+                # timed halves: the quantizing append, then the decode kernel and the combine
                 pkv.kv_append_q8(L.k_new, L.v_new, L.k_pages, L.v_pages, L.meta, S["bt"], S["positions"], stream)
                 ev[3 * li].record(stream)
-                if one_kernel:
-                    dec.attn_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out, stream)
-                    ev[3 * li + 1].record(stream)
-                else:
-                    dec.split_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out,
-                                 stream)
-                    ev[3 * li + 1].record(stream)
-                    dec.combine(S["seq_lens"], L.out, S["mb"], stream)
+                dec.split_q8(L.q, L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], w.scale, L.out, stream)
+                ev[3 * li + 1].record(stream)
+                dec.combine(S["seq_lens"], L.out, S["mb"], stream)
                 ev[3 * li + 2].record(stream)
                 continue
             if args.unfused:
@@ -489,7 +504,7 @@ def main():
     # otherwise the events around each launch isolate it from the other
     # kernels of the step, at the price of the events' own time (~1 %).
     events_avg = float(np.mean(split_ms))
-    single_launch = one_kernel and not u8 and not args.unfused and not graphs
+    single_launch = one_kernel and not args.unfused and not graphs
     split_avg = ms_per_step / n_layers if single_launch else events_avg
     timing = ("timed-region average, one decode launch per layer" if single_launch
               else "events around each decode launch")
@@ -537,7 +552,8 @@ def main():
             "schedule": "one workgroup per 4 query tiles, no split" if wide else
                         {1: "static", 2: "dynamic"}.get(dec.schedule, dec.schedule),
             "pool_copies": len(layers),
-            "append": "quantizing kernel" if u8 else ("separate kernel" if args.unfused else "fused into the decode kernel"),
+            "append": ("separate kernel" if args.unfused else
+                       "quantizing, fused into the decode kernel" if u8 else "fused into the decode kernel"),
             "merge": "combine kernel" if not one_kernel else "inside the decode kernel",
             "kv_cache": "8-bit codes + per-token scale/zero (2D+16 B per token and head)" if u8 else w.dtype,
             "launch": "hip graph replay" if graphs else "eager",

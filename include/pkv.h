@@ -408,8 +408,15 @@ int pkv_paged_decode_split_q8(const void* q, const void* k_codes, const void* v_
                               void* stream, int32_t batch, int32_t max_blocks_per_seq, int32_t num_pages,
                               void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts);
 
-/* Decode step over the 8-bit cache: pkv_kv_append_q8 of k_new / v_new (bf16)
- * at seq_lens - 1, then pkv_paged_decode_attn_q8 (two launches on stream). */
+/* Decode step over the 8-bit cache in one pass: the quantizing append of
+ * k_new / v_new (bf16 [batch][n_kv_heads][head_dim], 16-byte aligned) at
+ * position seq_lens - 1, done inside the decode kernel, then the decode of
+ * pkv_paged_decode_attn_q8.  The wavefront that computes a sequence's last
+ * page quantizes the new token exactly as pkv_kv_append_q8 does (same codes,
+ * scales and zero points, bit for bit), puts it into its registers and stores
+ * it to the pool; so the result and the pool equal pkv_kv_append_q8 at
+ * seq_lens - 1 followed by pkv_paged_decode_attn_q8.  One launch (two when
+ * the combine kernel is needed, as for the dense step). */
 int pkv_decode_step_q8(const void* q, const void* k_new, const void* v_new, void* k_codes, void* v_codes,
                        void* meta, const int32_t* block_table, const int32_t* seq_lens, int32_t n_q_heads,
                        int32_t n_kv_heads, int32_t head_dim, int32_t block_size, float scale, void* out,

@@ -41,6 +41,11 @@
 
 #include "pkv_internal.h"
 
+// Device helpers that take register arrays by reference are always inlined:
+// a call that the inliner leaves out of line passes the arrays through the
+// stack (scratch memory), whose loads wait behind the tile loads in flight.
+#define PKV_INLINE __attribute__((always_inline))
+
 // Pages each wavefront keeps in flight ahead of the one it computes.
 #ifndef PKV_PREFETCH_PAGES
 #define PKV_PREFETCH_PAGES 2
@@ -491,7 +496,7 @@ __device__ inline size_t out_row(const DecodeArgs& a, int b, int h, int g) {
 // when the pair lies in a single chunk, otherwise this chunk's partial, which
 // the last of the pair's chunks to finish then merges (if counters are on).
 template <bool kOutBf16, int D, bool kMulti, class Pending>
-__device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pages, int seg_start, int chunk,
+PKV_INLINE __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pages, int seg_start, int chunk,
                              int C, const f32x4 (&o)[D / 16], float lse, int lane, Pending& pending) {
   using O = Ops<kOutBf16, D>;
   const int c = lane >> 4;
@@ -561,7 +566,7 @@ __device__ void emit_segment(const DecodeArgs& a, int b, int h, int gb, int n_pa
 struct HeldResults {
   int n = 0, cap = 0, base = 0, words = 0;
   template <int D>
-  __device__ void put(const DecodeArgs& a, int b, int h, int n_pages, int seg_start, const f32x4 (&o)[D / 16],
+  PKV_INLINE __device__ void put(const DecodeArgs& a, int b, int h, int n_pages, int seg_start, const f32x4 (&o)[D / 16],
                       float lse, int lane) {
     const int c = lane >> 4, col = lane & 15;
     const int cols = a.cols;
@@ -577,7 +582,7 @@ struct HeldResults {
   }
   // Writes the held results (see emit_segment), in the order they ended.
   template <bool kOutBf16, int D, bool kMulti, class Pending>
-  __device__ void emit_all(const DecodeArgs& a, int gb, int chunk, int C, int lane, Pending& pending) {
+  PKV_INLINE __device__ void emit_all(const DecodeArgs& a, int gb, int chunk, int C, int lane, Pending& pending) {
     const int c = lane >> 4, col = lane & 15;
     const int rc = min(col, a.cols - 1);   // lanes past the group read a valid row and write nothing
     for (int i = 0; i < n; ++i) {
@@ -783,6 +788,15 @@ struct Segment {
     }
   }
 
+  // The fused append on the pair's last page: the new token into the page
+  // registers, and, if `store`, handed to `held` for page pg.
+  template <class Held>
+  __device__ void append_token(PageRegs<kBf16, D>& r, Held& t, char* kpool, char* vpool, size_t page_stride, int pg,
+                               bool store, int slot, int lane, bool now) const {
+    patch(r, lane);
+    if (store) hold(t, kpool, vpool, page_stride, pg, slot, lane, now);
+  }
+
   // Hands the new token (already in knew/vnew) to `held` (slot `slot`), to
   // be written to page pg of the pool (kpool/vpool point at head h of page 0)
   // once the wavefront's tile stream has drained, or at once if `now`.
@@ -811,7 +825,7 @@ struct Segment {
   // Normalises the segment's result in place and writes it (see
   // emit_segment); the segment is closed afterwards.
   // Normalises the result in place and returns its natural-log lse.
-  __device__ float normalise(bool bad) {
+  PKV_INLINE __device__ float normalise(bool bad) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = bad ? NAN : (!kMulti || lt > 0.f ? 1.0f / lt : 0.f);   // no key seen: zero row, lse -inf
@@ -820,7 +834,7 @@ struct Segment {
     return bad ? NAN : (m + __log2f(lt)) * kLn2;
   }
   template <class Pending>
-  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
+  PKV_INLINE __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
                          Pending& pending) {
     const float lse = normalise(bad);
     emit_segment<kBf16, D, kMulti>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
@@ -888,7 +902,7 @@ __device__ inline int arrive(const DecodeArgs& a, const PendingMerges& pm, int g
 // same bits.  32 f32x4 registers of loads per group by default; fewer where
 // the caller holds other live registers.
 template <bool kBf16, int D, bool kMulti, int kGroupParts, class Load>
-__device__ void merge_core(const DecodeArgs& a, int b, int h, int gb, int nparts, int lane, Load load) {
+PKV_INLINE __device__ void merge_core(const DecodeArgs& a, int b, int h, int gb, int nparts, int lane, Load load) {
   using O = Ops<kBf16, D>;
   const uint32_t c = lane >> 4, n = lane & 15;
   const int g = gb * 16 + static_cast<int>(n);   // column
@@ -1032,22 +1046,57 @@ struct PageRegsQ8 {
   f32x4 ks, kz, vs, vz;               // tokens 4c .. 4c+3
 };
 
+// The 8-bit quantizer of one vector of D features, decided in float32 with
+// IEEE division and round-half-to-even: lo = min(min x, 0), hi = max(max x,
+// 0), s = (hi - lo) / 255 (1 when hi == lo), z = rint(-lo / s), u =
+// clamp(rint(x / s) + z, 0, 255).  q8_params takes this lane's features d
+// = lane and lane + 64 (x1 = 0 when D = 64: the range includes 0 anyway)
+// and reduces over the wavefront.  The quantizing append kernel and the
+// decode kernel's fused append both use these, so their codes agree bit for
+// bit.
+__device__ inline float bf16_bits_to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits << 16); }
+__device__ inline void q8_params(float x0, float x1, float& sc, float& z) {
+  float lo = fminf(fminf(x0, x1), 0.f);
+  float hi = fmaxf(fmaxf(x0, x1), 0.f);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  sc = (hi - lo) / 255.0f;
+  if (sc == 0.f) sc = 1.0f;
+  z = __builtin_rintf(-lo / sc);
+}
+__device__ inline uint32_t q8_code(float x, float sc, float z) {
+  return static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(x / sc) + z, 0.f), 255.f));
+}
+
 // One segment of the 8-bit cache (same role and lane layout as Segment).
 template <int D, bool kMulti>
 struct SegmentQ8 {
   static constexpr int NQ = D / 32;   // fp16 query registers, one per 32-feature MFMA
   static constexpr int NV = D / 16;
+  static constexpr int NK = D / 64;   // 16-byte K code loads per lane
   int b, h, gb, g, hq, len, n_pages, fb, q_len, window, hi, lo;
   bool g_ok, append;
   u32x4 qh[NQ];
   float qsum, m, l, corr;
   f32x4 acc[NV];
+  // Fused quantizing append (the segment holding the pair's last page): the
+  // new token's slot, where its scales and zero points go, and its bf16
+  // features 2 lane and 2 lane + 1 of K and of V (zero past D), loaded with
+  // the query rows, whose wait they share.
+  int s_new;
+  char* meta_h;               // meta of page 0, KV head h
+  size_t meta_stride;         // bytes between pages of the meta array
+  uint32_t kn2, vn2;
 
   // Query operand: MFMA 2j + e takes, in lane (c, n), features
   // 16 (4j + c) + 8e .. +7 of head n: the features the K codes of load j
   // bring to lanes of group c.  qsum = sum of the fp16 query features of the
   // lane's head (the same fp16 values the MFMAs multiply).
-  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, int fb_, bool, int gblk, int lane) {
+  __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, int fb_, bool ends_pair, int gblk,
+                        int lane) {
     const int c = lane >> 4, n = lane & 15;
     b = b_;
     h = h_;
@@ -1064,7 +1113,16 @@ struct SegmentQ8 {
     window = kMulti ? a.window : 0;
     hi = len - q_len + qi + 1;
     lo = window > 0 ? max(0, hi - window) : 0;
-    append = false;
+    append = !kMulti && a.k_new != nullptr && ends_pair;
+    s_new = (len - 1) & (kBlock - 1);
+    if (append) {
+      const size_t row = (static_cast<size_t>(b) * a.n_kv + h) * D;
+      const bool in = 2 * lane < D;
+      kn2 = in ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k_new) + row)[lane] : 0u;
+      vn2 = in ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_new) + row)[lane] : 0u;
+      meta_h = const_cast<char*>(static_cast<const char*>(a.meta)) + static_cast<size_t>(h) * 4 * kBlock * 4;
+      meta_stride = static_cast<size_t>(a.n_kv) * 4 * kBlock * 4;
+    }
     const size_t qrow = g_ok ? (static_cast<size_t>(b) * q_len + qi) * a.n_q + hq : 0;
     const char* qb = static_cast<const char*>(a.q) + qrow * D * 2;
     float part = 0.f;
@@ -1092,6 +1150,93 @@ struct SegmentQ8 {
     corr = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // The fused append on the pair's last page: quantizes the new token (k_new
+  // / v_new, bf16) exactly as the quantizing append kernel does and puts it
+  // into the page registers (its K codes in lanes n == s_new, its V codes,
+  // scales and zero points in lanes c == s_new / 4, element s_new % 4); if
+  // `store`, hands it to `held` for page pg (LDS slot `slot`, or written at
+  // once if `now`).  Each lane quantizes its two features of kn2 / vn2; the
+  // codes reach the lanes that hold them in the page layout by lane
+  // permutes.  Runs once per pair, off the page loop's common path.
+  template <class Held>
+  __device__ void append_token(PageRegsQ8<D>& r, Held& t, char* kpool, char* vpool, size_t page_stride, int pg,
+                               bool store, int slot, int lane, bool now) const {
+    const int c = lane >> 4, n = lane & 15;
+    const float k0 = bf16_bits_to_f32(kn2 & 0xffffu), k1 = bf16_bits_to_f32(kn2 >> 16);
+    const float v0 = bf16_bits_to_f32(vn2 & 0xffffu), v1 = bf16_bits_to_f32(vn2 >> 16);
+    float ks, kz, vs, vz;
+    q8_params(k0, k1, ks, kz);
+    q8_params(v0, v1, vs, vz);
+    const uint32_t ck = q8_code(k0, ks, kz) | (q8_code(k1, ks, kz) << 8);   // features 2 lane, 2 lane + 1
+    const uint32_t cv = q8_code(v0, vs, vz) | (q8_code(v1, vs, vz) << 8);
+    // K: lane 2m holds the codes of features 4m .. 4m + 3 in kd; lane (c, n)
+    // needs features 16 (4 j + c) .. +15, m = 4 (4 j + c) + q.
+    const uint32_t kd = ck | (static_cast<uint32_t>(__shfl_down(static_cast<int>(ck), 1)) << 16);
+    u32x4 kq[NK];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int m0 = 8 * (4 * j + c);
+      kq[j] = u32x4{static_cast<uint32_t>(__shfl(static_cast<int>(kd), m0)),
+                    static_cast<uint32_t>(__shfl(static_cast<int>(kd), m0 + 2)),
+                    static_cast<uint32_t>(__shfl(static_cast<int>(kd), m0 + 4)),
+                    static_cast<uint32_t>(__shfl(static_cast<int>(kd), m0 + 6))};
+    }
+    // V: lane (c, n) needs feature 16 nb + n: byte n % 2 of lane 8 nb + n / 2.
+    uint32_t vq[NV];
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb)
+      vq[nb] = (static_cast<uint32_t>(__shfl(static_cast<int>(cv), 8 * nb + (n >> 1))) >> (8 * (n & 1))) & 0xffu;
+    if (n == s_new) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) r.k[j] = kq[j];
+    }
+    const int e = s_new & 3;
+    if (c == (s_new >> 2)) {
+      const uint32_t keep = ~(0xffu << (8 * e));
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb) r.v[nb] = (r.v[nb] & keep) | (vq[nb] << (8 * e));
+      // element e of each meta vector, by selects (a runtime vector index
+      // would put the page registers on the stack)
+      auto put = [e](f32x4 v, float x) {
+        return f32x4{e == 0 ? x : v[0], e == 1 ? x : v[1], e == 2 ? x : v[2], e == 3 ? x : v[3]};
+      };
+      r.ks = put(r.ks, ks);
+      r.kz = put(r.kz, kz);
+      r.vs = put(r.vs, vs);
+      r.vz = put(r.vz, vz);
+    }
+    if (store) {
+      const size_t off = static_cast<size_t>(pg) * page_stride;
+      t.take(kq, vq, f32x4{ks, kz, vs, vz}, kpool + off, vpool + off,
+             meta_h + static_cast<size_t>(pg) * meta_stride, s_new, slot, lane, now);
+    }
+  }
+
+  // Writes a token's codes, scales and zero points into slot s_new of one
+  // (page, KV head) tile: kbase / vbase / mbase are that tile's K codes, V
+  // codes and meta.  K: lanes n == s_new, 16 bytes per load; V: one byte per
+  // feature from lanes c == s_new / 4; meta: lanes 0-3.
+  __device__ static void store_codes(const u32x4 (&kq)[NK], const uint32_t (&vq)[NV], f32x4 meta, char* kbase,
+                                     char* vbase, char* mbase, int s_new, int lane) {
+    const int c = lane >> 4, n = lane & 15;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(kbase, 0, kBlock * D, PKV_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(vbase, 0, kBlock * D, PKV_RSRC_WORD3);
+    if (n == s_new) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) __builtin_amdgcn_raw_buffer_store_b128(kq[j], kr, 1024 * j + 16 * lane, 0, 0);
+    }
+    if (c == (s_new >> 2)) {
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb)
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(vq[nb]), vr, 16 * (16 * nb + n) + s_new, 0, 0);
+    }
+    if (lane < 4) {
+      const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(mbase, 0, 4 * kBlock * 4, PKV_RSRC_WORD3);
+      const float v = lane == 0 ? meta[0] : lane == 1 ? meta[1] : lane == 2 ? meta[2] : meta[3];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), mr, 64 * lane + 4 * s_new, 0, 0);
+    }
   }
 
   __device__ void page(PageRegsQ8<D>& r, int j, float scale_log2, int lane) {
@@ -1153,7 +1298,7 @@ struct SegmentQ8 {
     }
   }
 
-  __device__ float normalise(bool bad) {
+  PKV_INLINE __device__ float normalise(bool bad) {
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     float ct = corr + __shfl_xor(corr, 16);
@@ -1164,12 +1309,87 @@ struct SegmentQ8 {
     return bad ? NAN : (m + __log2f(lt)) * kLn2;
   }
   template <class Pending>
-  __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
+  PKV_INLINE __device__ void finish(const DecodeArgs& a, int seg_start, int chunk, int C, bool bad, int lane,
                          Pending& pending) {
     const float lse = normalise(bad);
     emit_segment<true, D, kMulti>(a, b, h, gb, n_pages, seg_start, chunk, C, acc, lse, lane, pending);
   }
 };
+
+// New tokens of the fused append on the 8-bit cache, held back like
+// HeldToken's: a slot holds the token's D K codes and D V codes in feature
+// order, its scales and zero points, and the K code, V code and meta
+// addresses of its tile and its slot in the tile.
+template <int D, bool kDefer = true>
+struct HeldTokenQ8 {
+  using Seg = SegmentQ8<D, false>;
+  static constexpr int kCodeWords = D / 4;
+  static constexpr int kSlotWords = 2 * kCodeWords + 4 + 8;   // K, V, meta, destination
+  static_assert(kSlotWords <= kHeldWords, "a held token fits its LDS slot");
+  uint32_t* lds;
+  uint32_t mask = 0;
+
+  __device__ void store_slot(int i, int lane) {
+    mask &= ~(1u << i);
+    const int c = lane >> 4, n = lane & 15;
+    const uint32_t* w = lds + i * kSlotWords;
+    u32x4 kq[Seg::NK];
+    uint32_t vq[Seg::NV];
+#pragma unroll
+    for (int j = 0; j < Seg::NK; ++j) kq[j] = reinterpret_cast<const u32x4*>(w)[4 * j + c];
+    const uint8_t* vb = reinterpret_cast<const uint8_t*>(w + kCodeWords);
+#pragma unroll
+    for (int nb = 0; nb < Seg::NV; ++nb) vq[nb] = vb[16 * nb + n];
+    const f32x4 meta = *reinterpret_cast<const f32x4*>(w + 2 * kCodeWords);
+    const uint32_t* d = w + 2 * kCodeWords + 4;
+    auto u = [](uint32_t x) { return static_cast<uint64_t>(static_cast<uint32_t>(uni(static_cast<int>(x)))); };
+    char* kb = reinterpret_cast<char*>((u(d[1]) << 32) | u(d[0]));
+    char* vb2 = reinterpret_cast<char*>((u(d[3]) << 32) | u(d[2]));
+    char* mb = reinterpret_cast<char*>((u(d[5]) << 32) | u(d[4]));
+    Seg::store_codes(kq, vq, meta, kb, vb2, mb, uni(static_cast<int>(d[6])), lane);
+  }
+
+  // kq / vq in the lane layout of SegmentQ8::append_token.
+  __device__ void take(const u32x4 (&kq)[Seg::NK], const uint32_t (&vq)[Seg::NV], f32x4 meta, char* kbase,
+                       char* vbase, char* mbase, int s_new, int slot, int lane, bool now) {
+    if (!kDefer || now) {
+      Seg::store_codes(kq, vq, meta, kbase, vbase, mbase, s_new, lane);
+      return;
+    }
+    if ((mask >> slot) & 1u) store_slot(slot, lane);
+    mask |= 1u << slot;
+    const int c = lane >> 4, n = lane & 15;
+    uint32_t* w = lds + slot * kSlotWords;
+    if (n == 0) {
+#pragma unroll
+      for (int j = 0; j < Seg::NK; ++j) reinterpret_cast<u32x4*>(w)[4 * j + c] = kq[j];
+    }
+    if (c == 0) {
+      uint8_t* vb = reinterpret_cast<uint8_t*>(w + kCodeWords);
+#pragma unroll
+      for (int nb = 0; nb < Seg::NV; ++nb) vb[16 * nb + n] = static_cast<uint8_t>(vq[nb]);
+    }
+    if (lane == 0) {
+      *reinterpret_cast<f32x4*>(w + 2 * kCodeWords) = meta;
+      const uint64_t kb = reinterpret_cast<uint64_t>(kbase), vb = reinterpret_cast<uint64_t>(vbase),
+                     mb = reinterpret_cast<uint64_t>(mbase);
+      uint32_t* d = w + 2 * kCodeWords + 4;
+      *reinterpret_cast<u32x4*>(d) = u32x4{static_cast<uint32_t>(kb), static_cast<uint32_t>(kb >> 32),
+                                           static_cast<uint32_t>(vb), static_cast<uint32_t>(vb >> 32)};
+      d[4] = static_cast<uint32_t>(mb);
+      d[5] = static_cast<uint32_t>(mb >> 32);
+      d[6] = static_cast<uint32_t>(s_new);
+    }
+  }
+
+  __device__ void store(int lane) {
+    if constexpr (kDefer) {
+      while (mask != 0) store_slot(__builtin_ctz(mask), lane);
+    }
+  }
+};
+static_assert(HeldTokenQ8<128>::kSlotWords == 128 / 2 + 12 && HeldTokenQ8<64>::kSlotWords == 64 / 2 + 12,
+              "the host sizes 8-bit token slots as head_dim / 2 + 12 words");
 
 // Position in the flattened (sequence, KV head, page) order of all pages:
 // flat index f, sequence b (with pb = pages before b and n = pages of b),
@@ -1251,7 +1471,7 @@ template <int D>
 struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
   static constexpr int kHeadDim = D;
   static constexpr bool kOutBf16 = true;
-  static constexpr bool kFusedAppend = false;
+  static constexpr bool kFusedAppend = true;    // quantized in the decode kernel
   static constexpr bool kMulti = false;
   static constexpr int kTileK = kBlock * D;        // bytes of one K (or V) code tile
   static constexpr int kMetaBytes = 4 * kBlock * 4;
@@ -1259,11 +1479,8 @@ struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
   static constexpr int kWavesPerEuGrouped = PKV_GROUPED_WAVES_PER_EU;
   using Regs = PageRegsQ8<D>;
   using Seg = SegmentQ8<D, false>;   // one query token, no window
-  template <bool>
-  struct Held {                      // no fused append on the 8-bit cache
-    uint32_t* lds;
-    __device__ void store(int) {}
-  };
+  template <bool kDefer>
+  using Held = HeldTokenQ8<D, kDefer>;
   template <int kAux>
   __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -1426,14 +1643,11 @@ split_kernel(DecodeArgs a) {
     // otherwise slot 0, whose previous token is pushed out.
     if constexpr (KV::kFusedAppend) {
       if (seg[0].append && cp.j == cp.n - 1) {
-        seg[0].patch(r, lane);
-        if (ok && gblk == 0) {
-          const bool by_result = kHoldResults && results.cap > 0;
-          const int slot = by_result ? results.n : 0;
-          const bool now = p == cnt - 1 || (by_result ? results.n >= results.cap : a.held_cap == 0);
-          seg[0].hold(held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
-                      page_stride, pg, slot, lane, now);
-        }
+        const bool by_result = kHoldResults && results.cap > 0;
+        const int slot = by_result ? results.n : 0;
+        const bool now = p == cnt - 1 || (by_result ? results.n >= results.cap : a.held_cap == 0);
+        seg[0].append_token(r, held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
+                            page_stride, pg, ok && gblk == 0, slot, lane, now);
       }
     }
 #pragma unroll
@@ -2200,13 +2414,9 @@ dyn_kernel(DecodeArgs a) {
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     bad |= !ok;
     if constexpr (KV::kFusedAppend) {
-      if (seg.append && cp.j == cp.n - 1) {
-        seg.patch(r, lane);
-        if (ok) {
-          seg.hold(held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
-                   page_stride, pg, 0, lane, false);
-        }
-      }
+      if (seg.append && cp.j == cp.n - 1)
+        seg.append_token(r, held, kp0 + static_cast<size_t>(cp.h) * kTile, vp0 + static_cast<size_t>(cp.h) * kTile,
+                         page_stride, pg, ok, 0, lane, false);
     }
     seg.page(r, cp.j, a.scale_log2, lane);
     if (++cpos < ccnt) cp.next(a, s_prefix);
@@ -2456,22 +2666,11 @@ append_q8_kernel(const void* k_new, const void* v_new, uint8_t* k_codes, uint8_t
     const void* src = which == 0 ? k_new : v_new;
     const float x0 = read(src, lane);
     const float x1 = two ? read(src, lane + kWave) : 0.f;
-    float lo = fminf(fminf(x0, x1), 0.f);
-    float hi = fmaxf(fmaxf(x0, x1), 0.f);
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      lo = fminf(lo, __shfl_xor(lo, off));
-      hi = fmaxf(hi, __shfl_xor(hi, off));
-    }
-    float sc = (hi - lo) / 255.0f;
-    if (sc == 0.f) sc = 1.0f;
-    const float z = __builtin_rintf(-lo / sc);
-    auto code = [&](float x) {
-      return static_cast<uint8_t>(fminf(fmaxf(__builtin_rintf(x / sc) + z, 0.f), 255.f));
-    };
+    float sc, z;
+    q8_params(x0, x1, sc, z);
     for (int e = 0; e < (two ? 2 : 1); ++e) {
       const int d = lane + e * kWave;
-      const uint8_t u = code(e == 0 ? x0 : x1);
+      const uint8_t u = static_cast<uint8_t>(q8_code(e == 0 ? x0 : x1, sc, z));
       if (which == 0)
         k_codes[tile * kBlock * D + static_cast<size_t>(d / 16) * 256 + slot * 16 + d % 16] = u;
       else
@@ -2954,8 +3153,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   if (do_split && q8 != (meta != nullptr))
     return fail(PKV_ERR_INVALID_ARG, f + (q8 ? ": the 8-bit cache needs its meta array (16-byte aligned)"
                                              : ": this entry point takes the 8-bit cache only with dtype PKV_U8"));
-  if (do_split && q8 && (!aligned(meta, 16) || k_new != nullptr))
-    return fail(PKV_ERR_INVALID_ARG, f + ": meta must be 16-byte aligned; no fused append on the 8-bit cache");
+  if (do_split && q8 && !aligned(meta, 16)) return fail(PKV_ERR_INVALID_ARG, f + ": meta must be 16-byte aligned");
   if ((k_new != nullptr) != (v_new != nullptr) ||
       (k_new && (!aligned(k_new, 16) || !aligned(v_new, 4))))
     return fail(PKV_ERR_INVALID_ARG, f + ": k_new/v_new must both be given, 16/4-byte aligned");
@@ -3041,7 +3239,8 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
       if (r.lds + wg * sizeof(float) <= kMaxLdsBytes) wg_words = wg;
     }
     const int es = dtype == PKV_F32 ? 4 : 2;
-    const int tok = k_new != nullptr && !q8 ? head_dim * es / 4 + head_dim + 8 : 0;   // HeldToken::kSlotWords
+    // HeldToken::kSlotWords, HeldTokenQ8::kSlotWords
+    const int tok = k_new == nullptr ? 0 : q8 ? head_dim / 2 + 12 : head_dim * es / 4 + head_dim + 8;
     int res = one_block ? ((cols * (head_dim + 1) + 3) & ~3) + 4 : 0;
     const size_t avail = kMaxLdsBytes / sizeof(int32_t) - held_offset(batch) - wg_words;
     int cap = res > 0 ? static_cast<int>(std::min<size_t>(kMaxHeldSlots, avail / (kWavesPerGroup * (tok + res))))
@@ -3297,13 +3496,7 @@ int pkv_decode_step_q8(const void* q, const void* k_new, const void* v_new, void
                        void* workspace, size_t workspace_bytes, const pkv_decode_opts* opts) {
   if (batch > 0 && (!k_new || !v_new))
     return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_q8: k_new and v_new are required");
-  if (batch > 0 && !seq_lens)
-    return fail(PKV_ERR_INVALID_ARG, "pkv_decode_step_q8: seq_lens is required");
-  const int st = pkv::append_q8_common("pkv_decode_step_q8", k_new, v_new, k_codes, v_codes, meta, block_table,
-                                       seq_lens, true, batch, n_kv_heads, head_dim, block_size,
-                                       max_blocks_per_seq, num_pages, PKV_BF16, stream);
-  if (st != PKV_OK) return st;
-  return pkv::decode_common(true, true, "pkv_decode_step_q8", q, nullptr, nullptr, k_codes, v_codes, meta,
+  return pkv::decode_common(true, true, "pkv_decode_step_q8", q, k_new, v_new, k_codes, v_codes, meta,
                             block_table, seq_lens, n_q_heads, n_kv_heads, head_dim, block_size, scale, out,
                             stream, batch, max_blocks_per_seq, num_pages, PKV_U8, workspace, workspace_bytes,
                             opts);
