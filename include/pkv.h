@@ -346,12 +346,17 @@ int pkv_decode_plan(const int32_t* seq_lens, int32_t batch, int32_t n_kv_heads,
  * hi = seq_lens[b] - q_len + i + 1 and lo = window > 0 ? max(0, hi - window)
  * : 0.  Their K/V must already be appended (pkv_kv_append per token).
  * q, out: [batch][q_len][n_q_heads][head_dim], dtype as pkv_paged_decode_attn.
- * Requires q_len >= 1, window >= 0, q_len * (n_q_heads / n_kv_heads) <= 64;
- * a length of 0 gives zero rows, a length below q_len NaN rows.  Pages wholly
- * before every query's window are not read.  The workspace and options are
- * those of pkv_paged_decode_attn for n_q_heads * q_len query heads (size it
- * with pkv_decode_resolve / pkv_decode_workspace_bytes given n_q_heads *
- * q_len).  q_len = 1, window = 0 is pkv_paged_decode_attn.
+ * Requires q_len >= 1, window >= 0; a length of 0 gives zero rows, a length
+ * below q_len NaN rows.  Pages wholly before every query's window are not
+ * read.  Up to 64 query columns per KV head (q_len * n_q_heads / n_kv_heads)
+ * the keys are split as in pkv_paged_decode_attn: the workspace and options
+ * are its own for n_q_heads * q_len query heads (size it with
+ * pkv_decode_resolve / pkv_decode_workspace_bytes given n_q_heads * q_len).
+ * Above 64 columns (a prefill chunk, a long drafted run) every 16-column
+ * query tile runs over its whole key range in one wavefront, with no
+ * partials: workspace, workspace_bytes and opts are then not used (may be
+ * NULL / 0), and dtype bf16 and fp32 are both taken.  q_len = 1, window = 0
+ * is pkv_paged_decode_attn.
  * ------------------------------------------------------------------------ */
 int pkv_paged_decode_multi(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                            const int32_t* seq_lens, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
