@@ -521,8 +521,8 @@ PKV_INLINE __device__ void emit_segment(const DecodeArgs& a, int b, int h, int g
     if (static_cast<int>(n) < cols) {
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb)
-        *reinterpret_cast<f32x4*>(lds_f32 + base + slot * cols * D + n * D + 16 * nb + 4 * c) = o[nb];
-      if (c == 0) lds_f32[base + 2 * kWavesPerGroup * cols * D + slot * cols + n] = lse;
+        *reinterpret_cast<f32x4*>(lds_f32 + base + (slot * cols + n) * lds_row(D) + 16 * nb + 4 * c) = o[nb];
+      if (c == 0) lds_f32[base + 2 * kWavesPerGroup * cols * lds_row(D) + slot * cols + n] = lse;
     }
     if (which == 1) {
       pending.nw = 1;
@@ -574,8 +574,8 @@ struct HeldResults {
     if (col < cols) {
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb)
-        *reinterpret_cast<f32x4*>(lds_f32 + sb + col * D + 16 * nb + 4 * c) = o[nb];
-      if (c == 0) lds_f32[sb + cols * D + col] = lse;
+        *reinterpret_cast<f32x4*>(lds_f32 + sb + col * lds_row(D) + 16 * nb + 4 * c) = o[nb];
+      if (c == 0) lds_f32[sb + cols * lds_row(D) + col] = lse;
     }
     if (lane == 0) *reinterpret_cast<int4*>(lds_f32 + sb + words - 4) = make_int4(b, h, n_pages, seg_start);
     ++n;
@@ -590,8 +590,9 @@ struct HeldResults {
       const int4 d = *reinterpret_cast<const int4*>(lds_f32 + sb + words - 4);
       f32x4 o[D / 16];
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) o[nb] = *reinterpret_cast<const f32x4*>(lds_f32 + sb + rc * D + 16 * nb + 4 * c);
-      const float lse = lds_f32[sb + a.cols * D + rc];
+      for (int nb = 0; nb < D / 16; ++nb)
+        o[nb] = *reinterpret_cast<const f32x4*>(lds_f32 + sb + rc * lds_row(D) + 16 * nb + 4 * c);
+      const float lse = lds_f32[sb + a.cols * lds_row(D) + rc];
       emit_segment<kOutBf16, D, kMulti>(a, uni(d.x), uni(d.y), gb, uni(d.z), uni(d.w), chunk, C, o, lse, lane,
                                         pending);
     }
@@ -980,10 +981,10 @@ __device__ void merge_workgroup(const DecodeArgs& a, const PendingMerges& p, int
   merge_core<kBf16, D, kMulti, 0>(a, p.wb, p.wh, 0, nparts, lane, [&](int i, float& l, f32x4 (&v)[O::NV]) {
     if (i < nparts && n < cols) {
       const int slot = (p.wfirst + i - p.wg_first) * 2 + (i == 0 ? 1 : 0);
-      const float* so = lds_f32 + p.wg_base + slot * cols * D;
-      l = lds_f32[p.wg_base + 2 * kWavesPerGroup * cols * D + slot * cols + n];
+      const float* so = lds_f32 + p.wg_base + (slot * cols + n) * lds_row(D);
+      l = lds_f32[p.wg_base + 2 * kWavesPerGroup * cols * lds_row(D) + slot * cols + n];
 #pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) v[nb] = *reinterpret_cast<const f32x4*>(so + n * D + 16 * nb + 4 * c);
+      for (int nb = 0; nb < O::NV; ++nb) v[nb] = *reinterpret_cast<const f32x4*>(so + 16 * nb + 4 * c);
     } else {
       l = 0.f;
 #pragma unroll
@@ -1985,7 +1986,8 @@ wide_kernel(DecodeArgs a) {
   constexpr int kNB = 4;
   constexpr int kTile = kBlock * D * O::ES;
   constexpr int kBufs = kDepth + 1;
-  constexpr int kSlotWords = 16 * (D + 2);   // one wavefront's block: rows [16][D], maxima [16], sums [16]
+  constexpr int kRow = lds_row(D);
+  constexpr int kSlotWords = 16 * kRow + 32;   // one block of one wavefront: rows [16][kRow], maxima [16], sums [16]
   extern __shared__ int32_t smem[];
   int32_t* s_prefix = smem;
   build_prefix(a.seq_lens, a.batch, a.max_blocks, a.q_len, a.window, s_prefix, smem + a.batch + 1);
@@ -2121,43 +2123,43 @@ wide_kernel(DecodeArgs a) {
         page_at(r, pg, f, true);
       }
     }
-    f32x4 res[O::NV];
-    float rm = kNoKeysMax, rl = 0.f;
+    // Every wavefront leaves its four blocks in LDS, then wavefront j merges
+    // block j of the four: one barrier to publish, one before the slots are
+    // written again.
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
       float lt = t.l[j] + __shfl_xor(t.l[j], 16);
       lt += __shfl_xor(lt, 32);
-      float* slot = mlds + wave * kSlotWords;
+      float* slot = mlds + (wave * kNB + j) * kSlotWords;
 #pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) *reinterpret_cast<f32x4*>(slot + n * D + 16 * nb + 4 * c) = t.acc[j][nb];
+      for (int nb = 0; nb < O::NV; ++nb) *reinterpret_cast<f32x4*>(slot + n * kRow + 16 * nb + 4 * c) = t.acc[j][nb];
       if (c == 0) {
-        slot[16 * D + n] = t.m[j];
-        slot[16 * D + 16 + n] = bad ? NAN : lt;
+        slot[16 * kRow + n] = t.m[j];
+        slot[16 * kRow + 16 + n] = bad ? NAN : lt;
       }
-      __syncthreads();
-      if (wave == j) {
-        float mw[kWavesPerGroup];
-        float mx = kNoKeysMax;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w) {
-          mw[w] = mlds[w * kSlotWords + 16 * D + n];
-          mx = fmaxf(mx, mw[w]);
-        }
-#pragma unroll
-        for (int nb = 0; nb < O::NV; ++nb) res[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        rl = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerGroup; ++w) {
-          const float e = __builtin_amdgcn_exp2f(mw[w] - mx);
-          rl += e * mlds[w * kSlotWords + 16 * D + 16 + n];
-#pragma unroll
-          for (int nb = 0; nb < O::NV; ++nb)
-            res[nb] += e * *reinterpret_cast<const f32x4*>(mlds + w * kSlotWords + n * D + 16 * nb + 4 * c);
-        }
-        rm = mx;
-      }
-      __syncthreads();
     }
+    __syncthreads();
+    f32x4 res[O::NV];
+    float mw[kWavesPerGroup];
+    float mx = kNoKeysMax;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+      mw[w] = mlds[(w * kNB + wave) * kSlotWords + 16 * kRow + n];
+      mx = fmaxf(mx, mw[w]);
+    }
+#pragma unroll
+    for (int nb = 0; nb < O::NV; ++nb) res[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float rl = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+      const float* slot = mlds + (w * kNB + wave) * kSlotWords;
+      const float e = __builtin_amdgcn_exp2f(mw[w] - mx);
+      rl += e * slot[16 * kRow + 16 + n];
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) res[nb] += e * *reinterpret_cast<const f32x4*>(slot + n * kRow + 16 * nb + 4 * c);
+    }
+    const float rm = mx;
+    __syncthreads();
     // Block `wave` of the segment's result (nothing for blocks past the group).
     if (16 * wave < a.cols) {
       const bool nan_row = rl != rl;
@@ -2891,7 +2893,7 @@ SplitFn dyn_fn(int dtype, int head_dim, bool q8) {
 inline bool uses_wide(int dtype, int cols, bool q8) { return !q8 && dtype == PKV_BF16 && cols > 32; }
 // Its LDS: the page prefix, then four wavefronts' merge slots of 16 columns.
 size_t wide_lds_bytes(int batch, int head_dim) {
-  return (static_cast<size_t>(held_offset(batch)) + kWavesPerGroup * 16 * (head_dim + 2)) * sizeof(int32_t);
+  return (static_cast<size_t>(held_offset(batch)) + kWavesPerGroup * 4 * (16 * lds_row(head_dim) + 32)) * sizeof(int32_t);
 }
 
 SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
@@ -3162,7 +3164,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   Resolved r;
   st = resolve_opts(dtype, head_dim, cols, batch, max_blocks_per_seq, n_kv_heads, opts, &r);
   if (st != PKV_OK) return st;
-  if (do_split && r.lds > kMaxLdsBytes)
+  if (do_split && r.lds > (uses_wide(dtype, cols, q8) ? kMaxLdsBytesWide : kMaxLdsBytes))
     return fail(PKV_ERR_UNSUPPORTED, f + ": batch too large for this group size (LDS " +
                                          std::to_string(r.lds) + " bytes)");
   const int64_t need = pkv_decode_workspace_bytes(batch, n_q_heads * q_len, n_kv_heads, head_dim, r.n_items);
@@ -3235,13 +3237,13 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
     const bool one_block = cols <= 16;
     size_t wg_words = 0;
     if (fuse && one_block) {
-      const size_t wg = static_cast<size_t>(kWavesPerGroup) * 2 * cols * (head_dim + 1);
+      const size_t wg = static_cast<size_t>(kWavesPerGroup) * 2 * cols * (lds_row(head_dim) + 1);
       if (r.lds + wg * sizeof(float) <= kMaxLdsBytes) wg_words = wg;
     }
     const int es = dtype == PKV_F32 ? 4 : 2;
     // HeldToken::kSlotWords, HeldTokenQ8::kSlotWords
     const int tok = k_new == nullptr ? 0 : q8 ? head_dim / 2 + 12 : head_dim * es / 4 + head_dim + 8;
-    int res = one_block ? ((cols * (head_dim + 1) + 3) & ~3) + 4 : 0;
+    int res = one_block ? ((cols * (lds_row(head_dim) + 1) + 3) & ~3) + 4 : 0;
     const size_t avail = kMaxLdsBytes / sizeof(int32_t) - held_offset(batch) - wg_words;
     int cap = res > 0 ? static_cast<int>(std::min<size_t>(kMaxHeldSlots, avail / (kWavesPerGroup * (tok + res))))
                       : 0;

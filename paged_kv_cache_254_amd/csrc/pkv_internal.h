@@ -33,6 +33,9 @@ __host__ __device__ inline int default_min_chunk(int group, bool q8 = false) {
 }
 constexpr int kMaxItems = 1 << 22;  // work items per decode launch
 constexpr size_t kMaxLdsBytes = 64 * 1024;  // LDS one decode workgroup may use
+// The wide kernel runs one workgroup per CU and may take the whole LDS of a
+// gfx950 CU for its merge slots.
+constexpr size_t kMaxLdsBytesWide = 160 * 1024;
 
 __host__ __device__ inline int pages_of_len(int64_t len, int64_t max_blocks) {
   if (len <= 0 || len > max_blocks * kBlock) return 0;
@@ -118,6 +121,13 @@ constexpr int kMaxPending = 64;
 // wavefront per chunk) its held results, then (dynamic kernel) each
 // wavefront's list of pending pairs (kMaxPending int4 entries).
 constexpr int kHeldWords = 128 * 4 / 4 + 128 + 8;
+// Row stride (floats) of a block of output rows [rows][head_dim] held in
+// LDS.  A 16-byte LDS access by lanes (c, n) touches row n at feature 4c
+// (+16 nb); with an unpadded stride of 128 or 64 floats every row starts in
+// the same bank and the 16 rows of one access serialise.  Four floats of
+// padding move row n by 4n banks, so the 16 rows of an access fall in
+// disjoint banks.
+__host__ __device__ constexpr int lds_row(int head_dim) { return head_dim + 4; }
 // Result and token slots per wavefront of the split kernel, at most.
 constexpr int kMaxHeldSlots = 8;
 __host__ __device__ inline int held_offset(int batch) { return (batch + 1 + kWavesPerGroup + 3) & ~3; }
