@@ -569,7 +569,9 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
         }) | {
-            "kernel": "prefill_kernel" if wide else "split_kernel", "avg_launch_ms": round(split_avg, 5),
+            "kernel": ("prefill_kernel" if wide else
+                       "wide_kernel" if not u8 and w.dtype == "bf16" and 32 < T * w.group <= 64 else "split_kernel"),
+            "avg_launch_ms": round(split_avg, 5),
             "timing": timing, "avg_launch_ms_events": round(events_avg, 5),
             "algorithmic_bytes_per_launch": S["kv_bytes_layer"], "algorithmic_flops_per_launch": int(flops_layer),
             "flop_per_byte": round(intensity, 2), "kv_gbs": round(achieved, 2), "tflops": round(tflops, 3),

@@ -1050,11 +1050,12 @@ struct PageRegsQ8 {
 // The 8-bit quantizer of one vector of D features, decided in float32 with
 // IEEE division and round-half-to-even: lo = min(min x, 0), hi = max(max x,
 // 0), s = (hi - lo) / 255 (1 when hi == lo), z = rint(-lo / s), u =
-// clamp(rint(x / s) + z, 0, 255).  q8_params takes this lane's features d
-// = lane and lane + 64 (x1 = 0 when D = 64: the range includes 0 anyway)
-// and reduces over the wavefront.  The quantizing append kernel and the
-// decode kernel's fused append both use these, so their codes agree bit for
-// bit.
+// clamp(rint(x / s) + z, 0, 255).  q8_params takes the two features this
+// lane holds (zeros where it holds none: the range includes 0 anyway) and
+// reduces over the wavefront; a minimum and a maximum do not depend on which
+// lane holds which feature.  The quantizing append kernel (features lane and
+// lane + 64) and the decode kernel's fused append (features 2 lane and
+// 2 lane + 1) both use these, so their codes agree bit for bit.
 __device__ inline float bf16_bits_to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits << 16); }
 __device__ inline void q8_params(float x0, float x1, float& sc, float& z) {
   float lo = fminf(fminf(x0, x1), 0.f);
@@ -1966,9 +1967,10 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
 // its four wavefronts take the chunk's pages in turn (wavefront w the pages
 // w, w + 4, ...), so they stream four neighbouring pages of the same pair
 // at a time.  The four walk the chunk's segments (the runs of pages of one
-// (sequence, KV head) pair) together; at the end of each segment they
-// merge their four partial softmax states through LDS, one 16-column block
-// per round, and wavefront j writes block j of the segment's result: the
+// (sequence, KV head) pair) together; at the end of each segment each
+// leaves its four 16-column blocks of partial softmax state in LDS, and
+// after one barrier wavefront j merges block j of the four and writes block
+// j of the segment's result: the
 // output rows when the pair lies in this chunk, else the chunk's partial,
 // merged with the pair's other chunks by the last to arrive (the same
 // slots, counters and merge as the other split kernels, per block j).
