@@ -197,11 +197,20 @@ def test_full_size_sampled_q8(pkv, name):
                    meta.index_select(0, pages).cpu().numpy())
     bt = torch.from_numpy(bt_np).cuda()
     lens = torch.from_numpy(att.astype(np.int32)).cuda()
+    kc0, vc0, meta0 = kc.clone(), vc.clone(), meta.clone()
     dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.uint8, mb)
     out = torch.full_like(q, float("nan"))
     H.log(f"q8 full {name}: step (n_items={dec.n_items})")
     dec.step_q8(q, k_new, v_new, kc, vc, meta, bt, lens, w.scale, out)
     torch.cuda.synchronize()
+    # The whole pools: the fused append wrote every sequence's token exactly
+    # as the standalone quantizing append (bit-exact against the oracle above)
+    # does, and nothing else.
+    pos = torch.from_numpy(cached.astype(np.int32)).cuda()
+    pkv.kv_append_q8(k_new, v_new, kc0, vc0, meta0, bt, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc0) and torch.equal(vc, vc0)
+    assert torch.equal(meta.view(torch.int32), meta0.view(torch.int32))
     for b in bs:
         pages, kp, vp, mp = host[b]
         sub = np.arange(len(pages), dtype=np.int32)[None, :]
@@ -213,3 +222,47 @@ def test_full_size_sampled_q8(pkv, name):
         H.log(f"  b={b} ({int(att[b])} tokens): max abs {mx:.2e} rel RMS {rel:.2e}")
         assert same_bits(kc.index_select(0, pages), k2) and same_bits(vc.index_select(0, pages), v2)
         assert same_bits(meta.index_select(0, pages), m2)
+
+
+def _q8_step(pkv, w, c, n_items, mc, schedule=0):
+    d = to_dev(c)
+    dec = pkv.Decoder(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, torch.uint8, c.mb, n_items, mc,
+                      schedule=schedule)
+    out = torch.full_like(d.q, float("nan"))
+    dec.step_q8(d.q, d.k_new, d.v_new, d.kc, d.vc, d.meta, d.bt, d.lens, w.scale, out)
+    torch.cuda.synchronize()
+    return dec, d, out
+
+
+def test_step_q8_dynamic_equals_static(pkv):
+    """The fused 8-bit step under the dynamic schedule (one held token slot
+    per wavefront, a second token pushes the first out) against the oracle,
+    bit-identical to the static schedule on the same chunks, and both pools
+    bit-exact."""
+    w = W.custom("q8dyn", 6, 16, 4, 128, "bf16", [0, 15, 16, 300, 999, 47], seed=95)
+    c = setup_q8(w)
+    ref, kc, vc, mt = oracle_step(c)
+    dyn, d1, o1 = _q8_step(pkv, w, c, 40, 2, pkv.PKV_SCHEDULE_DYNAMIC)
+    assert dyn.schedule == pkv.PKV_SCHEDULE_DYNAMIC
+    _, d2, o2 = _q8_step(pkv, w, c, dyn.n_items, dyn.min_chunk_pages, pkv.PKV_SCHEDULE_STATIC)
+    H.assert_close(H.f64(o1), ref, "bf16", "q8 dynamic step")
+    assert torch.equal(o1, o2)
+    for d in (d1, d2):
+        assert same_bits(d.kc, kc) and same_bits(d.vc, vc) and same_bits(d.meta, mt)
+    arrivals, work = dyn.counters()
+    assert int(work.item()) == 0 and int(arrivals.abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (64, 1)])
+def test_step_q8_many_pairs_in_one_chunk(pkv, Hq, Hkv):
+    """Forty short sequences in one chunk: far more pairs end inside the chunk
+    than a wavefront has LDS slots, so later tokens and results are written
+    at once; with 64 query heads per KV head the four head-block wavefronts
+    share each page and the first stores the token."""
+    lens = [(7 * i) % 45 + 1 for i in range(40)]
+    w = W.custom(f"q8many{Hq}", 40, Hq, Hkv, 128, "bf16", lens, seed=96 + Hq)
+    c = setup_q8(w)
+    ref, kc, vc, mt = oracle_step(c)
+    _, d, out = _q8_step(pkv, w, c, 1, 1)
+    H.assert_close(H.f64(out), ref, "bf16", f"q8 many pairs G={Hq // Hkv}")
+    assert same_bits(d.kc, kc) and same_bits(d.vc, vc) and same_bits(d.meta, mt)
