@@ -570,7 +570,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
         }) | {
             "kernel": ("prefill_kernel" if wide else
-                       "wide_kernel" if not u8 and w.dtype == "bf16" and 32 < T * w.group <= 64 else "split_kernel"),
+                       "wide_kernel" if (u8 or w.dtype == "bf16") and 32 < T * w.group <= 64 else "split_kernel"),
             "avg_launch_ms": round(split_avg, 5),
             "timing": timing, "avg_launch_ms_events": round(events_avg, 5),
             "algorithmic_bytes_per_launch": S["kv_bytes_layer"], "algorithmic_flops_per_launch": int(flops_layer),

@@ -38,6 +38,7 @@
 #include <cstdint>
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "pkv_internal.h"
 
@@ -1073,6 +1074,34 @@ __device__ inline uint32_t q8_code(float x, float sc, float z) {
   return static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(x / sc) + z, 0.f), 255.f));
 }
 
+// Weights of one page's four tokens in a lane, w = p s rounded to fp16
+// (p = 2^(x - m)), added to l, and their correction sum
+// sum_t w_t (1024 + z_t), returned.  On a page that some key range cuts
+// (`cut`, uniform), masked slots (x = -inf) weigh nothing whatever their
+// codes and scales hold (possibly NaN); elsewhere every slot is a key.
+__device__ inline float q8_weights(const float (&x)[4], float m, f32x4 vs, f32x4 vz, bool cut, float& l, f16x4& wh) {
+  float wz = 0.f;
+  if (cut) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(x[i] - m);
+      l += p;
+      const bool in = x[i] != -INFINITY;
+      wh[i] = static_cast<_Float16>(in ? p * vs[i] : 0.f);
+      wz += in ? static_cast<float>(wh[i]) * (kCodeBias + vz[i]) : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(x[i] - m);
+      l += p;
+      wh[i] = static_cast<_Float16>(p * vs[i]);
+      wz += static_cast<float>(wh[i]) * (kCodeBias + vz[i]);
+    }
+  }
+  return wz;
+}
+
 // One segment of the 8-bit cache (same role and lane layout as Segment).
 template <int D, bool kMulti>
 struct SegmentQ8 {
@@ -1093,10 +1122,35 @@ struct SegmentQ8 {
   size_t meta_stride;         // bytes between pages of the meta array
   uint32_t kn2, vn2;
 
-  // Query operand: MFMA 2j + e takes, in lane (c, n), features
-  // 16 (4j + c) + 8e .. +7 of head n: the features the K codes of load j
-  // bring to lanes of group c.  qsum = sum of the fp16 query features of the
-  // lane's head (the same fp16 values the MFMAs multiply).
+  // Query operand of one bf16 row qb (zeros if !g_ok): MFMA 2j + e takes,
+  // in lane (c, n), features 16 (4j + c) + 8e .. +7 of head n: the features
+  // the K codes of load j bring to lanes of group c.  Returns the sum of the
+  // row's fp16 features (the same fp16 values the MFMAs multiply), the same
+  // in every lane of the column.
+  __device__ static float load_query(const char* qb, bool g_ok, int c, u32x4 (&qh)[NQ]) {
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int j = i / 2, e = i % 2;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(qb + 128 * j + 32 * c + 16 * e);
+      f16x8 hv;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float lo = __builtin_bit_cast(float, t[w] << 16);
+        const float hi = __builtin_bit_cast(float, t[w] & 0xffff0000u);
+        hv[2 * w] = static_cast<_Float16>(lo);
+        hv[2 * w + 1] = static_cast<_Float16>(hi);
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) part += static_cast<float>(hv[w]);
+      qh[i] = g_ok ? __builtin_bit_cast(u32x4, hv) : u32x4{0u, 0u, 0u, 0u};
+    }
+    part = g_ok ? part : 0.f;
+    float sum = part + __shfl_xor(part, 16);
+    sum += __shfl_xor(sum, 32);
+    return sum;
+  }
+
   __device__ void begin(const DecodeArgs& a, int b_, int h_, int n_pages_, int fb_, bool ends_pair, int gblk,
                         int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -1126,27 +1180,7 @@ struct SegmentQ8 {
       meta_stride = static_cast<size_t>(a.n_kv) * 4 * kBlock * 4;
     }
     const size_t qrow = g_ok ? (static_cast<size_t>(b) * q_len + qi) * a.n_q + hq : 0;
-    const char* qb = static_cast<const char*>(a.q) + qrow * D * 2;
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int j = i / 2, e = i % 2;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(qb + 128 * j + 32 * c + 16 * e);
-      f16x8 hv;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float lo = __builtin_bit_cast(float, t[w] << 16);
-        const float hi = __builtin_bit_cast(float, t[w] & 0xffff0000u);
-        hv[2 * w] = static_cast<_Float16>(lo);
-        hv[2 * w + 1] = static_cast<_Float16>(hi);
-      }
-#pragma unroll
-      for (int w = 0; w < 8; ++w) part += static_cast<float>(hv[w]);
-      qh[i] = g_ok ? __builtin_bit_cast(u32x4, hv) : u32x4{0u, 0u, 0u, 0u};
-    }
-    part = g_ok ? part : 0.f;
-    qsum = part + __shfl_xor(part, 16);
-    qsum += __shfl_xor(qsum, 32);
+    qsum = load_query(static_cast<const char*>(a.q) + qrow * D * 2, g_ok, c, qh);
     m = kNoKeysMax;
     l = 0.f;
     corr = 0.f;
@@ -1154,17 +1188,15 @@ struct SegmentQ8 {
     for (int nb = 0; nb < NV; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // The fused append on the pair's last page: quantizes the new token (k_new
-  // / v_new, bf16) exactly as the quantizing append kernel does and puts it
-  // into the page registers (its K codes in lanes n == s_new, its V codes,
-  // scales and zero points in lanes c == s_new / 4, element s_new % 4); if
-  // `store`, hands it to `held` for page pg (LDS slot `slot`, or written at
-  // once if `now`).  Each lane quantizes its two features of kn2 / vn2; the
-  // codes reach the lanes that hold them in the page layout by lane
-  // permutes.  Runs once per pair, off the page loop's common path.
-  template <class Held>
-  __device__ void append_token(PageRegsQ8<D>& r, Held& t, char* kpool, char* vpool, size_t page_stride, int pg,
-                               bool store, int slot, int lane, bool now) const {
+  // The new token's codes as this lane holds them in the page registers (K:
+  // the 16 codes of features 16 (4 j + c) .. +15 per load j; V: the code of
+  // feature 16 nb + n) and its k scale, k zero, v scale, v zero (meta), from
+  // this lane's bf16 features 2 lane and 2 lane + 1 of K (kn2) and V (vn2),
+  // zeros past D.  Quantized exactly as the quantizing append kernel does;
+  // each lane quantizes its two features and lane permutes move the codes to
+  // the lanes that hold them.
+  __device__ static void quantize_token(uint32_t kn2, uint32_t vn2, int lane, u32x4 (&kq)[NK], uint32_t (&vq)[NV],
+                                        f32x4& meta) {
     const int c = lane >> 4, n = lane & 15;
     const float k0 = bf16_bits_to_f32(kn2 & 0xffffu), k1 = bf16_bits_to_f32(kn2 >> 16);
     const float v0 = bf16_bits_to_f32(vn2 & 0xffffu), v1 = bf16_bits_to_f32(vn2 >> 16);
@@ -1176,7 +1208,6 @@ struct SegmentQ8 {
     // K: lane 2m holds the codes of features 4m .. 4m + 3 in kd; lane (c, n)
     // needs features 16 (4 j + c) .. +15, m = 4 (4 j + c) + q.
     const uint32_t kd = ck | (static_cast<uint32_t>(__shfl_down(static_cast<int>(ck), 1)) << 16);
-    u32x4 kq[NK];
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int m0 = 8 * (4 * j + c);
@@ -1186,10 +1217,18 @@ struct SegmentQ8 {
                     static_cast<uint32_t>(__shfl(static_cast<int>(kd), m0 + 6))};
     }
     // V: lane (c, n) needs feature 16 nb + n: byte n % 2 of lane 8 nb + n / 2.
-    uint32_t vq[NV];
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb)
       vq[nb] = (static_cast<uint32_t>(__shfl(static_cast<int>(cv), 8 * nb + (n >> 1))) >> (8 * (n & 1))) & 0xffu;
+    meta = f32x4{ks, kz, vs, vz};
+  }
+
+  // Puts a token into the page registers at slot s_new: its K codes in the
+  // lanes n == s_new, its V codes, scales and zero points in the lanes
+  // c == s_new / 4, element s_new % 4.
+  __device__ static void patch_token(PageRegsQ8<D>& r, const u32x4 (&kq)[NK], const uint32_t (&vq)[NV], f32x4 meta,
+                                     int s_new, int lane) {
+    const int c = lane >> 4, n = lane & 15;
     if (n == s_new) {
 #pragma unroll
       for (int j = 0; j < NK; ++j) r.k[j] = kq[j];
@@ -1204,15 +1243,29 @@ struct SegmentQ8 {
       auto put = [e](f32x4 v, float x) {
         return f32x4{e == 0 ? x : v[0], e == 1 ? x : v[1], e == 2 ? x : v[2], e == 3 ? x : v[3]};
       };
-      r.ks = put(r.ks, ks);
-      r.kz = put(r.kz, kz);
-      r.vs = put(r.vs, vs);
-      r.vz = put(r.vz, vz);
+      r.ks = put(r.ks, meta[0]);
+      r.kz = put(r.kz, meta[1]);
+      r.vs = put(r.vs, meta[2]);
+      r.vz = put(r.vz, meta[3]);
     }
+  }
+
+  // The fused append on the pair's last page: the new token (k_new / v_new,
+  // bf16) quantized and put into the page registers; if `store`, handed to
+  // `held` for page pg (LDS slot `slot`, or written at once if `now`).  Runs
+  // once per pair, off the page loop's common path.
+  template <class Held>
+  __device__ void append_token(PageRegsQ8<D>& r, Held& t, char* kpool, char* vpool, size_t page_stride, int pg,
+                               bool store, int slot, int lane, bool now) const {
+    u32x4 kq[NK];
+    uint32_t vq[NV];
+    f32x4 meta;
+    quantize_token(kn2, vn2, lane, kq, vq, meta);
+    patch_token(r, kq, vq, meta, s_new, lane);
     if (store) {
       const size_t off = static_cast<size_t>(pg) * page_stride;
-      t.take(kq, vq, f32x4{ks, kz, vs, vz}, kpool + off, vpool + off,
-             meta_h + static_cast<size_t>(pg) * meta_stride, s_new, slot, lane, now);
+      t.take(kq, vq, meta, kpool + off, vpool + off, meta_h + static_cast<size_t>(pg) * meta_stride, s_new, slot,
+             lane, now);
     }
   }
 
@@ -1261,13 +1314,15 @@ struct SegmentQ8 {
     }
     const f32x4 raw = s0 + s1;   // lane (c, n): tokens 4c + i, head n
     float x[4];
-    bool in[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = tok0 + 4 * c + i;
-      in[i] = !cut || (kMulti ? (t < hi && t >= lo) : t < len);   // hi <= len: slots past the sequence are out too
-      const float sc = r.ks[i] * (raw[i] - (kCodeBias + r.kz[i]) * qsum) * scale_log2;
-      x[i] = in[i] ? sc : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = r.ks[i] * (raw[i] - (kCodeBias + r.kz[i]) * qsum) * scale_log2;
+    if (cut) {   // uniform: only pages where some column's key range starts or ends
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tok0 + 4 * c + i;
+        const bool in = kMulti ? (t < hi && t >= lo) : t < len;   // hi <= len: slots past the sequence are out too
+        x[i] = in ? x[i] : -INFINITY;
+      }
     }
     const float pm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     if (__builtin_amdgcn_ballot_w64(pm > m + kLazyRescale) != 0) {
@@ -1281,17 +1336,8 @@ struct SegmentQ8 {
       for (int nb = 0; nb < NV; ++nb) acc[nb] *= alpha;
       m = mn;
     }
-    // Weights w = p s in fp16 (round to nearest); slots past the length weigh
-    // nothing, whatever their codes and scales hold.
     f16x4 wh;
-    float wz = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(x[i] - m);
-      l += p;
-      wh[i] = static_cast<_Float16>(in[i] ? p * r.vs[i] : 0.f);
-      wz += in[i] ? static_cast<float>(wh[i]) * (kCodeBias + r.vz[i]) : 0.f;
-    }
+    const float wz = q8_weights(x, m, r.vs, r.vz, cut, l, wh);
     corr += wz;
 #pragma unroll
     for (int nb = 0; nb < NV; ++nb) {
@@ -1831,6 +1877,132 @@ struct PrefillTile {
   }
 };
 
+// PrefillTile's page step on the 8-bit cache (one query token, kNB blocks of
+// 16 query heads): the page's codes are turned into fp16 once for all
+// blocks, then each block takes SegmentQ8's score and weight corrections.
+// The correction sums (corr) are kept beside l; fold() takes them out of
+// the accumulators before a merge.
+template <int D, int kNB>
+struct WideTileQ8 {
+  using Seg = SegmentQ8<D, false>;
+  static constexpr int NQ = Seg::NQ, NK = Seg::NK, NV = Seg::NV;
+  u32x4 q[kNB][NQ];
+  float qsum[kNB];
+  int hi[kNB], lo[kNB];      // keys [lo, hi) of this lane's column
+  float m[kNB], l[kNB], corr[kNB];
+  f32x4 acc[kNB][NV];
+
+  __device__ void reset() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      m[k] = kNoKeysMax;
+      l[k] = 0.f;
+      corr[k] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Scores of page r in log2 units (-inf outside each column's key range
+  // when `cut`); pm: this lane's maximum per block.
+  __device__ void scores(const PageRegsQ8<D>& r, bool cut, int tok0, float scale_log2, int c, float (&x)[kNB][4],
+                         float (&pm)[kNB]) const {
+    u32x4 a0[NK], a1[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const u32x4 kk = r.k[i];
+      a0[i] = u32x4{code_pair_f16<0>(kk.x), code_pair_f16<1>(kk.x), code_pair_f16<0>(kk.y), code_pair_f16<1>(kk.y)};
+      a1[i] = u32x4{code_pair_f16<0>(kk.z), code_pair_f16<1>(kk.z), code_pair_f16<0>(kk.w), code_pair_f16<1>(kk.w)};
+    }
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0[i]),
+                                                   __builtin_bit_cast(f16x8, q[k][2 * i]), s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1[i]),
+                                                   __builtin_bit_cast(f16x8, q[k][2 * i + 1]), s1, 0, 0, 0);
+      }
+      const f32x4 raw = s0 + s1;   // lane (c, n): tokens 4c + i, head n of block k
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[k][i] = r.ks[i] * (raw[i] - (kCodeBias + r.kz[i]) * qsum[k]) * scale_log2;
+    }
+    if (cut) {   // uniform: only pages where some column's key range starts or ends
+#pragma unroll
+      for (int k = 0; k < kNB; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tok0 + 4 * c + i;
+          x[k][i] = ((t < hi[k]) & (t >= lo[k])) ? x[k][i] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) pm[k] = fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3]));
+  }
+
+  // One page of the accumulation; returns true (wave-uniform) if some score
+  // exceeded its column's maximum by more than kPrefillHeadroom.  fixed: the
+  // maxima are exact already (the redo pass).  valid is implied by the key
+  // ranges (hi <= the sequence length).
+  __device__ bool page(PageRegsQ8<D>& r, int, bool cut, int tok0, float scale_log2, int c, bool fixed) {
+    float x[kNB][4], pm[kNB];
+    scores(r, cut, tok0, scale_log2, c, x, pm);
+    bool init = false, over = false;
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      const bool unset = m[k] == kNoKeysMax;
+      init |= unset & (pm[k] > kNoKeysMax);
+      over |= !unset & (pm[k] > m[k] + kPrefillHeadroom);
+    }
+    if (!fixed && __builtin_amdgcn_ballot_w64(init) != 0) {
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
+      }
+    }
+    u32x2 va[NV];
+#pragma unroll
+    for (int nb = 0; nb < NV; ++nb) va[nb] = u32x2{code_pair_f16<0>(r.v[nb]), code_pair_f16<1>(r.v[nb])};
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      f16x4 wh;
+      corr[k] += q8_weights(x[k], m[k], r.vs, r.vz, cut, l[k], wh);
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb)
+        acc[k][nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va[nb]), wh, acc[k][nb], 0, 0, 0);
+    }
+    return __builtin_amdgcn_ballot_w64(over) != 0;
+  }
+
+  // Exact per-column maximum over page r (the redo pass).
+  __device__ void page_max(const PageRegsQ8<D>& r, bool cut, int tok0, float scale_log2, int c) {
+    float x[kNB][4], pm[kNB];
+    scores(r, cut, tok0, scale_log2, c, x, pm);
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      m[k] = fmaxf(m[k], cm);
+    }
+  }
+
+  // Takes each column's correction sum (over its four lane groups) out of
+  // its accumulators: acc then holds sum_t w_t (u_t - z_t) per feature.
+  __device__ void fold() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      float ct = corr[k] + __shfl_xor(corr[k], 16);
+      ct += __shfl_xor(ct, 32);
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb) acc[k][nb] -= ct;
+      corr[k] = 0.f;
+    }
+  }
+};
+
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 1
 #endif
@@ -1958,9 +2130,12 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
 }
 
 // Split-KV decode for 33 to 64 columns per KV head (MQA, or several query
-// tokens of a large group), bf16.  One wavefront computes all 64 columns of
-// every page it loads (four 16-column blocks, the prefill kernel's page
-// step), so each tile is loaded once per workgroup and the per-page work
+// tokens of a large group), bf16 or (kQ8) the 8-bit cache, whose codes are
+// turned into fp16 once per page for all four blocks (WideTileQ8); its
+// fused append quantizes the token on the page and stores it at once.  One
+// wavefront computes all 64 columns of every page it loads (four 16-column
+// blocks, the prefill kernel's page step), so each tile is loaded once per
+// workgroup and the per-page work
 // (page id, buffer resources, masks, cursors) is done once per page; the
 // kernel with one wavefront per 16-column block repeated it four times and
 // streamed a quarter as many distinct pages.  A chunk is a workgroup's:
@@ -1979,14 +2154,17 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
 // it is recomputed by that wavefront with exact maxima before the merge.
 // The number of segment ends is the same for the four wavefronts, so they
 // pass the same number of workgroup barriers.
-template <bool kBf16, int D, bool kMulti, int kDepth>
+template <bool kBf16, int D, bool kMulti, int kDepth, bool kQ8 = false>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 __attribute__((amdgpu_waves_per_eu(1)))
 wide_kernel(DecodeArgs a) {
+  static_assert(!kQ8 || (kBf16 && !kMulti), "the 8-bit cache: bf16 q and out, one query token");
   using O = Ops<kBf16, D>;
-  using Regs = PageRegs<kBf16, D>;
+  using Regs = std::conditional_t<kQ8, PageRegsQ8<D>, PageRegs<kBf16, D>>;
   constexpr int kNB = 4;
-  constexpr int kTile = kBlock * D * O::ES;
+  constexpr int NV = D / 16;
+  constexpr int kTile = kQ8 ? kBlock * D : kBlock * D * O::ES;   // bytes of one K (or V) tile
+  constexpr int kMetaTile = 4 * kBlock * 4;                       // 8-bit cache: meta of one tile
   constexpr int kBufs = kDepth + 1;
   constexpr int kRow = lds_row(D);
   constexpr int kSlotWords = 16 * kRow + 32;   // one block of one wavefront: rows [16][kRow], maxima [16], sums [16]
@@ -2017,7 +2195,7 @@ wide_kernel(DecodeArgs a) {
   FlatCursor<kMulti> sg;
   sg.seek(a, s_prefix, f0);
   int seg_start = 0, seg_hi = 0, len = 0;              // pair's first flat page; end of the segment in the chunk
-  PrefillTile<kBf16, D, kNB> t;
+  std::conditional_t<kQ8, WideTileQ8<D, kNB>, PrefillTile<kBf16, D, kNB>> t;
   bool bad = false, overflow = false;
   PendingMerges pending;
   // A segment's bounds (scalar), then its query operands and state; split
@@ -2038,10 +2216,14 @@ wide_kernel(DecodeArgs a) {
       const int ql = kMulti ? a.q_len : 1;
       const size_t qrow = g_ok ? (static_cast<size_t>(sg.b) * ql + qi) * a.n_q + hq : 0;
       const char* qb = static_cast<const char*>(a.q) + qrow * D * O::ES;
+      if constexpr (kQ8) {
+        t.qsum[k] = SegmentQ8<D, false>::load_query(qb, g_ok, c, t.q[k]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < O::NK; ++j) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * j + c));
-        t.q[k][j] = g_ok ? v : u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < O::NK; ++j) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qb + 16 * (4 * j + c));
+          t.q[k][j] = g_ok ? v : u32x4{0u, 0u, 0u, 0u};
+        }
       }
       t.hi[k] = len - ql + qi + 1;
       t.lo[k] = kMulti && a.window > 0 ? max(0, t.hi[k] - a.window) : 0;
@@ -2059,7 +2241,26 @@ wide_kernel(DecodeArgs a) {
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     bad |= !ok;
     if constexpr (!kMulti) {
-      if (a.k_new != nullptr && j == sg.n - 1) {
+      if (kQ8 && a.k_new != nullptr && j == sg.n - 1) {
+        if constexpr (kQ8) {   // quantized here and stored at once, like the dense token below
+          using Seg = SegmentQ8<D, false>;
+          const int s_new = (len - 1) & (kBlock - 1);
+          const size_t row = (static_cast<size_t>(sg.b) * a.n_kv + sg.h) * D;
+          const bool two = 2 * lane < D;
+          const uint32_t kn2 = two ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k_new) + row)[lane] : 0u;
+          const uint32_t vn2 = two ? reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_new) + row)[lane] : 0u;
+          u32x4 kq[Seg::NK];
+          uint32_t vq[Seg::NV];
+          f32x4 meta;
+          Seg::quantize_token(kn2, vn2, lane, kq, vq, meta);
+          Seg::patch_token(r, kq, vq, meta, s_new, lane);
+          if (ok && !fixed) {
+            const size_t tile = static_cast<size_t>(pg) * a.n_kv + sg.h;
+            Seg::store_codes(kq, vq, meta, kp0 + tile * kTile, vp0 + tile * kTile,
+                             const_cast<char*>(static_cast<const char*>(a.meta)) + tile * kMetaTile, s_new, lane);
+          }
+        }
+      } else if (!kQ8 && a.k_new != nullptr && j == sg.n - 1) {
         const int s_new = (len - 1) & (kBlock - 1);
         const size_t row = (static_cast<size_t>(sg.b) * a.n_kv + sg.h) * D;
         u32x4 kn[O::NK];
@@ -2072,17 +2273,19 @@ wide_kernel(DecodeArgs a) {
           if constexpr (kBf16) vn[nb] = static_cast<const uint16_t*>(a.v_new)[row + 16 * nb + n];
           else vn[nb] = static_cast<const uint32_t*>(a.v_new)[row + 16 * nb + n];
         }
-        if (n == s_new) {
+        if constexpr (!kQ8) {
+          if (n == s_new) {
 #pragma unroll
-          for (int i = 0; i < O::NK; ++i) r.k[i] = kn[i];
-        }
-        if (c == (s_new >> 2)) {
+            for (int i = 0; i < O::NK; ++i) r.k[i] = kn[i];
+          }
+          if (c == (s_new >> 2)) {
 #pragma unroll
-          for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::insert_v(r.v[nb], s_new & 3, vn[nb]);
-        }
-        if (ok && !fixed) {
-          const size_t off = static_cast<size_t>(pg) * page_stride + static_cast<size_t>(sg.h) * kTile;
-          HeldToken<kBf16, D, false>::store_regs(kn, vn, kp0 + off, vp0 + off, s_new, lane);
+            for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::insert_v(r.v[nb], s_new & 3, vn[nb]);
+          }
+          if (ok && !fixed) {
+            const size_t off = static_cast<size_t>(pg) * page_stride + static_cast<size_t>(sg.h) * kTile;
+            HeldToken<kBf16, D, false>::store_regs(kn, vn, kp0 + off, vp0 + off, s_new, lane);
+          }
         }
       }
     }
@@ -2090,12 +2293,20 @@ wide_kernel(DecodeArgs a) {
                             : tok0 + kBlock > len;
     return t.page(r, len - tok0, cut, tok0, a.scale_log2, c, fixed);
   };
+  // The (page pg, KV head h) tile's loads; a page id outside the pool reads
+  // nothing.
+  auto load_tile = [&](Regs& r, int pg, int h) {
+    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+    const size_t tile = static_cast<size_t>(ok ? pg : 0) * a.n_kv + h;
+    if constexpr (kQ8)
+      Q8KV<D>::template load<PKV_KV_LOAD_AUX>(r, a, tile, ok, lane);
+    else
+      load_page<kBf16, D, PKV_KV_LOAD_AUX>(r, kp0 + tile * kTile, vp0 + tile * kTile, 16u * lane,
+                                           O::ES * (n * kBlock + 4 * c), ok ? kTile : 0);
+  };
   auto load_flat = [&](Regs& r, int f) {              // page f of this segment, loaded and waited for
     const int pg = bt_row(sg.b)[sg.fb + (f - seg_start)];
-    const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-    load_page<kBf16, D, PKV_KV_LOAD_AUX>(r, kp0 + (static_cast<size_t>(ok ? pg : 0) * a.n_kv + sg.h) * kTile,
-                                         vp0 + (static_cast<size_t>(ok ? pg : 0) * a.n_kv + sg.h) * kTile,
-                                         16u * lane, O::ES * (n * kBlock + 4 * c), ok ? kTile : 0);
+    load_tile(r, pg, sg.h);
     return pg;
   };
   // End of a segment: exact redo if it overran, then the four-way merge
@@ -2117,7 +2328,7 @@ wide_kernel(DecodeArgs a) {
       for (int k = 0; k < kNB; ++k) {
         t.l[k] = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < O::NV; ++nb) t.acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NV; ++nb) t.acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       for (int f = first; f < seg_hi; f += 4) {
         Regs r;
@@ -2125,6 +2336,7 @@ wide_kernel(DecodeArgs a) {
         page_at(r, pg, f, true);
       }
     }
+    if constexpr (kQ8) t.fold();
     // Every wavefront leaves its four blocks in LDS, then wavefront j merges
     // block j of the four: one barrier to publish, one before the slots are
     // written again.
@@ -2134,14 +2346,14 @@ wide_kernel(DecodeArgs a) {
       lt += __shfl_xor(lt, 32);
       float* slot = mlds + (wave * kNB + j) * kSlotWords;
 #pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) *reinterpret_cast<f32x4*>(slot + n * kRow + 16 * nb + 4 * c) = t.acc[j][nb];
+      for (int nb = 0; nb < NV; ++nb) *reinterpret_cast<f32x4*>(slot + n * kRow + 16 * nb + 4 * c) = t.acc[j][nb];
       if (c == 0) {
         slot[16 * kRow + n] = t.m[j];
         slot[16 * kRow + 16 + n] = bad ? NAN : lt;
       }
     }
     __syncthreads();
-    f32x4 res[O::NV];
+    f32x4 res[NV];
     float mw[kWavesPerGroup];
     float mx = kNoKeysMax;
 #pragma unroll
@@ -2150,7 +2362,7 @@ wide_kernel(DecodeArgs a) {
       mx = fmaxf(mx, mw[w]);
     }
 #pragma unroll
-    for (int nb = 0; nb < O::NV; ++nb) res[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NV; ++nb) res[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float rl = 0.f;
 #pragma unroll
     for (int w = 0; w < kWavesPerGroup; ++w) {
@@ -2158,7 +2370,7 @@ wide_kernel(DecodeArgs a) {
       const float e = __builtin_amdgcn_exp2f(mw[w] - mx);
       rl += e * slot[16 * kRow + 16 + n];
 #pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) res[nb] += e * *reinterpret_cast<const f32x4*>(slot + n * kRow + 16 * nb + 4 * c);
+      for (int nb = 0; nb < NV; ++nb) res[nb] += e * *reinterpret_cast<const f32x4*>(slot + n * kRow + 16 * nb + 4 * c);
     }
     const float rm = mx;
     __syncthreads();
@@ -2167,7 +2379,7 @@ wide_kernel(DecodeArgs a) {
       const bool nan_row = rl != rl;
       const float inv = nan_row ? NAN : (rl > 0.f ? 1.0f / rl : 0.f);   // no key seen: zero row, lse -inf
 #pragma unroll
-      for (int nb = 0; nb < O::NV; ++nb) res[nb] *= inv;
+      for (int nb = 0; nb < NV; ++nb) res[nb] *= inv;
       const float lse = nan_row ? NAN : (rm + __log2f(rl)) * kLn2;
       emit_segment<kBf16, D, kMulti>(a, sg.b, sg.h, wave, sg.n, seg_start, chunk, C, res, lse, lane, pending);
     }
@@ -2187,10 +2399,7 @@ wide_kernel(DecodeArgs a) {
     int issued = 0;
     auto issue = [&](Regs& r, int& pg_out) {
       const int pg = issued < mine ? row[4 * issued] : -1;
-      const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
-      const size_t off = (static_cast<size_t>(ok ? pg : 0) * a.n_kv + sg.h) * kTile;
-      load_page<kBf16, D, PKV_KV_LOAD_AUX>(r, kp0 + off, vp0 + off, 16u * lane, O::ES * (n * kBlock + 4 * c),
-                                           ok ? kTile : 0);
+      load_tile(r, pg, sg.h);
       pg_out = pg;
       ++issued;
     };
@@ -2886,13 +3095,13 @@ SplitFn dyn_fn(int dtype, int head_dim, bool q8) {
 
 // cols: MFMA columns per KV head (query tokens x query heads); multi: more
 // than one query token or a sliding window (dense caches only).
-// 33 to 64 columns per KV head on a bf16 cache: the wide kernel (one
-// wavefront per page for all four 16-column blocks, pages of a chunk taken
-// in turn by the workgroup's four wavefronts).
+// 33 to 64 columns per KV head on a bf16 or 8-bit cache: the wide kernel
+// (one wavefront per page for all four 16-column blocks, pages of a chunk
+// taken in turn by the workgroup's four wavefronts).
 #ifndef PKV_WIDE_DEPTH
 #define PKV_WIDE_DEPTH 2
 #endif
-inline bool uses_wide(int dtype, int cols, bool q8) { return !q8 && dtype == PKV_BF16 && cols > 32; }
+inline bool uses_wide(int dtype, int cols, bool q8) { return (q8 || dtype == PKV_BF16) && cols > 32; }
 // Its LDS: the page prefix, then four wavefronts' merge slots of 16 columns.
 size_t wide_lds_bytes(int batch, int head_dim) {
   return (static_cast<size_t>(held_offset(batch)) + kWavesPerGroup * 4 * (16 * lds_row(head_dim) + 32)) * sizeof(int32_t);
@@ -2900,6 +3109,9 @@ size_t wide_lds_bytes(int batch, int head_dim) {
 
 SplitFn split_fn(int dtype, int head_dim, int cols, bool q8, bool multi) {
   if (uses_wide(dtype, cols, q8)) {
+    if (q8)
+      return head_dim == 128 ? wide_kernel<true, 128, false, PKV_WIDE_DEPTH, true>
+                             : wide_kernel<true, 64, false, PKV_WIDE_DEPTH, true>;
     if (multi)
       return head_dim == 128 ? wide_kernel<true, 128, true, PKV_WIDE_DEPTH> : wide_kernel<true, 64, true, PKV_WIDE_DEPTH>;
     return head_dim == 128 ? wide_kernel<true, 128, false, PKV_WIDE_DEPTH> : wide_kernel<true, 64, false, PKV_WIDE_DEPTH>;
