@@ -110,6 +110,9 @@ SMALL = [
     ("g24", 2, 48, 2, 128, [130, 61], 5, 1),
     ("mqa64", 2, 64, 1, 128, [300, 45], 6, 2),
     ("many_chunks", 3, 8, 2, 64, [1099, 39, 5], 150, 1),
+    ("mqa64_d64", 2, 64, 1, 64, [300, 45], 6, 2),         # wide kernel, head_dim 64
+    ("g48", 3, 96, 2, 128, [100, 17, 250], 5, 1),         # 48 columns: three blocks, the fourth empty
+    ("mqa_one_chunk", 3, 64, 1, 128, [40, 0, 7], 1, 1),   # every pair and segment end in one workgroup's chunk
 ]
 
 
@@ -164,7 +167,7 @@ def test_q8_rejects_mismatched_calls(pkv):
         dec.attn_q8(d.q, d.kc, d.vc, d.meta.view(-1)[1:], d.bt, d.lens, w.scale, out)
 
 
-@pytest.mark.parametrize("name", ["llama2_7b_mha", "llama3_8b_gqa"])
+@pytest.mark.parametrize("name", ["llama2_7b_mha", "llama3_8b_gqa", "long_70b_mqa"])
 def test_full_size_sampled_q8(pkv, name):
     # The full-size layer on the 8-bit cache in the benchmark's launch
     # configuration (library defaults, quantizing append then decode), checked
