@@ -258,7 +258,7 @@ def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0, max_workers=16):
             "seconds": secs}
 
 
-def gather_probe(w, S, dec, device, steps):
+def gather_probe(w, S, dec, device, steps, u8=False):
     """The gather probe (the decode kernel's tile stream, no arithmetic) on the
     same pools, block table and chunks, rotating the pool copies as the timed
     steps do: GB/s of algorithmic KV bytes."""
@@ -267,14 +267,19 @@ def gather_probe(w, S, dec, device, steps):
     sink = torch.empty(max(1, dec.n_items), dtype=torch.int32, device=device)
     layers = S["layers"]
     n = max(len(layers), steps)
+
+    def probe(L):
+        if u8:
+            pkv.gather_probe_q8(L.k_pages, L.v_pages, L.meta, S["bt"], S["seq_lens"], sink, dec.n_items,
+                                dec.min_chunk_pages)
+        else:
+            pkv.gather_probe(L.k_pages, L.v_pages, S["bt"], S["seq_lens"], sink, dec.n_items, dec.min_chunk_pages)
     for i in range(len(layers)):
-        L = layers[i]
-        pkv.gather_probe(L.k_pages, L.v_pages, S["bt"], S["seq_lens"], sink, dec.n_items, dec.min_chunk_pages)
+        probe(layers[i])
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for i in range(n):
-        L = layers[i % len(layers)]
-        pkv.gather_probe(L.k_pages, L.v_pages, S["bt"], S["seq_lens"], sink, dec.n_items, dec.min_chunk_pages)
+        probe(layers[i % len(layers)])
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / n
@@ -523,8 +528,8 @@ def main():
 
     probe = None if args.no_probe else hbm_probe(device)
     gprobe = None
-    if not args.no_probe and not multi and not u8:
-        gprobe = gather_probe(w, S, dec, device, args.steps * n_layers)
+    if not args.no_probe and not multi:
+        gprobe = gather_probe(w, S, dec, device, args.steps * n_layers, u8)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

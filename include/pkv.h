@@ -449,6 +449,17 @@ int pkv_copy_blocks(void* k_pages, void* v_pages, const int32_t* src_pages,
  * >= 4 * n_blocks bytes); pkv_copy_probe copies bytes (multiple of 16).
  * ------------------------------------------------------------------------ */
 int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_blocks, void* stream);
+/* The same probe on the 8-bit cache: the chunks, page-id reads and per-tile
+ * loads (K codes, V codes and meta, laid out as for pkv_paged_decode_attn_q8)
+ * of the 8-bit decode kernel with one query head per KV head, each tile only
+ * folded into an XOR written per chunk to sink (device uint32 [n_items],
+ * sink_bytes >= 4 * n_items); the ceiling the 8-bit decode is held to.  Page
+ * ids outside [0, num_pages) and invalid lengths are skipped. */
+int pkv_gather_probe_q8(const void* k_codes, const void* v_codes, const void* meta, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t n_kv_heads, int32_t head_dim, int32_t batch,
+                        int32_t max_blocks_per_seq, int32_t num_pages, int32_t n_items, int32_t min_chunk_pages,
+                        void* sink, size_t sink_bytes, void* stream);
+
 /* Gather probe: the decode kernel's own tile stream with no arithmetic, for
  * the bandwidth the memory system gives the workload's scattered (page, KV
  * head) tiles ("Transformer inference mechanics", "Knowledge check": measure

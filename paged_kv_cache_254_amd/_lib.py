@@ -111,6 +111,8 @@ SIGNATURES = {
     "pkv_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
     "pkv_gather_probe": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
                                         _i32, _vp, _sz, _vp]),
+    "pkv_gather_probe_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                                           _sz, _vp]),
 }
 
 for _name, (_res, _args) in SIGNATURES.items():

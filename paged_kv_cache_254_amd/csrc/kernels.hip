@@ -2991,6 +2991,73 @@ gather_probe_kernel(DecodeArgs a, size_t page_stride, size_t head_stride, uint32
   if (lane == 0) sink[chunk] = acc;
 }
 
+// The same probe for the 8-bit cache: the 8-bit decode kernel's chunks,
+// page-id reads and per-tile loads (K codes, V codes, meta; Q8KV::load),
+// each tile only folded into an XOR.
+template <int D, int kDepth>
+__global__ void __launch_bounds__(kWave * kWavesPerGroup)
+__attribute__((amdgpu_waves_per_eu(Q8KV<D>::kWavesPerEu)))
+gather_probe_q8_kernel(DecodeArgs a, uint32_t* sink) {
+  using Regs = PageRegsQ8<D>;
+  constexpr int kBufs = kDepth + 1;
+  extern __shared__ int32_t smem[];
+  int32_t* s_prefix = smem;
+  build_prefix(a.seq_lens, a.batch, a.max_blocks, 1, 0, s_prefix, smem + a.batch + 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = uni(threadIdx.x / kWave);
+  const int chunk = static_cast<int>(blockIdx.x) * kWavesPerGroup + wave;
+  if (chunk >= a.n_items) return;
+  const int total = uni(a.n_kv * s_prefix[a.batch]);
+  const int C = chunk_pages(total, a.n_items, a.min_chunk);
+  const int64_t f64 = static_cast<int64_t>(chunk) * C;
+  uint32_t acc = 0;
+  if (f64 < total) {
+    const int f0 = static_cast<int>(f64);
+    const int cnt = static_cast<int>(min(f64 + C, static_cast<int64_t>(total))) - f0;
+    FlatCursor<false> ld;
+    ld.seek(a, s_prefix, f0);
+    int issued = 0;
+    Regs buf[kBufs];
+    auto issue = [&](Regs& r) {
+      const bool in = issued < cnt;
+      const int pg = ((const const_i32*)(a.block_table + static_cast<size_t>(ld.b) * a.max_blocks))[ld.j];
+      const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
+      Q8KV<D>::template load<PKV_KV_LOAD_AUX>(r, a, static_cast<size_t>(ok ? pg : 0) * a.n_kv + ld.h, in && ok,
+                                              lane);
+      if (in) {
+        ++issued;
+        if (issued < cnt) ld.next(a, s_prefix);
+      }
+    };
+    auto fold = [&](const Regs& r) {
+#pragma unroll
+      for (int i = 0; i < Regs::NK; ++i) acc ^= r.k[i].x ^ r.k[i].y ^ r.k[i].z ^ r.k[i].w;
+#pragma unroll
+      for (int nb = 0; nb < Regs::NV; ++nb) acc ^= r.v[nb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc ^= __builtin_bit_cast(uint32_t, r.ks[i]) ^ __builtin_bit_cast(uint32_t, r.kz[i]) ^
+               __builtin_bit_cast(uint32_t, r.vs[i]) ^ __builtin_bit_cast(uint32_t, r.vz[i]);
+    };
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) issue(buf[s]);
+    int p = 0;
+    while (p < cnt) {
+#pragma unroll
+      for (int s = 0; s < kBufs; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(buf[(s + kDepth) % kBufs]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < cnt) fold(buf[s]);
+        ++p;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), off));
+  if (lane == 0) sink[chunk] = acc;
+}
+
 __global__ void __launch_bounds__(256)
 read_probe_kernel(const u32x4* __restrict__ buf, size_t n16, uint32_t* sink) {
   uint32_t x = 0;
@@ -3826,6 +3893,54 @@ int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* bl
   const int grid = (r.n_items + pkv::kWavesPerGroup - 1) / pkv::kWavesPerGroup;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(pkv::kWave * pkv::kWavesPerGroup), lds, static_cast<hipStream_t>(stream),
                      a, static_cast<size_t>(stride), static_cast<size_t>(hstride), static_cast<uint32_t*>(sink));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::hip_fail("gather probe launch", e);
+  return ok();
+}
+
+int pkv_gather_probe_q8(const void* k_codes, const void* v_codes, const void* meta, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t n_kv_heads, int32_t head_dim, int32_t batch,
+                        int32_t max_blocks_per_seq, int32_t num_pages, int32_t n_items, int32_t min_chunk_pages,
+                        void* sink, size_t sink_bytes, void* stream) {
+  int st = pkv::check_decode_shapes("pkv_gather_probe_q8", n_kv_heads, n_kv_heads, head_dim, pkv::kBlock, batch,
+                                    max_blocks_per_seq, num_pages, PKV_U8);
+  if (st != PKV_OK) return st;
+  if (batch == 0) return ok();
+  if (!k_codes || !v_codes || !meta || !block_table || !seq_lens || !sink || !pkv::aligned(k_codes, 16) ||
+      !pkv::aligned(v_codes, 16) || !pkv::aligned(meta, 16) || !pkv::aligned(block_table, 4) ||
+      !pkv::aligned(seq_lens, 4) || !pkv::aligned(sink, 4))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe_q8: NULL or misaligned pointer");
+  pkv_decode_opts o{n_items, min_chunk_pages, 0, PKV_SCHEDULE_STATIC};
+  pkv::Resolved r;
+  st = pkv::resolve_opts(PKV_U8, head_dim, 1, batch, max_blocks_per_seq, n_kv_heads, &o, &r);
+  if (st != PKV_OK) return st;
+  if (sink_bytes < static_cast<size_t>(r.n_items) * 4)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_gather_probe_q8: sink needs 4 * n_items bytes (" +
+                                         std::to_string(r.n_items) + " items)");
+  pkv::DecodeArgs a{};
+  a.k_pages = const_cast<void*>(k_codes);
+  a.v_pages = const_cast<void*>(v_codes);
+  a.meta = meta;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.n_q = n_kv_heads;
+  a.n_kv = n_kv_heads;
+  a.group = 1;
+  a.q_len = 1;
+  a.cols = 1;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.n_items = r.n_items;
+  a.min_chunk = r.min_chunk;
+  const size_t lds = pkv::split_lds_bytes(batch);
+  if (lds > pkv::kMaxLdsBytes) return fail(PKV_ERR_UNSUPPORTED, "pkv_gather_probe_q8: batch too large");
+  using Fn = void (*)(pkv::DecodeArgs, uint32_t*);
+  const Fn fn = head_dim == 128 ? pkv::gather_probe_q8_kernel<128, PKV_Q8_PREFETCH_PAGES>
+                                : pkv::gather_probe_q8_kernel<64, PKV_Q8_PREFETCH_PAGES>;
+  const int grid = (r.n_items + pkv::kWavesPerGroup - 1) / pkv::kWavesPerGroup;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(pkv::kWave * pkv::kWavesPerGroup), lds, static_cast<hipStream_t>(stream),
+                     a, static_cast<uint32_t*>(sink));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv::hip_fail("gather probe launch", e);
   return ok();

@@ -355,6 +355,21 @@ def gather_probe(k_pages, v_pages, block_table, seq_lens, sink, n_items: int = 0
           "pkv_gather_probe")
 
 
+def gather_probe_q8(k_codes, v_codes, meta, block_table, seq_lens, sink, n_items: int = 0,
+                    min_chunk_pages: int = 0, stream=None) -> None:
+    """The 8-bit decode kernel's tile stream without arithmetic (see
+    pkv_gather_probe_q8), on an 8-bit cache in the library's layout:
+    k_codes [P][Hkv][16 * D] uint8 (any shape with P and Hkv leading), meta
+    [P][Hkv][64] float32; sink: device int32 with at least n_items entries."""
+    B = block_table.shape[0]
+    P, Hkv = k_codes.shape[0], k_codes.shape[1]
+    D = k_codes[0, 0].numel() // 16
+    check(lib.pkv_gather_probe_q8(_ptr(k_codes), _ptr(v_codes), _ptr(meta), _ptr(block_table), _ptr(seq_lens), Hkv,
+                                  D, B, block_table.shape[1], P, int(n_items), int(min_chunk_pages), _ptr(sink),
+                                  sink.numel() * sink.element_size(), _stream(stream)),
+          "pkv_gather_probe_q8")
+
+
 def paged_decode_multi(q, k_pages, v_pages, block_table, seq_lens, q_len: int, scale, out, window: int = 0,
                        workspace=None, n_items: int = 0, min_chunk_pages: int = 0, stream=None):
     """pkv_paged_decode_multi: the last q_len cached tokens of each sequence

@@ -269,3 +269,27 @@ def test_step_q8_many_pairs_in_one_chunk(pkv, Hq, Hkv):
     _, d, out = _q8_step(pkv, w, c, 1, 1)
     H.assert_close(H.f64(out), ref, "bf16", f"q8 many pairs G={Hq // Hkv}")
     assert same_bits(d.kc, kc) and same_bits(d.vc, vc) and same_bits(d.meta, mt)
+
+
+def test_gather_probe_q8_reads_every_tile(pkv):
+    """pkv_gather_probe_q8 folds every attended page's K and V code tiles of a
+    chunk into one XOR (the meta words cancel: each is loaded by the 16 lanes
+    of its token group).  Against the same XOR computed on the host from the
+    chunk plan."""
+    w = W.custom("q8probe", 4, 8, 2, 128, "bf16", [300, 0, 45, 129], seed=97)
+    c = setup_q8(w)
+    d = to_dev(c)
+    n_items, mc = 7, 2
+    sink = torch.full((n_items,), -1, dtype=torch.int32, device="cuda")
+    pkv.gather_probe_q8(d.kc, d.vc, d.meta, d.bt, d.lens, sink, n_items, mc)
+    torch.cuda.synchronize()
+    C, _, _ = pkv.decode_plan(c.att.astype(np.int32), w.n_kv_heads, c.mb, n_items, mc)
+    kw = c.kc.numpy().reshape(c.kc.shape[0], w.n_kv_heads, -1).view(np.uint32)
+    vw = c.vc.numpy().reshape(c.vc.shape[0], w.n_kv_heads, -1).view(np.uint32)
+    flat = [(b, h, j) for b in range(w.batch) for h in range(w.n_kv_heads)
+            for j in range((int(c.att[b]) + 15) // 16)]
+    want = np.zeros(n_items, dtype=np.uint32)
+    for f, (b, h, j) in enumerate(flat):
+        pg = int(c.bt_np[b, j])
+        want[f // C] ^= np.bitwise_xor.reduce(kw[pg, h]) ^ np.bitwise_xor.reduce(vw[pg, h])
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
