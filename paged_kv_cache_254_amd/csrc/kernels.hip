@@ -3034,10 +3034,10 @@ gather_probe_q8_kernel(DecodeArgs a, uint32_t* sink) {
       for (int i = 0; i < Regs::NK; ++i) acc ^= r.k[i].x ^ r.k[i].y ^ r.k[i].z ^ r.k[i].w;
 #pragma unroll
       for (int nb = 0; nb < Regs::NV; ++nb) acc ^= r.v[nb];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc ^= __builtin_bit_cast(uint32_t, r.ks[i]) ^ __builtin_bit_cast(uint32_t, r.kz[i]) ^
-               __builtin_bit_cast(uint32_t, r.vs[i]) ^ __builtin_bit_cast(uint32_t, r.vz[i]);
+      // the meta as float sums (an XOR of their bits let the compiler drop
+      // the loads)
+      const f32x4 m = r.ks + r.kz + r.vs + r.vz;
+      acc ^= __builtin_bit_cast(uint32_t, m[0] + m[1] + m[2] + m[3]);
     };
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) issue(buf[s]);
