@@ -2135,18 +2135,18 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
 // fused append quantizes the token on the page and stores it at once.  One
 // wavefront computes all 64 columns of every page it loads (four 16-column
 // blocks, the prefill kernel's page step), so each tile is loaded once per
-// workgroup and the per-page work
-// (page id, buffer resources, masks, cursors) is done once per page; the
-// kernel with one wavefront per 16-column block repeated it four times and
-// streamed a quarter as many distinct pages.  A chunk is a workgroup's:
+// workgroup and the per-page work (page id, buffer resources, masks,
+// cursors) is done once per page; the kernel with one wavefront per
+// 16-column block repeated it four times and streamed a quarter as many
+// distinct pages.  A chunk is a workgroup's:
 // its four wavefronts take the chunk's pages in turn (wavefront w the pages
 // w, w + 4, ...), so they stream four neighbouring pages of the same pair
 // at a time.  The four walk the chunk's segments (the runs of pages of one
 // (sequence, KV head) pair) together; at the end of each segment each
 // leaves its four 16-column blocks of partial softmax state in LDS, and
 // after one barrier wavefront j merges block j of the four and writes block
-// j of the segment's result: the
-// output rows when the pair lies in this chunk, else the chunk's partial,
+// j of the segment's result: the output rows when the pair lies in this
+// chunk, else the chunk's partial,
 // merged with the pair's other chunks by the last to arrive (the same
 // slots, counters and merge as the other split kernels, per block j).
 // Running maxima are set on a column's first keys and not raised in the
