@@ -1660,6 +1660,17 @@ split_kernel(DecodeArgs a) {
   }
   bool open = false, bad = false;
   int seg_start = 0;
+  // The segment of the compute cursor's pair from the chunk's page p on:
+  // query rows (and the new token) requested, state cleared.
+  auto open_segment = [&](int p) {
+    const bool ends_pair = cp.j + (cnt - p) >= cp.n;
+#pragma unroll
+    for (int i = 0; i < kNB; ++i)
+      if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].begin(a, cp.b, cp.h, cp.n, cp.fb, i == 0 && ends_pair, gblk + i, lane);
+    seg_start = a.n_kv * cp.pb + cp.h * cp.n;
+    bad = false;
+    open = true;
+  };
   auto compute = [&](Regs& r, int pg, int p) {
     if (open && (cp.b != seg[0].b || cp.h != seg[0].h)) {
       if (kHoldResults && results.n < results.cap) {
@@ -1673,15 +1684,7 @@ split_kernel(DecodeArgs a) {
       }
       open = false;
     }
-    if (!open) {
-      const bool ends_pair = cp.j + (cnt - p) >= cp.n;
-#pragma unroll
-      for (int i = 0; i < kNB; ++i)
-        if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].begin(a, cp.b, cp.h, cp.n, cp.fb, i == 0 && ends_pair, gblk + i, lane);
-      seg_start = a.n_kv * cp.pb + cp.h * cp.n;
-      bad = false;
-      open = true;
-    }
+    if (!open) open_segment(p);
     const bool ok = static_cast<unsigned>(pg) < static_cast<unsigned>(a.num_pages);
     bad |= !ok;
     // Every head block patches its registers; the first one stores the token:
@@ -1703,6 +1706,10 @@ split_kernel(DecodeArgs a) {
       if (i == 0 || (gblk + i) * 16 < a.cols) seg[i].page(r, cp.j, a.scale_log2, lane);
   };
 
+  // The first segment's query rows go out before the ring's first tiles:
+  // vector memory loads complete in order, so the first page then waits for
+  // its own tiles only, not for the whole ring.
+  open_segment(0);
 #pragma unroll
   for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s]);
   // Whole turns of the ring, with the steps past the chunk's end skipped by
@@ -2198,9 +2205,10 @@ wide_kernel(DecodeArgs a) {
   std::conditional_t<kQ8, WideTileQ8<D, kNB>, PrefillTile<kBf16, D, kNB>> t;
   bool bad = false, overflow = false;
   PendingMerges pending;
-  // A segment's bounds (scalar), then its query operands and state; split
-  // so that the segment's first tile loads are in flight while the query
-  // rows arrive.
+  // A segment's bounds (scalar), then its query operands and state.  The
+  // query rows are requested before the segment's first tiles: vector memory
+  // loads complete in order, so the first page waits for its own tiles only,
+  // not for the whole ring.
   auto bounds = [&]() {
     seg_start = a.n_kv * sg.pb + sg.h * sg.n;
     seg_hi = min(seg_start + sg.n, fend);
@@ -2403,9 +2411,9 @@ wide_kernel(DecodeArgs a) {
       pg_out = pg;
       ++issued;
     };
+    open();
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s]);
-    open();
     int p = 0;
     while (p < mine) {
 #pragma unroll
