@@ -195,6 +195,7 @@ def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0, max_workers=16):
     import multiprocessing as mp
     import shutil
     import tempfile
+    import workloads as W
     n_workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     L = S["layers"][0]
     rng = np.random.default_rng(0)
@@ -214,9 +215,9 @@ def cpu_baseline(w, S, budget_s, kv="dense", q_len=1, window=0, max_workers=16):
             x = {"att": np.int64(S["att"][b]), "cached": np.int64(S["cached"][b]),
                  "bytes": np.int64(int(read[b]) * S["kv_bytes_layer"] // int(read.sum())),
                  "q": L.q[b:b + 1].float().cpu().numpy()}
-            if kv == "u8":
+            if kv == "u8":   # V codes into the oracle's [D][16] order
                 x.update(k=L.k_pages.index_select(0, pages).cpu().numpy(),
-                         v=L.v_pages.index_select(0, pages).cpu().numpy(),
+                         v=W.v_codes_to_logical(L.v_pages.index_select(0, pages).cpu().numpy()),
                          m=L.meta.index_select(0, pages).cpu().numpy(),
                          kn=L.k_new[b:b + 1].float().cpu().numpy(), vn=L.v_new[b:b + 1].float().cpu().numpy())
             else:

@@ -378,7 +378,11 @@ int pkv_paged_decode_multi(const void* q, const void* k_pages, const void* v_pag
  * Pools, per page and KV head (caller-owned device memory, 16-byte aligned):
  *   k_codes uint8 [num_pages][n_kv_heads][head_dim / 16][16][16]
  *           (token t, feature 16 c + x at [c][t][x])
- *   v_codes uint8 [num_pages][n_kv_heads][head_dim][16]  (feature d, token t at [d][t])
+ *   v_codes uint8 [num_pages][n_kv_heads][head_dim / 64][4][16][4][4]
+ *           (feature d = 64 j + 16 i + n, token t = 4 c + e at [j][c][n][i][e]:
+ *           byte 1024 (d / 64) + 256 (t / 4) + 16 (d % 16) + 4 ((d / 16) % 4)
+ *           + t % 4 of the tile, so that each lane of a wavefront reads its
+ *           operand bytes with 16-byte loads)
  *   meta    float [num_pages][n_kv_heads][4][16]  (k scale, k zero, v scale, v zero per slot)
  * 2 * head_dim + 16 bytes per token and KV head (272 at head_dim 128, against
  * 512 in bf16).  Unused slots may hold anything, NaN scales included.

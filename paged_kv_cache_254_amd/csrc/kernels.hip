@@ -1042,11 +1042,24 @@ __device__ inline uint32_t code_pair_f16(uint32_t w) {
 template <int D>
 struct PageRegsQ8 {
   static constexpr int NK = D / 64;   // 16-byte K loads per lane
-  static constexpr int NV = D / 16;   // 4-byte V loads per lane (4 tokens of one feature)
+  static constexpr int NV = D / 16;   // V words per lane (4 tokens of one feature), four per 16-byte load
   u32x4 k[NK];
   uint32_t v[NV];
   f32x4 ks, kz, vs, vz;               // tokens 4c .. 4c+3
 };
+
+// Byte of (feature d, slot s) in an 8-bit V-code tile.  The MFMA's value
+// operand puts slots 4c .. 4c+3 of feature 16 nb + n in lane (c, n) =
+// 16 c + n; the tile stores those four bytes, for nb = 4 j .. 4 j + 3, as
+// the 16 bytes at 1024 j + 16 lane, so a lane reads its V codes with D / 64
+// sixteen-byte loads (four-byte loads, one per feature block, gathered
+// measurably slower: about 5.3 against 6.3 TB/s for the whole tile stream).
+__host__ __device__ constexpr int q8_v_offset(int d, int s) {
+  return 1024 * (d >> 6) + 256 * (s >> 2) + 16 * (d & 15) + 4 * ((d >> 4) & 3) + (s & 3);
+}
+static_assert(q8_v_offset(127, 15) == 2047 && q8_v_offset(63, 15) == 1023 && q8_v_offset(16, 0) == 4 &&
+                  q8_v_offset(1, 4) == 272,
+              "V-code tile order");
 
 // The 8-bit quantizer of one vector of D features, decided in float32 with
 // IEEE division and round-half-to-even: lo = min(min x, 0), hi = max(max x,
@@ -1272,7 +1285,7 @@ struct SegmentQ8 {
   // Writes a token's codes, scales and zero points into slot s_new of one
   // (page, KV head) tile: kbase / vbase / mbase are that tile's K codes, V
   // codes and meta.  K: lanes n == s_new, 16 bytes per load; V: one byte per
-  // feature from lanes c == s_new / 4; meta: lanes 0-3.
+  // feature from lanes c == s_new / 4 (at q8_v_offset); meta: lanes 0-3.
   __device__ static void store_codes(const u32x4 (&kq)[NK], const uint32_t (&vq)[NV], f32x4 meta, char* kbase,
                                      char* vbase, char* mbase, int s_new, int lane) {
     const int c = lane >> 4, n = lane & 15;
@@ -1285,7 +1298,7 @@ struct SegmentQ8 {
     if (c == (s_new >> 2)) {
 #pragma unroll
       for (int nb = 0; nb < NV; ++nb)
-        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(vq[nb]), vr, 16 * (16 * nb + n) + s_new, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(vq[nb]), vr, q8_v_offset(16 * nb + n, s_new), 0, 0);
     }
     if (lane < 4) {
       const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(mbase, 0, 4 * kBlock * 4, PKV_RSRC_WORD3);
@@ -1531,7 +1544,7 @@ struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
   using Held = HeldTokenQ8<D, kDefer>;
   template <int kAux>
   __device__ static void load(Regs& r, const DecodeArgs& a, size_t tile, bool on, int lane) {
-    const int c = lane >> 4, n = lane & 15;
+    const int c = lane >> 4;
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<char*>(a.k_pages) + tile * kTileK, 0, on ? kTileK : 0, PKV_RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
@@ -1542,8 +1555,13 @@ struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
 #pragma unroll
     for (int j = 0; j < Regs::NK; ++j) r.k[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, 1024 * j + 16 * lane, 0, kAux);
 #pragma unroll
-    for (int nb = 0; nb < Regs::NV; ++nb)
-      r.v[nb] = __builtin_amdgcn_raw_buffer_load_b32(vr, 16 * (16 * nb + n) + 4 * c, 0, kAux);
+    for (int j = 0; j < Regs::NV / 4; ++j) {   // V words 4 j .. 4 j + 3 (q8_v_offset)
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(vr, 1024 * j + 16 * lane, 0, kAux);
+      r.v[4 * j] = w.x;
+      r.v[4 * j + 1] = w.y;
+      r.v[4 * j + 2] = w.z;
+      r.v[4 * j + 3] = w.w;
+    }
     r.ks = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 16 * c, 0, kAux));
     r.kz = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 64 + 16 * c, 0, kAux));
     r.vs = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(mr, 128 + 16 * c, 0, kAux));
@@ -2895,7 +2913,7 @@ append_q8_kernel(const void* k_new, const void* v_new, uint8_t* k_codes, uint8_t
       if (which == 0)
         k_codes[tile * kBlock * D + static_cast<size_t>(d / 16) * 256 + slot * 16 + d % 16] = u;
       else
-        v_codes[tile * kBlock * D + static_cast<size_t>(d) * kBlock + slot] = u;
+        v_codes[tile * kBlock * D + q8_v_offset(d, slot)] = u;
     }
     if (lane == 0) {
       meta[tile * 64 + (2 * which) * kBlock + slot] = sc;

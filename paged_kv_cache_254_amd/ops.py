@@ -162,8 +162,11 @@ def kv_append_tokens(k_new, v_new, k_pages, v_pages, block_table, positions, str
 
 
 def q8_pool_shapes(num_pages: int, n_kv_heads: int, head_dim: int):
-    """Shapes of the 8-bit cache's (k_codes uint8, v_codes uint8, meta float32)."""
-    return ((num_pages, n_kv_heads, head_dim // 16, BLOCK_SIZE, 16), (num_pages, n_kv_heads, head_dim, BLOCK_SIZE),
+    """Shapes of the 8-bit cache's (k_codes uint8, v_codes uint8, meta float32)
+    in the library's layout (include/pkv.h): v_codes [P][Hkv][D/64][4][16][4][4]
+    holds feature d = 64 j + 16 i + n, token t = 4 c + e at [j][c][n][i][e]."""
+    return ((num_pages, n_kv_heads, head_dim // 16, BLOCK_SIZE, 16),
+            (num_pages, n_kv_heads, head_dim // 64, 4, 16, 4, 4),
             (num_pages, n_kv_heads, 4, BLOCK_SIZE))
 
 

@@ -198,10 +198,35 @@ def make_pools(w: Workload, layer: int = 0, device="cpu"):
 
 
 def q8_pool_shapes(w: Workload, num_pages: Optional[int] = None):
-    """(k_codes, v_codes, meta) shapes of the 8-bit cache for this workload."""
+    """(k_codes, v_codes, meta) shapes of the 8-bit cache for this workload, in
+    the library's layout: v_codes [P][Hkv][D/64][4][16][4][4] (see
+    v_codes_to_logical)."""
     P = pool_pages(w) if num_pages is None else num_pages
     D = w.head_dim
-    return ((P, w.n_kv_heads, D // 16, 16, 16), (P, w.n_kv_heads, D, 16), (P, w.n_kv_heads, 4, 16))
+    return ((P, w.n_kv_heads, D // 16, 16, 16), (P, w.n_kv_heads, D // 64, 4, 16, 4, 4), (P, w.n_kv_heads, 4, 16))
+
+
+# The library's 8-bit V-code tile [D/64][4][16][4][4] holds feature
+# d = 64 j + 16 i + n, slot t = 4 c + e at [j][c][n][i][e]; the oracle's pools
+# keep the plain [D][16] (feature, slot) order.  Both conversions are the same
+# swap of the c and i axes (a pure byte permutation); numpy arrays or torch
+# tensors.
+_V_SWAP = (0, 1, 2, 5, 4, 3, 6)
+
+
+def v_codes_to_logical(v):
+    """Library-order 8-bit V codes [P][Hkv][D/64][4][16][4][4] -> [P][Hkv][D][16]."""
+    P, H, J = v.shape[:3]
+    t = v.permute(*_V_SWAP) if hasattr(v, "permute") else v.transpose(_V_SWAP)
+    return t.reshape(P, H, 64 * J, 16)
+
+
+def v_codes_from_logical(v):
+    """[P][Hkv][D][16] 8-bit V codes -> the library's order [P][Hkv][D/64][4][16][4][4]."""
+    P, H, D = v.shape[:3]
+    t = v.reshape(P, H, D // 64, 4, 16, 4, 4)
+    t = t.permute(*_V_SWAP) if hasattr(t, "permute") else t.transpose(_V_SWAP)
+    return t.contiguous() if hasattr(t, "contiguous") else np.ascontiguousarray(t)
 
 
 def make_q8_pools(w: Workload, layer: int = 0, device="cpu"):
