@@ -531,6 +531,14 @@ def main():
     gprobe = None
     if not args.no_probe and not multi:
         gprobe = gather_probe(w, S, dec, device, args.steps * n_layers, u8)
+    # Fixed cost per kernel launch on this stream (an empty kernel, one
+    # workgroup per CU): ordinary, cooperative, and cooperative with one
+    # grid-wide barrier (what folding the combine into the decode kernel
+    # would need).
+    launch_us = None
+    if not args.no_probe:
+        launch_us = {k: round(pkv.launch_probe(m, stream=stream), 2)
+                     for k, m in (("launch", 0), ("cooperative", 1), ("cooperative_grid_barrier", 2))}
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -591,6 +599,7 @@ def main():
         "gather_probe_gbs": None if gprobe is None else round(gprobe[0], 1),
         "gather_probe_ms": None if gprobe is None else round(gprobe[1], 5),
         "pct_of_gather_probe": None if gprobe is None else round(100 * achieved / gprobe[0], 1),
+        "launch_probe_us": launch_us,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),
     }

@@ -488,6 +488,23 @@ int pkv_gather_probe(const void* k_pages, const void* v_pages, const int32_t* bl
                      size_t sink_bytes, void* stream);
 int pkv_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Launch-cost probe: the fixed cost a step pays per kernel, which decides
+ * whether a second kernel (the combine of pairs split over more than 96
+ * chunks) can be folded into the decode kernel ("Transformer inference
+ * mechanics", "Knowledge check": kernel time and launch gaps).  Launches a
+ * kernel that does nothing over `grid` workgroups of 256 threads (0: one per
+ * compute unit) `iters` times back to back on `stream` after 5 untimed
+ * launches, and writes the mean time per launch in microseconds (HIP events)
+ * to *us_per_launch (host).  mode 0: ordinary launches; 1: cooperative
+ * launches (the whole grid resident at once); 2: cooperative launches whose
+ * workgroups meet once at a grid-wide barrier in bar (device int32 [3],
+ * zeroed by the caller; on return bar[0] is 0 again, bar[1] counts the
+ * barriers passed and bar[2] the polls that gave up, 0 unless the barrier
+ * failed).  Blocks until the launches have finished.  Errors: bad mode,
+ * grid, iters or pointers; no cooperative launch on the device; a
+ * cooperative grid larger than the device holds at once (PKV_ERR_HIP). */
+int pkv_launch_probe(int32_t mode, int32_t grid, int32_t iters, int32_t* bar, float* us_per_launch, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,7 +8,7 @@ from ._lib import (LIB_PATH, PKV_BF16, PKV_F32, PKV_SCHEDULE_AUTO, PKV_SCHEDULE_
                    PKV_SCHEDULE_STATIC, PKV_U8, PkvError, lib)
 from .ops import (BLOCK_SIZE, Decoder, PagePool, copy_blocks, copy_probe, decode_resolve,  # noqa: F401
                   decode_plan, decode_workspace_bytes, gather_probe, gather_probe_q8, hbm_read_probe, kv_append,
-                  kv_append_q8, kv_append_tokens, q8_pool_shapes,
+                  kv_append_q8, kv_append_tokens, launch_probe, q8_pool_shapes,
                   kv_bytes_per_token, kv_cache_bytes, paged_decode_attn, paged_decode_multi)
 
 __version__ = lib.pkv_version().decode()

@@ -109,6 +109,7 @@ SIGNATURES = {
                                           ctypes.POINTER(DecodeOpts)]),
     "pkv_hbm_read_probe": (ctypes.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "pkv_copy_probe": (ctypes.c_int, [_vp, _vp, _sz, _vp]),
+    "pkv_launch_probe": (ctypes.c_int, [_i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_gather_probe": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
                                         _i32, _vp, _sz, _vp]),
     "pkv_gather_probe_q8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,

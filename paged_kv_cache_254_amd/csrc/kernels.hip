@@ -3104,6 +3104,36 @@ copy_probe_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, size_t
     dst[i] = src[i];
 }
 
+// Launch-cost probe: a kernel that does nothing but, with `barrier` set, meet
+// every other workgroup of the grid once.  The barrier is one arrival counter
+// (bar[0]) and a generation word (bar[1]): each workgroup's first lane adds 1
+// to the counter; the last to arrive clears it and advances the generation,
+// the others poll the generation until it moves.  Only valid in a
+// cooperative launch, which guarantees that the whole grid is resident; a
+// poll still gives up after spin_limit rounds and counts a timeout in
+// bar[2], so every wave ends whatever happens.
+__global__ void __launch_bounds__(256) launch_probe_kernel(int* bar, int barrier, int spin_limit) {
+  if (!barrier) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int gen = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(&bar[0], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == static_cast<int>(gridDim.x) - 1) {
+      __hip_atomic_store(&bar[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&bar[1], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      for (int i = 0; __hip_atomic_load(&bar[1], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen; ++i) {
+        if (i >= spin_limit) {
+          __hip_atomic_fetch_add(&bar[2], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
@@ -3981,6 +4011,47 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, void* sink, int32_t n_bloc
                      static_cast<uint32_t*>(sink));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv::hip_fail("read probe launch", e);
+  return ok();
+}
+
+int pkv_launch_probe(int32_t mode, int32_t grid, int32_t iters, int32_t* bar, float* us_per_launch, void* stream) {
+  if (mode < 0 || mode > 2 || grid < 0 || iters < 1 || us_per_launch == nullptr || (mode == 2 && bar == nullptr) ||
+      (bar != nullptr && !pkv::aligned(bar, 4)))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_launch_probe: bad argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0, n_cu = 0, coop = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (e != hipSuccess) return pkv::hip_fail("launch probe device query", e);
+  if (mode > 0 && !coop) return fail(PKV_ERR_UNSUPPORTED, "pkv_launch_probe: no cooperative launch on this device");
+  if (grid == 0) grid = n_cu;
+  int* bar_arg = bar;
+  int barrier = mode == 2 ? 1 : 0;
+  int spin_limit = 1 << 20;
+  void* args[] = {&bar_arg, &barrier, &spin_limit};
+  auto launch = [&]() -> hipError_t {
+    if (mode == 0) {
+      hipLaunchKernelGGL(pkv::launch_probe_kernel, dim3(grid), dim3(256), 0, s, bar_arg, barrier, spin_limit);
+      return hipGetLastError();
+    }
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(pkv::launch_probe_kernel), dim3(grid), dim3(256),
+                                      args, 0, s);
+  };
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  for (int i = 0; i < 5 && e == hipSuccess; ++i) e = launch();   // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  for (int i = 0; i < iters && e == hipSuccess; ++i) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return pkv::hip_fail("launch probe", e);
+  *us_per_launch = 1000.f * ms / static_cast<float>(iters);
   return ok();
 }
 

@@ -344,6 +344,20 @@ def copy_probe(dst, src, stream=None) -> None:
           "pkv_copy_probe")
 
 
+def launch_probe(mode: int, grid: int = 0, iters: int = 200, bar=None, stream=None) -> float:
+    """Mean microseconds per launch of an empty kernel (see pkv_launch_probe):
+    mode 0 ordinary, 1 cooperative, 2 cooperative with one grid-wide barrier
+    in bar (device int32 [3], zeroed; allocated here when None)."""
+    import ctypes
+    if mode == 2 and bar is None:
+        import torch
+        bar = torch.zeros(3, dtype=torch.int32, device="cuda")
+    us = ctypes.c_float(0.0)
+    check(lib.pkv_launch_probe(int(mode), int(grid), int(iters), _ptr(bar) if bar is not None else None,
+                               ctypes.byref(us), _stream(stream)), "pkv_launch_probe")
+    return float(us.value)
+
+
 def gather_probe(k_pages, v_pages, block_table, seq_lens, sink, n_items: int = 0, min_chunk_pages: int = 0,
                  stream=None) -> None:
     """The decode kernel's tile stream without arithmetic (see pkv_gather_probe),

@@ -244,6 +244,17 @@ def test_append_rejects_bad_arguments():
     assert f(*base[:6], 0, *base[7:]) == _lib.PKV_OK  # empty batch: nothing to do
 
 
+def test_launch_probe_rejects_bad_arguments_before_any_launch():
+    import ctypes
+    f = _lib.lib.pkv_launch_probe
+    us = ctypes.c_float(0.0)
+    assert f(3, 0, 10, None, ctypes.byref(us), None) == _lib.PKV_ERR_INVALID_ARG   # no such mode
+    assert f(0, -1, 10, None, ctypes.byref(us), None) == _lib.PKV_ERR_INVALID_ARG  # negative grid
+    assert f(0, 0, 0, None, ctypes.byref(us), None) == _lib.PKV_ERR_INVALID_ARG    # no launches
+    assert f(2, 0, 10, None, ctypes.byref(us), None) == _lib.PKV_ERR_INVALID_ARG   # barrier without bar
+    assert f(0, 0, 10, None, None, None) == _lib.PKV_ERR_INVALID_ARG               # no result pointer
+
+
 def test_single_hip_runtime_in_process():
     # libpkv.so must share torch's HIP runtime (two runtimes cannot exchange
     # device pointers or streams).  Run in a fresh interpreter that imports the
