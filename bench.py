@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-launch-probe", action="store_true",
+                    help="skip the launch-cost probe (its cooperative launches; e.g. under a profiler)")
     ap.add_argument("--kv", choices=["dense", "u8"], default="dense",
                     help="cache format: the workload's dtype, or the 8-bit cache (bf16 q/out)")
     ap.add_argument("--q-len", type=int, default=1,
@@ -536,7 +538,7 @@ def main():
     # grid-wide barrier (what folding the combine into the decode kernel
     # would need).
     launch_us = None
-    if not args.no_probe:
+    if not args.no_probe and not args.no_launch_probe:
         launch_us = {k: round(pkv.launch_probe(m, stream=stream), 2)
                      for k, m in (("launch", 0), ("cooperative", 1), ("cooperative_grid_barrier", 2))}
     cpu = None
