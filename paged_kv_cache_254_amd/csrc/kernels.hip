@@ -1031,6 +1031,7 @@ __device__ void write_empty_rows(const DecodeArgs& a, const int32_t* s_prefix, i
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr float kCodeBias = 1024.0f;
 
 // Codes 2e and 2e + 1 of the word as the fp16 pair (1024 + u, 1024 + u').
@@ -1141,11 +1142,21 @@ struct SegmentQ8 {
   // row's fp16 features (the same fp16 values the MFMAs multiply), the same
   // in every lane of the column.
   __device__ static float load_query(const char* qb, bool g_ok, int c, u32x4 (&qh)[NQ]) {
+    fetch_row(qb, c, qh);
+    return convert_query(qh, g_ok);
+  }
+  // The two halves of load_query: the row's bf16 pieces as loaded (into qh),
+  // then converted in place (returns the sum).  Split so that a caller can
+  // issue other loads between them.
+  __device__ static void fetch_row(const char* qb, int c, u32x4 (&qh)[NQ]) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) qh[i] = *reinterpret_cast<const u32x4*>(qb + 128 * (i / 2) + 32 * c + 16 * (i % 2));
+  }
+  __device__ static float convert_query(u32x4 (&qh)[NQ], bool g_ok) {
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
-      const int j = i / 2, e = i % 2;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(qb + 128 * j + 32 * c + 16 * e);
+      const u32x4 t = qh[i];
       f16x8 hv;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -1904,17 +1915,18 @@ struct PrefillTile {
 
 // PrefillTile's page step on the 8-bit cache (one query token, kNB blocks of
 // 16 query heads): the page's codes are turned into fp16 once for all
-// blocks, then each block takes SegmentQ8's score and weight corrections.
-// The correction sums (corr) are kept beside l; fold() takes them out of
-// the accumulators before a merge.
+// blocks, each block's scores take SegmentQ8's zero-point correction, and
+// the value operand carries the zero points itself (codes minus zero
+// points), so the accumulators hold sum_t w_t (u_t - z_t) directly.
 template <int D, int kNB>
 struct WideTileQ8 {
   using Seg = SegmentQ8<D, false>;
   static constexpr int NQ = Seg::NQ, NK = Seg::NK, NV = Seg::NV;
-  u32x4 q[kNB][NQ];
+  u32x4 q[kNB][NQ];          // the query rows: bf16 as loaded, then fp16 (convert)
   float qsum[kNB];
+  bool gok[kNB];
   int hi[kNB], lo[kNB];      // keys [lo, hi) of this lane's column
-  float m[kNB], l[kNB], corr[kNB];
+  float m[kNB], l[kNB];
   f32x4 acc[kNB][NV];
 
   __device__ void reset() {
@@ -1922,10 +1934,17 @@ struct WideTileQ8 {
     for (int k = 0; k < kNB; ++k) {
       m[k] = kNoKeysMax;
       l[k] = 0.f;
-      corr[k] = 0.f;
 #pragma unroll
       for (int nb = 0; nb < NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
+
+  // The query rows fetched into q (SegmentQ8::fetch_row) converted to fp16
+  // in place, with their sums; after the segment's first tile loads, so that
+  // the wait for the rows does not hold those loads back.
+  __device__ void convert() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) qsum[k] = Seg::convert_query(q[k], gok[k]);
   }
 
   // Scores of page r in log2 units (-inf outside each column's key range
@@ -1939,19 +1958,26 @@ struct WideTileQ8 {
       a0[i] = u32x4{code_pair_f16<0>(kk.x), code_pair_f16<1>(kk.x), code_pair_f16<0>(kk.y), code_pair_f16<1>(kk.y)};
       a1[i] = u32x4{code_pair_f16<0>(kk.z), code_pair_f16<1>(kk.z), code_pair_f16<0>(kk.w), code_pair_f16<1>(kk.w)};
     }
+    f32x4 ksl, kzb;   // per token, shared by the blocks: k scale in log2 units, biased k zero
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ksl[i] = r.ks[i] * scale_log2;
+      kzb[i] = kCodeBias + r.kz[i];
+    }
+    // One accumulation chain per block: the blocks are independent, so the
+    // matrix core always has work without a second chain and its sum.
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 raw = {0.f, 0.f, 0.f, 0.f};   // lane (c, n): tokens 4c + i, head n of block k
 #pragma unroll
       for (int i = 0; i < NK; ++i) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0[i]),
-                                                   __builtin_bit_cast(f16x8, q[k][2 * i]), s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1[i]),
-                                                   __builtin_bit_cast(f16x8, q[k][2 * i + 1]), s1, 0, 0, 0);
+        raw = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0[i]),
+                                                    __builtin_bit_cast(f16x8, q[k][2 * i]), raw, 0, 0, 0);
+        raw = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1[i]),
+                                                    __builtin_bit_cast(f16x8, q[k][2 * i + 1]), raw, 0, 0, 0);
       }
-      const f32x4 raw = s0 + s1;   // lane (c, n): tokens 4c + i, head n of block k
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[k][i] = r.ks[i] * (raw[i] - (kCodeBias + r.kz[i]) * qsum[k]) * scale_log2;
+      for (int i = 0; i < 4; ++i) x[k][i] = (raw[i] - kzb[i] * qsum[k]) * ksl[i];
     }
     if (cut) {   // uniform: only pages where some column's key range starts or ends
 #pragma unroll
@@ -1988,13 +2014,27 @@ struct WideTileQ8 {
         m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
       }
     }
+    // Value operand: each code minus its token's zero point, (1024 + u) -
+    // (1024 + z) in fp16, exact (integers in [-255, 255]), once per page for
+    // the four blocks; so the accumulators need no zero-point correction.
+    // Slots past the key range (cut pages only) may hold NaN zero points:
+    // they take 0 (their weights are 0).
+    f32x4 vz = r.vz;
+    if (cut) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vz[i] = tok0 + 4 * c + i < hi[0] ? vz[i] : 0.f;
+    }
+    const f16x2 z01 = {static_cast<_Float16>(kCodeBias + vz[0]), static_cast<_Float16>(kCodeBias + vz[1])};
+    const f16x2 z23 = {static_cast<_Float16>(kCodeBias + vz[2]), static_cast<_Float16>(kCodeBias + vz[3])};
     u32x2 va[NV];
 #pragma unroll
-    for (int nb = 0; nb < NV; ++nb) va[nb] = u32x2{code_pair_f16<0>(r.v[nb]), code_pair_f16<1>(r.v[nb])};
+    for (int nb = 0; nb < NV; ++nb)
+      va[nb] = u32x2{__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, code_pair_f16<0>(r.v[nb])) - z01),
+                     __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, code_pair_f16<1>(r.v[nb])) - z23)};
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
       f16x4 wh;
-      corr[k] += q8_weights(x[k], m[k], r.vs, r.vz, cut, l[k], wh);
+      (void)q8_weights(x[k], m[k], r.vs, r.vz, cut, l[k], wh);   // its zero-point sum is not needed here
 #pragma unroll
       for (int nb = 0; nb < NV; ++nb)
         acc[k][nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va[nb]), wh, acc[k][nb], 0, 0, 0);
@@ -2014,18 +2054,6 @@ struct WideTileQ8 {
     }
   }
 
-  // Takes each column's correction sum (over its four lane groups) out of
-  // its accumulators: acc then holds sum_t w_t (u_t - z_t) per feature.
-  __device__ void fold() {
-#pragma unroll
-    for (int k = 0; k < kNB; ++k) {
-      float ct = corr[k] + __shfl_xor(corr[k], 16);
-      ct += __shfl_xor(ct, 32);
-#pragma unroll
-      for (int nb = 0; nb < NV; ++nb) acc[k][nb] -= ct;
-      corr[k] = 0.f;
-    }
-  }
 };
 
 #ifndef PKV_PREFILL_WAVES_PER_EU
@@ -2242,8 +2270,9 @@ wide_kernel(DecodeArgs a) {
       const int ql = kMulti ? a.q_len : 1;
       const size_t qrow = g_ok ? (static_cast<size_t>(sg.b) * ql + qi) * a.n_q + hq : 0;
       const char* qb = static_cast<const char*>(a.q) + qrow * D * O::ES;
-      if constexpr (kQ8) {
-        t.qsum[k] = SegmentQ8<D, false>::load_query(qb, g_ok, c, t.q[k]);
+      if constexpr (kQ8) {   // converted after the first tile loads (t.convert)
+        SegmentQ8<D, false>::fetch_row(qb, c, t.q[k]);
+        t.gok[k] = g_ok;
       } else {
 #pragma unroll
         for (int j = 0; j < O::NK; ++j) {
@@ -2362,7 +2391,6 @@ wide_kernel(DecodeArgs a) {
         page_at(r, pg, f, true);
       }
     }
-    if constexpr (kQ8) t.fold();
     // Every wavefront leaves its four blocks in LDS, then wavefront j merges
     // block j of the four: one barrier to publish, one before the slots are
     // written again.
@@ -2432,6 +2460,7 @@ wide_kernel(DecodeArgs a) {
     open();
 #pragma unroll
     for (int s = 0; s < kDepth; ++s) issue(buf[s], page_of[s]);
+    if constexpr (kQ8) t.convert();
     int p = 0;
     while (p < mine) {
 #pragma unroll
