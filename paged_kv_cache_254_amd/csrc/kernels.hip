@@ -29,6 +29,8 @@
 //   K page [D/X][16][X]: lane l of load i reads bytes 1024 i + 16 l;
 //   V page [D][16]:      lane (c = l/16, n = l%16) reads tokens 4c..4c+3 of
 //                        feature row 16 nb + n.
+// The 8-bit cache stores its V codes in the order the lanes read them
+// (q8_v_offset), so they too arrive with 16-byte loads.
 // No LDS is needed for the tiles; each K/V tile is read from HBM once and used
 // for all query heads of the group from registers.
 #include <hip/hip_runtime.h>

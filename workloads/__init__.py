@@ -34,6 +34,9 @@ oracle; the pages fix only that a block holds 16 tokens):
   4 for fp32): each token's key is cut into 16-byte pieces, and the pieces of
   all 16 tokens that cover the same feature range are stored next to each other.
 * V pool ``[P][Hkv][D][16]``: the page holds V transposed (feature-major).
+* 8-bit pools (``make_q8_pools``): K codes ``[P][Hkv][D / 16][16][16]``, V codes
+  ``[P][Hkv][D / 64][4][16][4][4]`` in the library's order (the oracle keeps
+  ``[D][16]``; ``v_codes_to_logical`` converts), meta ``[P][Hkv][4][16]``.
 """
 from __future__ import annotations
 
