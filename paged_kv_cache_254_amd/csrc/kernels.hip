@@ -110,6 +110,18 @@ struct Ops<true, D> {  // bfloat16
     }
     return s0 + s1;
   }
+  // The same product as one accumulation chain, for callers that compute
+  // several independent blocks per page (their chains keep the matrix core
+  // busy, and the sum of two chains would cost a register move and an add
+  // per score).
+  __device__ static f32x4 qk1(const u32x4 (&k)[NK], const u32x4 (&q)[NK]) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NK; ++i)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[i]), __builtin_bit_cast(bf16x8, q[i]),
+                                                  s, 0, 0, 0);
+    return s;
+  }
 
   // Zero the V elements of tokens >= valid (lane holds tokens 4c..4c+3).
   __device__ static VReg mask_v(VReg v, int c, int valid) {
@@ -172,6 +184,17 @@ struct Ops<false, D> {  // float32
                                                 lane_f32<3>(q[i]), s1, 0, 0, 0);
     }
     return s0 + s1;
+  }
+  __device__ static f32x4 qk1(const u32x4 (&k)[NK], const u32x4 (&q)[NK]) {   // one chain (see Ops<true>)
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<0>(k[i]), lane_f32<0>(q[i]), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<1>(k[i]), lane_f32<1>(q[i]), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<2>(k[i]), lane_f32<2>(q[i]), s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(lane_f32<3>(k[i]), lane_f32<3>(q[i]), s, 0, 0, 0);
+    }
+    return s;
   }
 
   __device__ static VReg insert_v(VReg v, int e, uint32_t bits) {
@@ -1848,7 +1871,7 @@ struct PrefillTile {
                          float (&x)[kNB][4], float (&pm)[kNB]) const {
     f32x4 s[kNB];
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) s[k] = O::qk(r.k, q[k]);
+    for (int k = 0; k < kNB; ++k) s[k] = kNB > 1 ? O::qk1(r.k, q[k]) : O::qk(r.k, q[k]);
 #pragma unroll
     for (int k = 0; k < kNB; ++k)
 #pragma unroll
@@ -3425,8 +3448,10 @@ int scratch_of_current_device(hipStream_t stream, void** out) {
 #endif
 // 16-column blocks (query tokens x query heads of one KV head) per
 // wavefront of the prefill kernel, and its ring depth.  Four blocks fit the
-// register file (bf16: 256 VGPRs + 236 AGPRs at head_dim 128, no scratch);
-// fp32 at head_dim 128 takes two, with one page ahead.
+// register file (bf16: 232 VGPRs + 140 AGPRs at head_dim 128, no scratch; one
+// wavefront per SIMD); fp32 at head_dim 128 takes two, with one page ahead.
+// Two wavefronts of two blocks per SIMD measured 36 % slower, three blocks
+// 10 % slower.
 #ifndef PKV_PREFILL_BLOCKS
 #define PKV_PREFILL_BLOCKS 4
 #endif
