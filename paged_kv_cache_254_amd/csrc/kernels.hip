@@ -92,6 +92,20 @@ __device__ inline float lane_f32(u32x4 v) {
 template <bool kBf16, int D>
 struct Ops;
 
+// Four floats rounded to bf16 (nearest even) and packed as an MFMA operand.
+// Converted two at a time: the compiler turns each two-wide conversion into
+// one v_cvt_pk_bf16_f32, but splits a four-wide one into single conversions
+// and permutes.  (Ops::pv keeps single conversions: its sum of the rounded
+// values reads them one by one, and the split kernel measured 1.6 % slower
+// on the 32-layer step with the pairs.)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ inline i16x4 pack_bf16x4(float p0, float p1, float p2, float p3) {
+  const bf16x2 lo = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector(f32x2{p2, p3}, bf16x2);
+  return __builtin_bit_cast(i16x4, u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)});
+}
+
 template <int D>
 struct Ops<true, D> {  // bfloat16
   static constexpr int ES = 2;
@@ -1852,16 +1866,36 @@ struct PrefillTile {
   using O = Ops<kBf16, D>;
   u32x4 q[kNB][O::NK];
   int hi[kNB], lo[kNB];      // keys [lo, hi) of this lane's column
-  float m[kNB], l[kNB];
+  float m[kNB];
+  // Sums of the weights.  bf16: accumulated by the matrix core as the
+  // product of an all-ones operand with the same rounded weights the PV
+  // product takes, so every element holds its column's sum over all tokens
+  // (and the weights are converted to bf16 in pairs, with nothing to unpack
+  // for a vector-unit sum).  fp32: element 0 holds this lane's sum over its
+  // four tokens.
+  f32x4 lsum[kNB];
   f32x4 acc[kNB][O::NV];
 
-  __device__ void reset() {
+  __device__ void clear_sums() {
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
-      m[k] = kNoKeysMax;
-      l[k] = 0.f;
+      lsum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int nb = 0; nb < O::NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __device__ void reset() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) m[k] = kNoKeysMax;
+    clear_sums();
+  }
+  // Column k's sum of weights (the same in every lane of the column).
+  __device__ float col_sum(int k) const {
+    if constexpr (kBf16) {
+      return lsum[k][0];
+    } else {
+      float lt = lsum[k][0] + __shfl_xor(lsum[k][0], 16);
+      return lt + __shfl_xor(lt, 32);
     }
   }
 
@@ -1920,7 +1954,19 @@ struct PrefillTile {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[k][i] - m[k]);
-      O::pv(r.v, p, l[k], acc[k]);
+      if constexpr (kBf16) {
+        constexpr i16x4 kOnes = {0x3f80, 0x3f80, 0x3f80, 0x3f80};   // bf16 1.0
+        const i16x4 pk = pack_bf16x4(p[0], p[1], p[2], p[3]);
+#pragma unroll
+        for (int nb = 0; nb < O::NV; ++nb)
+          acc[k][nb] =
+              __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, r.v[nb]), pk, acc[k][nb], 0, 0, 0);
+        lsum[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kOnes, pk, lsum[k], 0, 0, 0);
+      } else {
+        float lk = lsum[k][0];
+        O::pv(r.v, p, lk, acc[k]);
+        lsum[k][0] = lk;
+      }
     }
     return __builtin_amdgcn_ballot_w64(over) != 0;
   }
@@ -1962,6 +2008,21 @@ struct WideTileQ8 {
 #pragma unroll
       for (int nb = 0; nb < NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
+
+  __device__ void clear_sums() {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      l[k] = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // Column k's sum of weights: this lane's four tokens' plus the other lane
+  // groups'.
+  __device__ float col_sum(int k) const {
+    const float lt = l[k] + __shfl_xor(l[k], 16);
+    return lt + __shfl_xor(lt, 32);
   }
 
   // The query rows fetched into q (SegmentQ8::fetch_row) converted to fp16
@@ -2195,8 +2256,7 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
   bad = bad && len != 0;
 #pragma unroll
   for (int k = 0; k < kNB; ++k) {
-    float lt = t.l[k] + __shfl_xor(t.l[k], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = t.col_sum(k);
     const float inv = bad ? NAN : (lt > 0.f ? 1.0f / lt : 0.f);
     const int g = g0 + 16 * k + n;
     if (g < a.cols) {
@@ -2404,12 +2464,7 @@ wide_kernel(DecodeArgs a) {
                                 : tok0 + kBlock > len;
         t.page_max(r, cut, tok0, a.scale_log2, c);
       }
-#pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        t.l[k] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NV; ++nb) t.acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      t.clear_sums();
       for (int f = first; f < seg_hi; f += 4) {
         Regs r;
         const int pg = load_flat(r, f);
@@ -2421,8 +2476,7 @@ wide_kernel(DecodeArgs a) {
     // written again.
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
-      float lt = t.l[j] + __shfl_xor(t.l[j], 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = t.col_sum(j);
       float* slot = mlds + (wave * kNB + j) * kSlotWords;
 #pragma unroll
       for (int nb = 0; nb < NV; ++nb) *reinterpret_cast<f32x4*>(slot + n * kRow + 16 * nb + 4 * c) = t.acc[j][nb];
