@@ -1861,6 +1861,17 @@ split_kernel(DecodeArgs a) {
 // maximum, then the accumulation again from zero with that maximum fixed.
 constexpr float kPrefillHeadroom = 64.0f;
 
+// Largest of four scores with two v_max3_f32.  fmaxf on values that cross a
+// branch (the masked and unmasked pages) makes the compiler quiet each
+// input first (one extra move per value), in case it is a signalling NaN;
+// scores come from multiplications and selects and never are one.
+__device__ inline float max4_scores(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(r), "v"(d));
+  return r;
+}
+
 template <bool kBf16, int D, int kNB>
 struct PrefillTile {
   using O = Ops<kBf16, D>;
@@ -1921,7 +1932,7 @@ struct PrefillTile {
         }
     }
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) pm[k] = fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3]));
+    for (int k = 0; k < kNB; ++k) pm[k] = max4_scores(x[k][0], x[k][1], x[k][2], x[k][3]);
   }
 
   // One page of the accumulation.  Returns true (wave-uniform) if some
@@ -2075,7 +2086,7 @@ struct WideTileQ8 {
         }
     }
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) pm[k] = fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3]));
+    for (int k = 0; k < kNB; ++k) pm[k] = max4_scores(x[k][0], x[k][1], x[k][2], x[k][3]);
   }
 
   // One page of the accumulation; returns true (wave-uniform) if some score
