@@ -1878,6 +1878,11 @@ struct PrefillTile {
   u32x4 q[kNB][O::NK];
   int hi[kNB], lo[kNB];      // keys [lo, hi) of this lane's column
   float m[kNB];
+  // m + kPrefillHeadroom, the score above which a page overruns the column
+  // (+inf while the column has no maximum yet); settled (wave-uniform): every
+  // column of the wavefront has its maximum, so pages skip the first-keys test.
+  float mlim[kNB];
+  bool settled;
   // Sums of the weights.  bf16: accumulated by the matrix core as the
   // product of an all-ones operand with the same rounded weights the PV
   // product takes, so every element holds its column's sum over all tokens
@@ -1898,7 +1903,18 @@ struct PrefillTile {
   __device__ void reset() {
 #pragma unroll
     for (int k = 0; k < kNB; ++k) m[k] = kNoKeysMax;
+    set_limits();
     clear_sums();
+  }
+  // mlim and settled from the current maxima.
+  __device__ void set_limits() {
+    bool unset = false;
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      mlim[k] = m[k] == kNoKeysMax ? INFINITY : m[k] + kPrefillHeadroom;
+      unset |= m[k] == kNoKeysMax;
+    }
+    settled = __builtin_amdgcn_ballot_w64(unset) == 0;
   }
   // Column k's sum of weights (the same in every lane of the column).
   __device__ float col_sum(int k) const {
@@ -1945,19 +1961,21 @@ struct PrefillTile {
 #pragma unroll
       for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::mask_v(r.v[nb], c, valid);
     }
-    bool init = false, over = false;
+    bool over = false;
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) {
-      const bool unset = m[k] == kNoKeysMax;
-      init |= unset & (pm[k] > kNoKeysMax);
-      over |= !unset & (pm[k] > m[k] + kPrefillHeadroom);
-    }
-    if (!fixed && __builtin_amdgcn_ballot_w64(init) != 0) {
+    for (int k = 0; k < kNB; ++k) over |= pm[k] > mlim[k];
+    if (!settled) {
+      bool init = false;
 #pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
+      for (int k = 0; k < kNB; ++k) init |= (m[k] == kNoKeysMax) & (pm[k] > kNoKeysMax);
+      if (!fixed && __builtin_amdgcn_ballot_w64(init) != 0) {
+#pragma unroll
+        for (int k = 0; k < kNB; ++k) {
+          float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
+          cm = fmaxf(cm, __shfl_xor(cm, 32));
+          m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
+        }
+        set_limits();
       }
     }
 #pragma unroll
@@ -2021,6 +2039,7 @@ struct WideTileQ8 {
     }
   }
 
+  __device__ void set_limits() {}   // (this tile tests first keys and overruns on every page)
   __device__ void clear_sums() {
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
@@ -2261,6 +2280,7 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
       const int tok0 = kBlock * (fb + p);
       t.page_max(r, tok0 + kBlock > hi0 || tok0 < lo1, tok0, a.scale_log2, c);
     }
+    t.set_limits();
     run(true);
   }
   // A length of 0 gives zero rows (no key seen), an invalid one NaN rows.
@@ -2475,6 +2495,7 @@ wide_kernel(DecodeArgs a) {
                                 : tok0 + kBlock > len;
         t.page_max(r, cut, tok0, a.scale_log2, c);
       }
+      t.set_limits();
       t.clear_sums();
       for (int f = first; f < seg_hi; f += 4) {
         Regs r;
