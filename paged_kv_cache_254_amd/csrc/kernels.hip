@@ -2027,6 +2027,8 @@ struct WideTileQ8 {
   bool gok[kNB];
   int hi[kNB], lo[kNB];      // keys [lo, hi) of this lane's column
   float m[kNB], l[kNB];
+  float mlim[kNB];           // see PrefillTile
+  bool settled;
   f32x4 acc[kNB][NV];
 
   __device__ void reset() {
@@ -2037,9 +2039,18 @@ struct WideTileQ8 {
 #pragma unroll
       for (int nb = 0; nb < NV; ++nb) acc[k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    set_limits();
   }
 
-  __device__ void set_limits() {}   // (this tile tests first keys and overruns on every page)
+  __device__ void set_limits() {   // mlim and settled, as in PrefillTile
+    bool unset = false;
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      mlim[k] = m[k] == kNoKeysMax ? INFINITY : m[k] + kPrefillHeadroom;
+      unset |= m[k] == kNoKeysMax;
+    }
+    settled = __builtin_amdgcn_ballot_w64(unset) == 0;
+  }
   __device__ void clear_sums() {
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
@@ -2115,19 +2126,21 @@ struct WideTileQ8 {
   __device__ bool page(PageRegsQ8<D>& r, int, bool cut, int tok0, float scale_log2, int c, bool fixed) {
     float x[kNB][4], pm[kNB];
     scores(r, cut, tok0, scale_log2, c, x, pm);
-    bool init = false, over = false;
+    bool over = false;
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) {
-      const bool unset = m[k] == kNoKeysMax;
-      init |= unset & (pm[k] > kNoKeysMax);
-      over |= !unset & (pm[k] > m[k] + kPrefillHeadroom);
-    }
-    if (!fixed && __builtin_amdgcn_ballot_w64(init) != 0) {
+    for (int k = 0; k < kNB; ++k) over |= pm[k] > mlim[k];
+    if (!settled) {   // as in PrefillTile::page
+      bool init = false;
 #pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
+      for (int k = 0; k < kNB; ++k) init |= (m[k] == kNoKeysMax) & (pm[k] > kNoKeysMax);
+      if (!fixed && __builtin_amdgcn_ballot_w64(init) != 0) {
+#pragma unroll
+        for (int k = 0; k < kNB; ++k) {
+          float cm = fmaxf(pm[k], __shfl_xor(pm[k], 16));
+          cm = fmaxf(cm, __shfl_xor(cm, 32));
+          m[k] = (m[k] == kNoKeysMax && cm > kNoKeysMax) ? cm : m[k];
+        }
+        set_limits();
       }
     }
     // Value operand: each code minus its token's zero point, (1024 + u) -
