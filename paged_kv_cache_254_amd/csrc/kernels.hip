@@ -1930,6 +1930,12 @@ struct PrefillTile {
   // `cut`; pm: this lane's maximum per block.
   __device__ void scores(const PageRegs<kBf16, D>& r, bool cut, int tok0, float scale_log2, int c,
                          float (&x)[kNB][4], float (&pm)[kNB]) const {
+    raw_scores(r, scale_log2, x, pm);
+    if (cut) mask_scores(tok0, c, x, pm);
+  }
+  // The scores without masks, and their maxima.
+  __device__ void raw_scores(const PageRegs<kBf16, D>& r, float scale_log2, float (&x)[kNB][4],
+                             float (&pm)[kNB]) const {
     f32x4 s[kNB];
 #pragma unroll
     for (int k = 0; k < kNB; ++k) s[k] = kNB > 1 ? O::qk1(r.k, q[k]) : O::qk(r.k, q[k]);
@@ -1937,16 +1943,19 @@ struct PrefillTile {
     for (int k = 0; k < kNB; ++k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[k][i] = s[k][i] * scale_log2;
-    if (cut) {
 #pragma unroll
-      for (int k = 0; k < kNB; ++k)
+    for (int k = 0; k < kNB; ++k) pm[k] = max4_scores(x[k][0], x[k][1], x[k][2], x[k][3]);
+  }
+  // Scores outside each column's key range set to -inf, and the maxima again.
+  __device__ void mask_scores(int tok0, int c, float (&x)[kNB][4], float (&pm)[kNB]) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tok0 + 4 * c + i;
-          const bool in = (t < hi[k]) & (t >= lo[k]);
-          x[k][i] = in ? x[k][i] : -INFINITY;
-        }
-    }
+    for (int k = 0; k < kNB; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tok0 + 4 * c + i;
+        const bool in = (t < hi[k]) & (t >= lo[k]);
+        x[k][i] = in ? x[k][i] : -INFINITY;
+      }
 #pragma unroll
     for (int k = 0; k < kNB; ++k) pm[k] = max4_scores(x[k][0], x[k][1], x[k][2], x[k][3]);
   }
@@ -1957,6 +1966,15 @@ struct PrefillTile {
   __device__ bool page(PageRegs<kBf16, D>& r, int valid, bool cut, int tok0, float scale_log2, int c, bool fixed) {
     float x[kNB][4], pm[kNB];
     scores(r, cut, tok0, scale_log2, c, x, pm);
+    const bool over = prepare(r, pm, valid, c, fixed);
+    finish(r, x);
+    return over;
+  }
+
+  // The page step's branches, given its (masked) score maxima: values past
+  // the length zeroed, overrun test, the maxima of columns seeing their first
+  // keys.  Returns true (wave-uniform) on an overrun.
+  __device__ bool prepare(PageRegs<kBf16, D>& r, const float (&pm)[kNB], int valid, int c, bool fixed) {
     if (valid < kBlock) {
 #pragma unroll
       for (int nb = 0; nb < O::NV; ++nb) r.v[nb] = O::mask_v(r.v[nb], c, valid);
@@ -1978,6 +1996,11 @@ struct PrefillTile {
         set_limits();
       }
     }
+    return __builtin_amdgcn_ballot_w64(over) != 0;
+  }
+
+  // The page step's arithmetic, free of branches: weights, PV products, sums.
+  __device__ void finish(const PageRegs<kBf16, D>& r, const float (&x)[kNB][4]) {
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
       float p[4];
@@ -1997,7 +2020,6 @@ struct PrefillTile {
         lsum[k][0] = lk;
       }
     }
-    return __builtin_amdgcn_ballot_w64(over) != 0;
   }
 
   // Exact per-column maximum over page r (the redo pass).
@@ -2283,8 +2305,54 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
     }
     return overflow;
   };
+  // The first pass, software-pipelined: step p runs page p's branches (masks
+  // of a cut page, values past the length, first keys, overrun test), then in
+  // one basic block the score products of page p + 1 and the weights and PV
+  // products of page p, so that the matrix core works on one page while the
+  // vector unit finishes the other (one wavefront per SIMD: nothing else
+  // would fill either).  Past the last page the next buffer holds zeros from
+  // an empty range, and its scores are dropped.
+  auto run_pipelined = [&]() {
+    Regs buf[kBufs];
+    int page_of[kBufs];
+    int issued = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) page_of[s] = load(buf[s], issued++);
+    float x[kNB][4], pm[kNB];   // scores of the page computed next, unmasked
+    t.raw_scores(buf[0], a.scale_log2, x, pm);
+    int p = 0;
+    while (p < cnt) {
+#pragma unroll
+      for (int s = 0; s < kBufs; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        page_of[(s + kDepth) % kBufs] = load(buf[(s + kDepth) % kBufs], issued++);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < cnt) {
+          bad |= static_cast<unsigned>(page_of[s]) >= static_cast<unsigned>(a.num_pages);
+          const int tok0 = kBlock * (fb + p);
+          if (tok0 + kBlock > hi0 || tok0 < lo1) t.mask_scores(tok0, c, x, pm);
+          overflow |= t.prepare(buf[s], pm, len - tok0, c, false);
+          float xn[kNB][4], pmn[kNB];
+          t.raw_scores(buf[(s + 1) % kBufs], a.scale_log2, xn, pmn);
+          t.finish(buf[s], x);
+#pragma unroll
+          for (int k = 0; k < kNB; ++k) {
+            pm[k] = pmn[k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[k][i] = xn[k][i];
+          }
+        }
+        ++p;
+      }
+    }
+    return overflow;
+  };
   t.reset();
-  if (run(false)) {
+  bool overran;
+  if constexpr (kDepth >= 2) overran = run_pipelined();
+  else overran = run(false);
+  if (overran) {
     // Rare: redo the tile with every column's exact maximum.
     t.reset();
     for (int p = 0; p < cnt; ++p) {
