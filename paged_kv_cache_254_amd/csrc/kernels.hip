@@ -1543,8 +1543,14 @@ struct FlatCursor {
 // At least two wavefronts per SIMD: caps registers at 256 per lane, which the
 // bf16 kernels fit without spilling; fp32 at head_dim 128 needs more and runs
 // one wavefront per SIMD.
+#ifndef PKV_SPLIT_WAVES_PER_EU
+#define PKV_SPLIT_WAVES_PER_EU 2
+#endif
+#ifndef PKV_Q8_WAVES_PER_EU
+#define PKV_Q8_WAVES_PER_EU 2
+#endif
 template <bool kBf16, int D>
-constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? 2 : 1;
+constexpr int kSplitWavesPerEu = (kBf16 || D == 64) ? PKV_SPLIT_WAVES_PER_EU : 1;
 
 // Ring depth of the kernels whose sibling wavefronts (one per 16-head block
 // of a large group) read the same pages.
@@ -1586,7 +1592,7 @@ struct Q8KV {                          // 8-bit codes + scales; bf16 q and out
   static constexpr bool kMulti = false;
   static constexpr int kTileK = kBlock * D;        // bytes of one K (or V) code tile
   static constexpr int kMetaBytes = 4 * kBlock * 4;
-  static constexpr int kWavesPerEu = 2;
+  static constexpr int kWavesPerEu = PKV_Q8_WAVES_PER_EU;
   static constexpr int kWavesPerEuGrouped = PKV_GROUPED_WAVES_PER_EU;
   using Regs = PageRegsQ8<D>;
   using Seg = SegmentQ8<D, false>;   // one query token, no window
@@ -2022,6 +2028,55 @@ struct PrefillTile {
     }
   }
 
+  // bf16: the weights of one page, rounded and packed as the value
+  // product's operand (tokens 4c .. 4c + 3 of this lane's column), per block.
+  __device__ void weights(const float (&x)[kNB][4], i16x4 (&pk)[kNB]) const {
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[k][i] - m[k]);
+      pk[k] = pack_bf16x4(p[0], p[1], p[2], p[3]);
+    }
+  }
+  // bf16: value products and weight sums of two pages a and b in one
+  // 16x16x32 product per feature block, which does the work of two 16x16x16
+  // ones in the time of one.  The contraction index of a 16x16x32 product
+  // runs over eight elements per lane where the 16x16x16 one has four, and
+  // the two operands number them alike, so a lane can put page a's four
+  // tokens (4c .. 4c + 3) first and page b's second in both operands: its V
+  // registers and its weights as they are, with nothing moved between lanes.
+  __device__ void pv_pair(const PageRegs<kBf16, D>& ra, const i16x4 (&pa)[kNB], const PageRegs<kBf16, D>& rb,
+                          const i16x4 (&pb)[kNB]) {
+    constexpr u32x4 kOnes = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      const u32x2 wa = __builtin_bit_cast(u32x2, pa[k]), wb = __builtin_bit_cast(u32x2, pb[k]);
+      const bf16x8 w = __builtin_bit_cast(bf16x8, u32x4{wa.x, wa.y, wb.x, wb.y});
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) {
+        const u32x4 v = {ra.v[nb].x, ra.v[nb].y, rb.v[nb].x, rb.v[nb].y};
+        acc[k][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), w, acc[k][nb], 0, 0, 0);
+      }
+      lsum[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kOnes), w, lsum[k], 0, 0, 0);
+    }
+  }
+  // bf16: the same for a page without a partner (the second half zero).
+  __device__ void pv_last(const PageRegs<kBf16, D>& ra, const i16x4 (&pa)[kNB]) {
+    constexpr u32x4 kOnes = {0x3f803f80u, 0x3f803f80u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      const u32x2 wa = __builtin_bit_cast(u32x2, pa[k]);
+      const bf16x8 w = __builtin_bit_cast(bf16x8, u32x4{wa.x, wa.y, 0u, 0u});
+#pragma unroll
+      for (int nb = 0; nb < O::NV; ++nb) {
+        const u32x4 v = {ra.v[nb].x, ra.v[nb].y, 0u, 0u};
+        acc[k][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), w, acc[k][nb], 0, 0, 0);
+      }
+      lsum[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kOnes), w, lsum[k], 0, 0, 0);
+    }
+  }
+
   // Exact per-column maximum over page r (the redo pass).
   __device__ void page_max(const PageRegs<kBf16, D>& r, bool cut, int tok0, float scale_log2, int c) {
     float x[kNB][4], pm[kNB];
@@ -2210,6 +2265,15 @@ struct WideTileQ8 {
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 1
 #endif
+// bf16 prefill: value products of two pages per 16x16x32 product
+// (PrefillTile::pv_pair); 0 keeps one 16x16x16 product per page.
+#ifndef PKV_PREFILL_PAIRED
+#define PKV_PREFILL_PAIRED 1
+#endif
+// Largest batch whose sequences the prefill kernel orders longest first.
+#ifndef PKV_PREFILL_RANKED_BATCH
+#define PKV_PREFILL_RANKED_BATCH 1024
+#endif
 template <bool kBf16, int D, int kNB, int kDepth>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
@@ -2224,14 +2288,44 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
   const int i = static_cast<int>(blockIdx.x);
   const int slot = i >> 3;
   const int pg_group = slot / wg_per_pair;
-  if (pg_group >= n_pair_groups) return;
+  if (pg_group >= n_pair_groups) return;                // the whole workgroup
   const int pair = pg_group * 8 + (i & 7);
+  if (pair >= a.batch * a.n_kv) return;                 // the whole workgroup
+  // Longest sequences first: pair index r * n_kv + h is KV head h of the
+  // sequence of rank r in decreasing length (ties by index).  Workgroups are
+  // dispatched in index order as CUs free up, so the long tiles start first
+  // and the short ones fill in behind them instead of leaving a long tail.
+  // Each workgroup ranks the lengths in LDS (batches up to kRankedBatch;
+  // larger ones keep the sequence order).  Not with a window: a tile then
+  // attends at most the window plus its own tokens, so the tiles of long
+  // sequences all take about the same time and the ranking would only add
+  // its cost.
+  constexpr int kRankedBatch = PKV_PREFILL_RANKED_BATCH;
+  __shared__ int32_t s_len[kRankedBatch > 0 ? kRankedBatch : 1];
+  __shared__ int32_t s_pick;
+  const int r = pair / a.n_kv;
+  int b = r;
+  const bool ranked = a.window == 0 && a.batch <= kRankedBatch;
+  if (ranked) {
+    for (int t = threadIdx.x; t < a.batch; t += blockDim.x) s_len[t] = seq_len_of(a, t);
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.batch; t += blockDim.x) {
+      const int lt = s_len[t];
+      int rank = 0;
+      for (int j = 0; j < a.batch; ++j) {
+        const int lj = s_len[j];
+        rank += (lj > lt) | ((lj == lt) & (j < t));
+      }
+      if (rank == r) s_pick = t;
+    }
+    __syncthreads();
+    b = uni(s_pick);
+  }
+  const int h = pair - r * a.n_kv;
   const int tile = (slot - pg_group * wg_per_pair) * kWavesPerGroup + wave;
-  if (pair >= a.batch * a.n_kv || tile >= tiles_per_pair) return;
-  const int b = pair / a.n_kv;
-  const int h = pair - b * a.n_kv;
+  if (tile >= tiles_per_pair) return;
   const int g0 = tile * kCols;                          // first column of the tile
-  const int len = seq_len_of(a, b);
+  const int len = ranked ? s_len[b] : seq_len_of(a, b);
   const bool len_ok = len >= a.q_len && len <= a.max_blocks * kBlock;
   // Keys the tile's columns attend: from the window start of its first
   // query token to its last query token.
@@ -2348,9 +2442,63 @@ prefill_kernel(DecodeArgs a, int tiles_per_pair, int wg_per_pair, int n_pair_gro
     }
     return overflow;
   };
+  // bf16: the same pipeline with the value products of pages 2i and 2i + 1
+  // done together (PrefillTile::pv_pair) in the step of page 2i + 1: page
+  // 2i's weights wait in registers and its tile stays in the ring, which
+  // holds kDepth + 2 pages (p - 1 .. p + kDepth; one more for an odd depth)
+  // so that the load issued in step p overwrites a page whose products are
+  // done.  The ring's size is even, so a page's parity is its ring slot's.
+  auto run_paired = [&]() {
+    constexpr int R = kDepth + 2 + (kDepth % 2);   // even
+    Regs buf[R];
+    int page_of[R];
+    int issued = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s) page_of[s] = load(buf[s], issued++);
+    float x[kNB][4], pm[kNB];
+    t.raw_scores(buf[0], a.scale_log2, x, pm);
+    i16x4 pk_prev[kNB];
+    int p = 0;
+    while (p < cnt) {
+#pragma unroll
+      for (int s = 0; s < R; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        page_of[(s + kDepth) % R] = load(buf[(s + kDepth) % R], issued++);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < cnt) {
+          bad |= static_cast<unsigned>(page_of[s]) >= static_cast<unsigned>(a.num_pages);
+          const int tok0 = kBlock * (fb + p);
+          if (tok0 + kBlock > hi0 || tok0 < lo1) t.mask_scores(tok0, c, x, pm);
+          overflow |= t.prepare(buf[s], pm, len - tok0, c, false);
+          float xn[kNB][4], pmn[kNB];
+          t.raw_scores(buf[(s + 1) % R], a.scale_log2, xn, pmn);
+          i16x4 pk[kNB];
+          t.weights(x, pk);
+          if (s % 2 == 1) {
+            t.pv_pair(buf[s - 1], pk_prev, buf[s], pk);
+          } else if (p + 1 < cnt) {
+#pragma unroll
+            for (int k = 0; k < kNB; ++k) pk_prev[k] = pk[k];
+          } else {
+            t.pv_last(buf[s], pk);
+          }
+#pragma unroll
+          for (int k = 0; k < kNB; ++k) {
+            pm[k] = pmn[k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[k][i] = xn[k][i];
+          }
+        }
+        ++p;
+      }
+    }
+    return overflow;
+  };
   t.reset();
   bool overran;
-  if constexpr (kDepth >= 2) overran = run_pipelined();
+  if constexpr (kBf16 && kDepth >= 2 && PKV_PREFILL_PAIRED) overran = run_paired();
+  else if constexpr (kDepth >= 2) overran = run_pipelined();
   else overran = run(false);
   if (overran) {
     // Rare: redo the tile with every column's exact maximum.
@@ -3615,8 +3763,9 @@ int scratch_of_current_device(hipStream_t stream, void** out) {
 #endif
 // 16-column blocks (query tokens x query heads of one KV head) per
 // wavefront of the prefill kernel, and its ring depth.  Four blocks fit the
-// register file (bf16: 232 VGPRs + 140 AGPRs at head_dim 128, no scratch; one
-// wavefront per SIMD); fp32 at head_dim 128 takes two, with one page ahead.
+// register file (bf16: 256 VGPRs + 192 AGPRs at head_dim 128 with the paired
+// value products' ring of four pages, no scratch; one wavefront per SIMD);
+// fp32 at head_dim 128 takes two, with one page ahead.
 // Two wavefronts of two blocks per SIMD measured 36 % slower, three blocks
 // 10 % slower.
 #ifndef PKV_PREFILL_BLOCKS

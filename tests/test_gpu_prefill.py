@@ -82,6 +82,16 @@ def test_prefill_empty_and_short_sequences(pkv):
     run_prefill(pkv, 4, 16, 4, 128, "bf16", [120, 80, 150, 100], 24, 0, seed=212, zero=(1,), short=(3,))
 
 
+def test_prefill_longest_first_order(pkv):
+    """Without a window the prefill kernel hands the sequences to its
+    workgroups longest first (ties by index): equal lengths, a zero length and
+    an invalid one among them, in a batch it ranks and in one above the
+    ranking's 1024-sequence limit, which keeps the sequence order."""
+    run_prefill(pkv, 6, 8, 2, 128, "bf16", [150, 300, 150, 40, 300, 90], 24, 0, seed=214, zero=(3,), short=(5,))
+    lens = [17 + (b * 7) % 23 for b in range(1030)]
+    run_prefill(pkv, 1030, 8, 2, 64, "bf16", lens, 17, 0, seed=215, zero=(1029,))
+
+
 def test_prefill_just_above_the_split_kernel(pkv):
     """68 columns: four past the 64 the split kernel takes, so the last tile
     holds 4 live columns and 12 idle lanes per MFMA."""
