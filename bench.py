@@ -368,8 +368,12 @@ def main():
                                         combine_mode=1 if args.separate_combine else 0, schedule=args.schedule)
     # One kernel per layer when every pair can be merged inside the decode
     # kernel: a pair spans at most ceil(max_blocks / min_chunk) + 1 chunks, and
-    # the library merges pairs of at most 96 chunks there.
-    one_kernel = wide or (not args.separate_combine and -(-S["mb"] // dec.min_chunk_pages) + 1 <= 96)
+    # the library merges pairs of at most 96 chunks there, or 24 in its wide
+    # kernel (33 to 64 query columns per KV head), whose larger merges it
+    # leaves to the combine kernel.
+    wide_decode = not wide and T * w.group > 32
+    one_kernel = wide or (not args.separate_combine and
+                          -(-S["mb"] // dec.min_chunk_pages) + 1 <= (24 if wide_decode else 96))
     layers = S["layers"]
     n_layers = w.n_layers
     kv_step = S["kv_bytes_layer"] * n_layers

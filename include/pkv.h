@@ -182,7 +182,10 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_p
  * one atomic per chunk; merge order is fixed, so results are run-to-run
  * identical); pairs that may span more than 96 chunks (ceil(max_blocks_per_seq
  * / min_chunk_pages) + 1 > 96) are merged by a second kernel, which is then
- * launched on the same stream.
+ * launched on the same stream.  With 33 to 64 query columns per KV head
+ * (query heads per KV head times query tokens) the bound is 24 chunks, and
+ * above it only pairs of at most 8 chunks are merged in the decode kernel.
+ * Either way every pair is merged by the same formula in a fixed order.
  *
  * workspace: device, 256-byte aligned, at least
  * pkv_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, n_items)

@@ -3917,7 +3917,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.scale_log2 = scale * kLog2e;
   // Merge in the decode kernel when both halves run in this call; the
   // combine kernel then runs only if some pair may span more than
-  // kFuseMaxParts chunks (C >= min_chunk, so a pair of at most
+  // fuse_limit chunks (C >= min_chunk, so a pair of at most
   // max_blocks_per_seq pages spans at most ceil(max_blocks / min_chunk) + 1).
   const bool fuse = do_split && do_combine && r.combine_mode == 0;
   const int64_t max_parts = (static_cast<int64_t>(max_blocks_per_seq) + r.min_chunk - 1) / r.min_chunk + 1;
@@ -3925,7 +3925,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   // word, which is the dynamic schedule's chunk counter.
   int32_t* tail = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + (workspace_bytes & ~size_t{3})) - 1;
   a.counters = fuse ? tail : nullptr;
-  a.fuse_max_parts = kFuseMaxParts;
+  a.fuse_max_parts = fuse_limit(uses_wide(dtype, cols, q8), max_parts);
   a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                         decode_prefix_offset(batch, cols, n_kv_heads, head_dim, r.n_items));
   a.work = tail;
@@ -3978,7 +3978,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
       lds = r.lds;
     }
   }
-  const bool run_combine = do_combine && (!fuse || max_parts > kFuseMaxParts);
+  const bool run_combine = do_combine && (!fuse || max_parts > a.fuse_max_parts);
   // One combine workgroup per slice of an output row.
   const int64_t combine_rows = static_cast<int64_t>(batch) * q_len * n_q_heads;
   const int fs_log2 = combine_slices_log2(combine_rows, head_dim);

@@ -76,6 +76,21 @@ __host__ __device__ inline int64_t decode_slots(int64_t batch, int64_t n_kv, int
 // that finishes last, inside the decode kernel; longer ones by the combine
 // kernel (one wavefront would read all their partials).
 constexpr int kFuseMaxParts = 96;
+// The wide kernel (33 to 64 columns per KV head) merges 64 columns per pair,
+// four partials per round trip, in the one wavefront per 16-column block of
+// the pair's last workgroup, while the rest of the chip has finished: at 32
+// partials a pair (the 8-token 70B layer) that tail cost about 30 % of the
+// launch against the combine kernel.  So when a pair may span more than
+// kWideFuseMaxParts chunks the combine kernel runs, and only pairs of at most
+// kWideFuseSmallParts chunks are merged inside the wide kernel.
+constexpr int kWideFuseMaxParts = 24;
+constexpr int kWideFuseSmallParts = 8;
+// The largest pair (in chunks) merged inside the decode kernel, given the
+// bound max_parts on a pair's chunks; the combine kernel runs for the rest
+// when max_parts exceeds it.
+inline int fuse_limit(bool wide, int64_t max_parts) {
+  return wide && max_parts > kWideFuseMaxParts ? kWideFuseSmallParts : kFuseMaxParts;
+}
 constexpr int kMaxWavesPerChunk = 4;
 
 // Workspace layout: partial outputs [slots][group][head_dim] f32, partial
