@@ -1111,14 +1111,39 @@ static_assert(q8_v_offset(127, 15) == 2047 && q8_v_offset(63, 15) == 1023 && q8_
 // lane + 64) and the decode kernel's fused append (features 2 lane and
 // 2 lane + 1) both use these, so their codes agree bit for bit.
 __device__ inline float bf16_bits_to_f32(uint32_t bits) { return __builtin_bit_cast(float, bits << 16); }
+// Value of lane i ^ 1, i ^ 2 (within each quad), 7 - i within each half row
+// and 15 - i within each row of 16 lanes: DPP moves, no LDS round trip.
+template <int kCtrl>
+__device__ inline float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+// Wave-wide minimum and maximum: within each row by DPP (neighbours, pairs,
+// then the mirrored half and row, which after the quad steps hold the other
+// quad and the other half), then the four rows' results as scalars.  A
+// minimum or maximum does not depend on the order it is taken in.
+__device__ inline void wave_min_max(float& lo, float& hi) {
+  lo = fminf(lo, dpp_f32<kDppXor1>(lo));
+  hi = fmaxf(hi, dpp_f32<kDppXor1>(hi));
+  lo = fminf(lo, dpp_f32<kDppXor2>(lo));
+  hi = fmaxf(hi, dpp_f32<kDppXor2>(hi));
+  lo = fminf(lo, dpp_f32<kDppHalfMirror>(lo));
+  hi = fmaxf(hi, dpp_f32<kDppHalfMirror>(hi));
+  lo = fminf(lo, dpp_f32<kDppMirror>(lo));
+  hi = fmaxf(hi, dpp_f32<kDppMirror>(hi));
+  auto lane_f = [](float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  };
+  lo = fminf(fminf(lane_f(lo, 0), lane_f(lo, 16)), fminf(lane_f(lo, 32), lane_f(lo, 48)));
+  hi = fmaxf(fmaxf(lane_f(hi, 0), lane_f(hi, 16)), fmaxf(lane_f(hi, 32), lane_f(hi, 48)));
+}
 __device__ inline void q8_params(float x0, float x1, float& sc, float& z) {
   float lo = fminf(fminf(x0, x1), 0.f);
   float hi = fmaxf(fmaxf(x0, x1), 0.f);
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off));
-    hi = fmaxf(hi, __shfl_xor(hi, off));
-  }
+  wave_min_max(lo, hi);
   sc = (hi - lo) / 255.0f;
   if (sc == 0.f) sc = 1.0f;
   z = __builtin_rintf(-lo / sc);
