@@ -605,36 +605,48 @@ PKV_INLINE __device__ void emit_segment(const DecodeArgs& a, int b, int h, int g
 // PendingMerges::wg_base).
 struct HeldResults {
   int n = 0, cap = 0, base = 0, words = 0;
+  // Rows 16 blk .. 16 blk + 15 of slot n (head block blk of the wavefront's
+  // one or two): the block's normalised result o and its lse.
   template <int D>
-  PKV_INLINE __device__ void put(const DecodeArgs& a, int b, int h, int n_pages, int seg_start, const f32x4 (&o)[D / 16],
-                      float lse, int lane) {
-    const int c = lane >> 4, col = lane & 15;
+  PKV_INLINE __device__ void put_block(const DecodeArgs& a, int blk, const f32x4 (&o)[D / 16], float lse, int lane) {
+    const int c = lane >> 4, row = 16 * blk + (lane & 15);
     const int cols = a.cols;
     const int sb = uni(base + n * words);
-    if (col < cols) {
+    if (row < cols) {
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb)
-        *reinterpret_cast<f32x4*>(lds_f32 + sb + col * lds_row(D) + 16 * nb + 4 * c) = o[nb];
-      if (c == 0) lds_f32[sb + cols * lds_row(D) + col] = lse;
+        *reinterpret_cast<f32x4*>(lds_f32 + sb + row * lds_row(D) + 16 * nb + 4 * c) = o[nb];
+      if (c == 0) lds_f32[sb + cols * lds_row(D) + row] = lse;
     }
+  }
+  // Closes slot n with the segment's coordinates.
+  PKV_INLINE __device__ void commit(int b, int h, int n_pages, int seg_start, int lane) {
+    const int sb = uni(base + n * words);
     if (lane == 0) *reinterpret_cast<int4*>(lds_f32 + sb + words - 4) = make_int4(b, h, n_pages, seg_start);
     ++n;
   }
-  // Writes the held results (see emit_segment), in the order they ended.
-  template <bool kOutBf16, int D, bool kMulti, class Pending>
-  PKV_INLINE __device__ void emit_all(const DecodeArgs& a, int gb, int chunk, int C, int lane, Pending& pending) {
+  // Writes the held results (see emit_segment), in the order they ended:
+  // block blk of each as head block gb + blk; the pairs to merge are listed
+  // in `pending` by block 0 (the other block's pairs are the same).
+  template <bool kOutBf16, int D, bool kMulti, int kNB, class Pending>
+  PKV_INLINE __device__ void emit_all(const DecodeArgs& a, int gb, int chunk, int C, int lane, Pending& pending,
+                                      Pending& unused) {
     const int c = lane >> 4, col = lane & 15;
-    const int rc = min(col, a.cols - 1);   // lanes past the group read a valid row and write nothing
     for (int i = 0; i < n; ++i) {
       const int sb = uni(base + i * words);
       const int4 d = *reinterpret_cast<const int4*>(lds_f32 + sb + words - 4);
-      f32x4 o[D / 16];
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
-        o[nb] = *reinterpret_cast<const f32x4*>(lds_f32 + sb + rc * lds_row(D) + 16 * nb + 4 * c);
-      const float lse = lds_f32[sb + a.cols * lds_row(D) + rc];
-      emit_segment<kOutBf16, D, kMulti>(a, uni(d.x), uni(d.y), gb, uni(d.z), uni(d.w), chunk, C, o, lse, lane,
-                                        pending);
+      for (int blk = 0; blk < kNB; ++blk) {
+        if (blk > 0 && (gb + blk) * 16 >= a.cols) continue;
+        const int rc = min(16 * blk + col, a.cols - 1);   // lanes past the group read a valid row and write nothing
+        f32x4 o[D / 16];
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb)
+          o[nb] = *reinterpret_cast<const f32x4*>(lds_f32 + sb + rc * lds_row(D) + 16 * nb + 4 * c);
+        const float lse = lds_f32[sb + a.cols * lds_row(D) + rc];
+        emit_segment<kOutBf16, D, kMulti>(a, uni(d.x), uni(d.y), gb + blk, uni(d.z), uni(d.w), chunk, C, o, lse,
+                                          lane, blk == 0 ? pending : unused);
+      }
     }
     n = 0;
   }
@@ -1735,12 +1747,12 @@ split_kernel(DecodeArgs a) {
   FlatCursor<KV::kMulti> cp;
   cp.seek(a, s_prefix, f0);
   typename KV::Seg seg[kNB];
-  // This wavefront's LDS: held_cap token slots (fused append), then, with one
-  // 16-column block per chunk, as many result slots.
+  // This wavefront's LDS: held_cap token slots (fused append), then as many
+  // result slots (the wavefront's one or two 16-column blocks each).
   const int held_base = held_offset(a.batch) + wave * a.held_wave_words;
   typename KV::template Held<kNG == 1> held;
   held.lds = reinterpret_cast<uint32_t*>(smem + held_base);
-  constexpr bool kHoldResults = kNG == 1 && kNB == 1;
+  constexpr bool kHoldResults = kNG == 1;
   HeldResults results;
   if constexpr (kHoldResults) {
     if (a.held_res_words > 0) {
@@ -1773,8 +1785,13 @@ split_kernel(DecodeArgs a) {
   auto compute = [&](Regs& r, int pg, int p) {
     if (open && (cp.b != seg[0].b || cp.h != seg[0].h)) {
       if (kHoldResults && results.n < results.cap) {
-        const float lse = seg[0].normalise(bad);
-        results.put<D>(a, seg[0].b, seg[0].h, seg[0].n_pages, seg_start, seg[0].acc, lse, lane);
+#pragma unroll
+        for (int i = 0; i < kNB; ++i)
+          if (i == 0 || (gblk + i) * 16 < a.cols) {
+            const float lse = seg[i].normalise(bad);
+            results.put_block<D>(a, i, seg[i].acc, lse, lane);
+          }
+        results.commit(seg[0].b, seg[0].h, seg[0].n_pages, seg_start, lane);
       } else {
 #pragma unroll
         for (int i = 0; i < kNB; ++i)
@@ -1831,7 +1848,7 @@ split_kernel(DecodeArgs a) {
       ++p;
     }
   }
-  if constexpr (kHoldResults) results.emit_all<KV::kOutBf16, D, KV::kMulti>(a, gblk, chunk, C, lane, pending);
+  if constexpr (kHoldResults) results.emit_all<KV::kOutBf16, D, KV::kMulti, kNB>(a, gblk, chunk, C, lane, pending, unused);
   if (open) {
 #pragma unroll
     for (int i = 0; i < kNB; ++i)
@@ -3959,7 +3976,9 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   // - workgroup merges (one wavefront per chunk and one 16-column block,
   //   in-kernel merge on) when their slots fit;
   // - then per wavefront as many slots (up to kMaxHeldSlots) of held tokens
-  //   and, with one 16-column block, held results as the rest allows.
+  //   and held results (one or two 16-column blocks) as the rest allows;
+  //   the two-block kernel runs one workgroup per CU and may take the CU's
+  //   whole LDS for them.
   size_t lds = r.lds;
   a.wg_merge = 0;
   a.wg_lds_offset = 0;
@@ -3969,6 +3988,7 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
   a.held_wave_words = kHeldWords;
   if (r.schedule == PKV_SCHEDULE_STATIC) {
     const bool one_block = cols <= 16;
+    const bool two_blocks = cols > 16 && cols <= 32;   // split_fn: one wavefront per SIMD, both blocks
     size_t wg_words = 0;
     if (fuse && one_block) {
       const size_t wg = static_cast<size_t>(kWavesPerGroup) * 2 * cols * (lds_row(head_dim) + 1);
@@ -3977,8 +3997,9 @@ int decode_common(bool do_split, bool do_combine, const char* fn, const void* q,
     const int es = dtype == PKV_F32 ? 4 : 2;
     // HeldToken::kSlotWords, HeldTokenQ8::kSlotWords
     const int tok = k_new == nullptr ? 0 : q8 ? head_dim / 2 + 12 : head_dim * es / 4 + head_dim + 8;
-    int res = one_block ? ((cols * (lds_row(head_dim) + 1) + 3) & ~3) + 4 : 0;
-    const size_t avail = kMaxLdsBytes / sizeof(int32_t) - held_offset(batch) - wg_words;
+    int res = one_block || two_blocks ? ((cols * (lds_row(head_dim) + 1) + 3) & ~3) + 4 : 0;
+    const size_t budget = two_blocks ? kMaxLdsBytesWide : kMaxLdsBytes;
+    const size_t avail = budget / sizeof(int32_t) - held_offset(batch) - wg_words;
     int cap = res > 0 ? static_cast<int>(std::min<size_t>(kMaxHeldSlots, avail / (kWavesPerGroup * (tok + res))))
                       : 0;
     if (cap == 0) {   // no results held: one token slot (fits, see r.lds)
