@@ -482,12 +482,13 @@ struct PendingMerges {
   int n = 0;
   int b0 = 0, h0 = 0, first0 = 0, nparts0 = 0;
   int b1 = 0, h1 = 0, first1 = 0, nparts1 = 0;
+  // Selects, not a branch on n: a branch made the compiler keep the two
+  // entries as an array indexed at run time, in scratch memory, whose stores
+  // then queued behind the tile loads.
   __device__ void add(int b, int h, int first, int nparts) {
-    if (n == 0) {
-      b0 = b; h0 = h; first0 = first; nparts0 = nparts;
-    } else {
-      b1 = b; h1 = h; first1 = first; nparts1 = nparts;
-    }
+    const bool f = n == 0;
+    b0 = f ? b : b0; h0 = f ? h : h0; first0 = f ? first : first0; nparts0 = f ? nparts : nparts0;
+    b1 = f ? b1 : b; h1 = f ? h1 : h; first1 = f ? first1 : first; nparts1 = f ? nparts1 : nparts;
     n = n < 2 ? n + 1 : 2;
   }
   // Pairs whose chunks all run in this workgroup (static schedule): their
