@@ -79,6 +79,10 @@ CASES = [
     # tokens' windows start in different pages, so the first chunks hold
     # empty (lse -inf) rows for the later queries
     (2, 4, 2, 128, "bf16", [3000, 70], 32, 1600, 300, 1),
+    # 64 columns (wide kernel) with a bound of 76 chunks per pair: the combine
+    # kernel merges the long sequence's pairs (about 20 chunks each) and the
+    # decode kernel the short ones (at most 8 chunks), in the same call
+    (3, 32, 4, 128, "bf16", [1200, 60, 300], 8, 0, 100, 1),
 ]
 
 
