@@ -112,6 +112,7 @@ SMALL = [
     ("gqa4_ragged", 3, 8, 2, 128, [70, 0, 200], 7, 1),
     ("gqa8_tail", 4, 32, 4, 128, [15, 16, 17, 260], 9, 1),
     ("g24", 2, 48, 2, 128, [130, 61], 5, 1),
+    ("g24_ragged", 6, 48, 2, 128, [0, 1, 15, 16, 40, 300], 5, 1),   # two blocks, more results than LDS slots
     ("mqa64", 2, 64, 1, 128, [300, 45], 6, 2),
     ("many_chunks", 3, 8, 2, 64, [1099, 39, 5], 150, 1),
     ("mqa64_d64", 2, 64, 1, 64, [300, 45], 6, 2),         # wide kernel, head_dim 64
