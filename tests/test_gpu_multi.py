@@ -112,11 +112,13 @@ def test_one_token_equals_single_token_decode(pkv):
     assert torch.equal(a, b[:, 0])
 
 
-@pytest.mark.parametrize("T,window", [(4, 0), (4, 1024)])
+@pytest.mark.parametrize("T,window", [(4, 0), (4, 1024), (8, 0), (16, 0)])
 def test_full_size_sampled_multi(pkv, T, window):
     # The full-size GQA layer with q_len query tokens per sequence (and a
     # sliding window), the library's default launch, checked on sampled
-    # sequences against the oracle run on just their pages.
+    # sequences against the oracle run on just their pages: 16 columns per
+    # KV head (one block per wavefront), 32 (two blocks) and 64 (the wide
+    # kernel).
     w = W.get("llama3_8b_gqa")
     c = H.setup(w, device="cuda")
     att = c.attended.astype(np.int64)
